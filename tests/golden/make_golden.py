@@ -1,0 +1,48 @@
+"""Write the stored expected row statistics for the large workloads.
+
+For every token row of the ``4b``, ``headline``, ``block`` and ``shard``
+workloads this stores the oracle's float64 logsumexp over the FULL vocabulary,
+the target logit and the row sum of the logits (``oracle.row_stats``).  The
+parity tests then finish the loss, sampled dH rows and sampled dW rows with
+the oracle at test time; only this O(N*H*V) float64 GEMM is too slow to redo
+there.  Inputs come from ``lm_head_linear_bf16_amd.synth``; nothing here
+touches the HIP library.
+
+Usage:  python tests/golden/make_golden.py [workload ...]
+"""
+
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+sys.path.insert(0, ROOT)
+
+import oracle as O  # noqa: E402
+from lm_head_linear_bf16_amd import synth  # noqa: E402
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def path_for(name: str) -> str:
+    return os.path.join(HERE, f"rowstats_{name}.npz")
+
+
+def make(name: str) -> None:
+    w = synth.WORKLOADS[name]
+    t0 = time.time()
+    target, _ = synth.targets(w)
+    h = synth.hidden(w).values
+    W = synth.weight(w).values               # full vocabulary (all shards)
+    lse, zt, zs = O.row_stats(h, W, target, np.arange(w.N), w.logit_scale, row_block=1024)
+    np.savez(path_for(name), lse=lse, z_target=zt, z_sum=zs,
+             fingerprint=np.array(synth.fingerprint(w)))
+    print(f"{name}: N={w.N} H={w.H} V={w.V} in {time.time() - t0:.1f}s", flush=True)
+
+
+if __name__ == "__main__":
+    names = sys.argv[1:] or ["4b", "headline", "block", "shard"]
+    for n in names:
+        make(n)
