@@ -1,0 +1,192 @@
+/*
+ * fldce.h - fused linear diffusion cross-entropy (LM head) for MI355X / gfx950.
+ *
+ * C ABI of libfldce.so.  Every pointer argument is caller-owned device memory
+ * (HIP / PyTorch allocations) unless stated otherwise; the library never
+ * allocates, frees or synchronises inside a call.  All work is enqueued on the
+ * caller's HIP stream (`stream`, a hipStream_t passed as void*; NULL = the
+ * null stream) and is asynchronous with respect to the host.
+ *
+ * What is computed (model page "fused_linear_diffusion_cross_entropy.py",
+ * functions fused_linear_cross_entropy_forward, logsumexp_fwd and
+ * cross_entropy_kernel, steps 4-6):
+ *
+ *   z      = s * (h W^T)                             logits, s = logit_scale
+ *   lse_i  = log sum_j exp(z_ij)                     stable row logsumexp
+ *   l_i    = [(1-eps)(lse_i - z_{i,y_i}) + eps(lse_i - mean_j z_ij)] / p_i
+ *            (0 when y_i == ignore_index)            eps = label_smoothing
+ *   loss   = sum_i l_i / D                           D = 1 (sum) or total (mean)
+ *   g_ij   = s/(p_i D) (softmax_ij - eps/V - (1-eps)[j == y_i])   (0 if ignored)
+ *   dH     = g W,   dW = g^T h                       gradients for d(loss) = 1
+ *
+ * Reading taken where the page is inconsistent: the whole label-smoothed CE of
+ * a row is divided by p_i (the page's gradient divides every term by p_mask;
+ * its printed loss leaves the smoothing term undivided).
+ *
+ * The vocabulary-shard entry points follow the tensor-parallel tutorial page
+ * (daliqc.cn developer article 673292621566021), section 4 "output-layer
+ * embedding": each shard produces per-row softmax partials, the partials are
+ * combined across shards, and each shard then forms its own slice of the
+ * gradient.
+ *
+ * Layouts: all matrices are dense row-major with no padding: h [N,H],
+ * W [V,H] (nn.Linear layout), dH [N,H], dW [V,H].  target is int64 [N];
+ * p_mask is float32 [N] (NULL means all ones).  h, W, dH, dW share one dtype:
+ * FLDCE_DTYPE_F32 or FLDCE_DTYPE_BF16.  Accumulation is float32 in both cases.
+ *
+ * Preconditions not checked on the device (undefined results otherwise):
+ * 0 <= target[i] < V or target[i] == ignore_index; p_mask[i] > 0 on rows that
+ * are not ignored (p_mask of ignored rows is never read as a divisor).
+ *
+ * Error behaviour: every entry point returns FLDCE_OK (0) or a negative
+ * status; on error nothing has been enqueued and no output is touched.
+ * fldce_status_string() gives a static description.  No exception crosses the
+ * ABI.  Results are deterministic: no floating-point atomics are used, every
+ * reduction has a fixed order.
+ *
+ * Thread safety: calls are re-entrant; concurrent calls need distinct
+ * workspaces and outputs.
+ */
+#ifndef FLDCE_H
+#define FLDCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FLDCE_VERSION 1
+
+enum fldce_dtype { FLDCE_DTYPE_F32 = 0, FLDCE_DTYPE_BF16 = 1 };
+
+/* Page 1: reduction "mean" divides by total, "sum" does not. */
+enum fldce_reduction { FLDCE_REDUCTION_SUM = 0, FLDCE_REDUCTION_MEAN = 1 };
+
+enum fldce_status {
+  FLDCE_OK = 0,
+  FLDCE_ERR_NULL_POINTER = -1,   /* a required pointer is NULL                */
+  FLDCE_ERR_BAD_SHAPE = -2,      /* N, H or V out of range, shard outside V   */
+  FLDCE_ERR_BAD_DTYPE = -3,      /* dtype not one of fldce_dtype              */
+  FLDCE_ERR_BAD_ARGUMENT = -4,   /* reduction, label_smoothing or logit_scale */
+  FLDCE_ERR_WORKSPACE = -5,      /* workspace NULL or smaller than required   */
+  FLDCE_ERR_ALIGNMENT = -6,      /* a pointer is not 16-byte aligned          */
+  FLDCE_ERR_HIP = -7,            /* a kernel launch failed                    */
+  FLDCE_ERR_UNSUPPORTED = -8     /* shape the bf16 path does not handle       */
+};
+
+/* Library version (FLDCE_VERSION of the build). */
+int fldce_version(void);
+
+/* Static, human-readable text for a status code. */
+const char* fldce_status_string(int status);
+
+/* Token rows processed per chunk when chunk_rows == 0 is passed: all N rows
+ * while the chunk's logits buffers stay within a fixed budget, else the
+ * largest multiple of 256 that fits.  Page 1 chunks rows to bound the [C, V]
+ * logits buffer; 288 GB of HBM lets one chunk cover every workload here. */
+int64_t fldce_default_chunk_rows(int64_t N, int64_t H, int64_t V);
+
+/* Bytes of device workspace fldce_fwd_bwd needs for these sizes (chunk_rows 0
+ * = default).  Returns 0 for invalid sizes. */
+size_t fldce_workspace_size(int64_t N, int64_t H, int64_t V, int dtype,
+                            int64_t chunk_rows);
+
+/*
+ * Loss and gradients of the fused LM-head cross-entropy (page 1,
+ * fused_linear_cross_entropy_forward: the forward pass computes the loss and
+ * both gradients in one go).
+ *
+ *   h            [N,H] dtype       hidden states (row-major, H contiguous)
+ *   W            [V,H] dtype       LM-head weight
+ *   target       [N]   int64       class index or ignore_index
+ *   p_mask       [N]   float32     masking probability per token; NULL = 1
+ *   ignore_index                   rows with this target contribute nothing
+ *   label_smoothing  0 <= eps <= 1
+ *   logit_scale      s > 0, finite
+ *   reduction        FLDCE_REDUCTION_SUM or FLDCE_REDUCTION_MEAN
+ *   total            divisor for "mean" when > 0; <= 0 counts the rows whose
+ *                    target != ignore_index on the device (no host sync)
+ *   loss         [1]   float32     out: loss (overwritten)
+ *   dH           [N,H] dtype       out: d loss / d h (overwritten)
+ *   dW           [V,H] dtype       out: d loss / d W (overwritten; float32
+ *                                  accumulation, rounded once to dtype)
+ *   row_lse      [N]   float32     optional out (NULL ok): per-row lse
+ *   row_loss     [N]   float32     optional out (NULL ok): per-row l_i
+ *   chunk_rows       rows per chunk, 0 = fldce_default_chunk_rows
+ *   workspace        device scratch of at least fldce_workspace_size bytes
+ *
+ * bf16 requires H % 64 == 0 (FLDCE_ERR_UNSUPPORTED otherwise); all pointers
+ * must be 16-byte aligned.
+ */
+int fldce_fwd_bwd(const void* h, const void* W, const int64_t* target,
+                  const float* p_mask, int64_t N, int64_t H, int64_t V,
+                  int dtype, int64_t ignore_index, float label_smoothing,
+                  float logit_scale, int reduction, int64_t total,
+                  float* loss, void* dH, void* dW, float* row_lse,
+                  float* row_loss, int64_t chunk_rows, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace fldce_shard_partials needs. */
+size_t fldce_shard_partials_workspace_size(int64_t N, int64_t H,
+                                           int64_t V_local, int dtype);
+
+/*
+ * Per-row softmax partials of one vocabulary shard W_local = rows
+ * [vocab_start, vocab_start + V_local) of the full weight (tutorial page,
+ * section 4: each shard sums exp of its own logits; the per-shard maximum is
+ * kept alongside, as in page 1's two-stage logsumexp).  The [N, V_local]
+ * logits are never written to memory.
+ *
+ *   row_max      [N] float32 out   m_i = max_{j in shard} z_ij
+ *   row_sumexp   [N] float32 out   S_i = sum_{j in shard} exp(z_ij - m_i)
+ *   target_logit [N] float32 out   z_{i,y_i} if y_i is in the shard and the
+ *                                  row is not ignored, else 0
+ *   row_sumlogit [N] float32 out   sum_{j in shard} z_ij (NULL ok: skipped;
+ *                                  only needed when label_smoothing > 0)
+ *
+ * Combining over shards: M = max_k m_k, lse = M + log sum_k S_k e^{m_k - M},
+ * z_target = sum_k target_logit_k, sum_j z_ij = sum_k row_sumlogit_k.
+ */
+int fldce_shard_partials(const void* h, const void* W_local,
+                         const int64_t* target, int64_t N, int64_t H,
+                         int64_t V_local, int64_t vocab_start, int dtype,
+                         int64_t ignore_index, float logit_scale,
+                         float* row_max, float* row_sumexp,
+                         float* target_logit, float* row_sumlogit,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* Bytes of workspace fldce_shard_bwd needs (chunk_rows 0 = default). */
+size_t fldce_shard_bwd_workspace_size(int64_t N, int64_t H, int64_t V_local,
+                                      int dtype, int64_t chunk_rows);
+
+/*
+ * Gradient slices of one vocabulary shard given every row's GLOBAL lse
+ * (combined from all shards' partials).  eps/V uses V_global; the target
+ * entry is corrected only when y_i falls inside the shard.
+ *
+ *   lse          [N]         float32 in   global row logsumexp
+ *   total        as fldce_fwd_bwd (the count, when done on the device, is
+ *                over all N rows, which every shard sees)
+ *   dH_partial   [N,H]       float32 out  g[:, shard] W_local; the sum over
+ *                                         shards is dH (tutorial page,
+ *                                         section 1.1: row-split product
+ *                                         summed across devices)
+ *   dW_local     [V_local,H] dtype out    g[:, shard]^T h (complete)
+ */
+int fldce_shard_bwd(const void* h, const void* W_local, const int64_t* target,
+                    const float* p_mask, const float* lse, int64_t N,
+                    int64_t H, int64_t V_local, int64_t vocab_start,
+                    int64_t V_global, int dtype, int64_t ignore_index,
+                    float label_smoothing, float logit_scale, int reduction,
+                    int64_t total, float* dH_partial, void* dW_local,
+                    int64_t chunk_rows, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLDCE_H */

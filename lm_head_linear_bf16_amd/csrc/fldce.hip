@@ -1,0 +1,493 @@
+// libfldce: host side of the C ABI declared in include/fldce.h.
+//
+// Validation, workspace layout, the row-chunk loop and kernel launches on the
+// caller's stream.  No allocation, no host synchronisation.
+//
+// One chunk of C token rows (page 1, fused_linear_cross_entropy_forward: the
+// rows are processed in chunks to bound the [C, V] logits buffer):
+//   1. logits GEMM + softmax partials (+ z stored as bf16 / fp32)
+//   2. per-row combine -> lse, per-row loss, coefficient s / (p_i D)
+//   3. dlogits pass: z -> g in place, and g^T for the dW GEMM
+//   4. dH = g W     (split-K GEMM over the vocabulary + ordered reduction)
+//   5. dW += g^T h  (fp32 across chunks, rounded once at the end)
+// Before the loop: divisor D, W^T, column sums of W (label smoothing), target
+// logits and row sums of z by per-row dot products.  After it: the loss.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <mutex>
+
+#include "../../include/fldce.h"
+#include "fldce_common.h"
+#include "gemm_bf16.h"
+#include "kernels.h"
+
+using namespace fldce;
+
+namespace {
+
+enum Mode { kFwdBwd = 0, kShardPartials = 1, kShardBwd = 2 };
+
+constexpr int64_t kZBudgetBytes = int64_t(16) << 30;  // chunk logits + g^T buffers
+constexpr int kGroupM = 4;
+
+struct Plan {
+  int64_t N = 0, H = 0, V = 0, C = 0, Cp = 0, Vp = 0, nT = 0, nchunks = 0;
+  int64_t esz = 0;
+  int splits = 1;
+  size_t oD = 0, oWT = 0, oColpart = 0, oWsum = 0, oZt = 0, oR = 0, oLse = 0, oRloss = 0,
+         oCoef = 0, oPart = 0, oZ = 0, oGT = 0, oHT = 0, oDHpart = 0, oDW32 = 0;
+  size_t total = 0;
+};
+
+size_t take(size_t& cur, size_t bytes) {
+  const size_t o = cur;
+  cur += (bytes + 255) & ~size_t(255);
+  return o;
+}
+
+int choose_splits(int64_t tiles, int64_t k_tiles) {
+  int best = 1;
+  double bestc = 1e300;
+  for (int S = 1; S <= 8; ++S) {
+    if (k_tiles / S < 8) break;
+    const double waves = std::ceil((double)(tiles * S) / 256.0);
+    const double c = waves / S + 0.02 * S;  // small charge for the fp32 partials traffic
+    if (c < bestc - 1e-12) {
+      bestc = c;
+      best = S;
+    }
+  }
+  return best;
+}
+
+int64_t default_chunk(int64_t N, int64_t V, int64_t esz) {
+  const int64_t Vp = round_up(V, 64);
+  const int64_t per_row = 2 * esz * Vp;  // z/g [C, Vp] + g^T [Vp, C]
+  if (round_up(std::max<int64_t>(N, 1), 64) * per_row <= kZBudgetBytes) return std::max<int64_t>(N, 1);
+  int64_t c = (kZBudgetBytes / per_row) / 256 * 256;
+  return std::max<int64_t>(c, 256);
+}
+
+Plan make_plan(int mode, int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_rows) {
+  Plan p;
+  p.N = N;
+  p.H = H;
+  p.V = V;
+  p.esz = dtype == FLDCE_DTYPE_BF16 ? 2 : 4;
+  p.Vp = round_up(V, 64);
+  p.nT = cdiv(V, 128);
+  const bool bf = dtype == FLDCE_DTYPE_BF16;
+  if (mode == kShardPartials && bf) {
+    p.C = std::max<int64_t>(N, 1);  // logits never stored: one pass over all rows
+  } else {
+    p.C = chunk_rows > 0 ? std::min<int64_t>(chunk_rows, std::max<int64_t>(N, 1))
+                         : default_chunk(N, V, p.esz);
+  }
+  p.Cp = round_up(p.C, 64);
+  p.nchunks = N > 0 ? cdiv(N, p.C) : 0;
+  size_t cur = 0;
+  p.oD = take(cur, 256);
+  p.oColpart = take(cur, (size_t)cdiv(V, 64) * H * 4);
+  p.oWsum = take(cur, (size_t)H * 4);
+  p.oPart = take(cur, (size_t)p.nT * p.C * 8);
+  if (mode == kShardPartials) {
+    if (!bf) p.oZ = take(cur, (size_t)p.C * p.Vp * 4);
+    p.total = cur;
+    return p;
+  }
+  p.oWT = take(cur, (size_t)H * p.Vp * p.esz);
+  p.oZt = take(cur, (size_t)N * 4);
+  p.oR = take(cur, (size_t)N * 4);
+  p.oLse = take(cur, (size_t)N * 4);
+  p.oRloss = take(cur, (size_t)N * 4);
+  p.oCoef = take(cur, (size_t)p.C * 4);
+  p.oZ = take(cur, (size_t)p.Cp * p.Vp * p.esz);
+  p.oGT = take(cur, (size_t)p.Vp * p.Cp * p.esz);
+  p.oHT = take(cur, (size_t)H * p.Cp * p.esz);
+  if (bf) {
+    const int64_t tiles = cdiv(p.C, kBM) * cdiv(H, kBN);
+    p.splits = choose_splits(tiles, p.Vp / kBK);
+    p.oDHpart = take(cur, (size_t)p.splits * p.C * H * 4);
+    if (p.nchunks > 1) p.oDW32 = take(cur, (size_t)V * H * 4);
+  }
+  p.total = cur;
+  return p;
+}
+
+void set_gemm_attributes() {
+  static std::once_flag once;
+  std::call_once(once, [] {
+    (void)hipFuncSetAttribute((const void*)k_logits_bf16<true, true>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
+    (void)hipFuncSetAttribute((const void*)k_logits_bf16<true, false>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
+    (void)hipFuncSetAttribute((const void*)k_logits_bf16<false, true>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
+    (void)hipFuncSetAttribute((const void*)k_gemm_splitk_bf16,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
+    (void)hipFuncSetAttribute((const void*)k_gemm_dw_bf16<0>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
+    (void)hipFuncSetAttribute((const void*)k_gemm_dw_bf16<1>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
+    (void)hipFuncSetAttribute((const void*)k_gemm_dw_bf16<2>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
+    (void)hipFuncSetAttribute((const void*)k_gemm_dw_bf16<3>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
+  });
+}
+
+bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+int check_common(const void* h, const void* W, const int64_t* target, int64_t N, int64_t H,
+                 int64_t V, int dtype, float logit_scale) {
+  if (!W || (N > 0 && (!h || !target))) return FLDCE_ERR_NULL_POINTER;
+  if (dtype != FLDCE_DTYPE_F32 && dtype != FLDCE_DTYPE_BF16) return FLDCE_ERR_BAD_DTYPE;
+  if (N < 0 || H <= 0 || V <= 0 || N > (int64_t(1) << 31) - 1 || V > (int64_t(1) << 31) - 1 ||
+      H > (int64_t(1) << 20))
+    return FLDCE_ERR_BAD_SHAPE;
+  if (!(logit_scale > 0.f) || !std::isfinite(logit_scale)) return FLDCE_ERR_BAD_ARGUMENT;
+  if (dtype == FLDCE_DTYPE_BF16 && H % kBK != 0) return FLDCE_ERR_UNSUPPORTED;
+  return FLDCE_OK;
+}
+
+int launch_status() { return hipGetLastError() == hipSuccess ? FLDCE_OK : FLDCE_ERR_HIP; }
+
+inline unsigned grid1(int64_t n, int64_t per) { return (unsigned)cdiv(n, per); }
+
+template <typename T>
+void launch_transpose(const T* src, int64_t R, int64_t Cn, int64_t lds, T* dst, int64_t ldd,
+                      int64_t Rp, hipStream_t st) {
+  dim3 g((unsigned)cdiv(Rp, 64), (unsigned)cdiv(Cn, 64));
+  k_transpose<T><<<g, 256, 0, st>>>(src, R, Cn, lds, dst, ldd, Rp);
+}
+
+// wsum[c] = sum_j W[j, c] (two ordered passes).
+template <typename T>
+void launch_colsum(const T* W, int64_t V, int64_t H, float* colpart, float* wsum, hipStream_t st) {
+  dim3 g((unsigned)cdiv(V, 64), (unsigned)cdiv(H, 256));
+  k_colsum_slabs<T><<<g, 256, 0, st>>>(W, V, H, colpart);
+  k_colsum_finish<<<grid1(H, 256), 256, 0, st>>>(colpart, cdiv(V, 64), H, wsum);
+}
+
+// Everything of the gradient path that fwd_bwd and shard_bwd share.
+struct Core {
+  const void* h;
+  const void* W;
+  const int64_t* target;
+  const float* p_mask;
+  int64_t N, H, V, v0, Vg;
+  int dtype;
+  int64_t ignore;
+  float eps, s;
+  const float* lse_in;   // shard: given global lse; nullptr: computed (fwd_bwd)
+  float* lse_out;        // fwd_bwd: per-row lse  [N]
+  float* rloss_out;      // fwd_bwd: per-row loss [N]
+  const float* zt;       // fwd_bwd: target logits [N]
+  const float* R;        // fwd_bwd: row sums of z [N] or nullptr
+  const float* D;
+  void* dH;              // [N, H]: h dtype (fwd_bwd) or fp32 (shard)
+  bool dH_f32;
+  void* dW;              // [V, H] W dtype
+};
+
+template <typename T>
+int run_core(const Core& c, const Plan& p, char* ws, hipStream_t st) {
+  const bool bf = sizeof(T) == 2;
+  T* WT = reinterpret_cast<T*>(ws + p.oWT);
+  T* zb = reinterpret_cast<T*>(ws + p.oZ);
+  T* gT = reinterpret_cast<T*>(ws + p.oGT);
+  T* hT = reinterpret_cast<T*>(ws + p.oHT);
+  float* coef = reinterpret_cast<float*>(ws + p.oCoef);
+  floatx2* part = reinterpret_cast<floatx2*>(ws + p.oPart);
+  float* dHpart = reinterpret_cast<float*>(ws + p.oDHpart);
+  float* dW32 = reinterpret_cast<float*>(ws + p.oDW32);
+  const T* h = static_cast<const T*>(c.h);
+  const T* W = static_cast<const T*>(c.W);
+  const int64_t H = c.H, V = c.V, Vp = p.Vp;
+
+  launch_transpose<T>(W, V, H, H, WT, Vp, Vp, st);
+  for (int64_t ic = 0; ic < p.nchunks; ++ic) {
+    const int64_t c0 = ic * p.C;
+    const int64_t Cc = std::min(p.C, c.N - c0);
+    const int64_t Cpc = round_up(Cc, 64);
+    const T* hc = h + c0 * H;
+    launch_transpose<T>(hc, Cc, H, H, hT, p.Cp, Cpc, st);
+    // 1. logits
+    if (bf) {
+      const int blocks = (int)(cdiv(V, kBM) * cdiv(Cc, kBN));
+      if (c.lse_in == nullptr)
+        k_logits_bf16<true, true><<<blocks, kGemmThreads, kGemmLds, st>>>(
+            (const bf16*)W, (const bf16*)hc, (int)V, (int)Cc, (int)H, c.s, part, p.C, (bf16*)zb, Vp,
+            kGroupM);
+      else
+        k_logits_bf16<true, false><<<blocks, kGemmThreads, kGemmLds, st>>>(
+            (const bf16*)W, (const bf16*)hc, (int)V, (int)Cc, (int)H, c.s, part, p.C, (bf16*)zb, Vp,
+            kGroupM);
+    } else {
+      dim3 g((unsigned)cdiv(V, 64), (unsigned)cdiv(Cc, 64));
+      k_gemm_f32_nt<<<g, 256, 0, st>>>((const float*)hc, H, Cc, (const float*)W, H, V, H, c.s,
+                                       (float*)zb, Vp, 0);
+      if (c.lse_in == nullptr) {
+        dim3 g2((unsigned)cdiv(Cc, 64), (unsigned)p.nT);
+        k_row_partials_f32<<<g2, 64, 0, st>>>((const float*)zb, Vp, Cc, V, part, p.C);
+      }
+    }
+    // 2. per-row combine (or coefficients only, when lse is given)
+    const float* lse_c;
+    if (c.lse_in == nullptr) {
+      k_combine_rows<<<grid1(Cc, 32), 256, 0, st>>>(
+          part, p.C, p.nT, Cc, 0, c.target + c0, c.p_mask ? c.p_mask + c0 : nullptr, c.ignore,
+          c.zt + c0, c.R ? c.R + c0 : nullptr, c.eps, (float)c.Vg, c.s, c.D, c.lse_out + c0,
+          c.rloss_out + c0, coef, nullptr, nullptr);
+      lse_c = c.lse_out + c0;
+    } else {
+      k_coef_rows<<<grid1(Cc, 256), 256, 0, st>>>(c.target + c0, c.p_mask ? c.p_mask + c0 : nullptr,
+                                                   c.ignore, Cc, c.s, c.D, coef);
+      lse_c = c.lse_in + c0;
+    }
+    // 3. dlogits, in place, plus g^T
+    {
+      dim3 g((unsigned)(Vp / 64), (unsigned)(Cpc / 64));
+      k_gpass<T><<<g, 256, 0, st>>>(zb, Vp, Cc, V, lse_c, coef, c.target + c0, c.v0, c.eps,
+                                    (float)c.Vg, gT, p.Cp);
+    }
+    // 4. dH = g W
+    if (bf) {
+      const int S = p.splits;
+      const int blocks = (int)(cdiv(Cc, kBM) * cdiv(H, kBN) * S);
+      k_gemm_splitk_bf16<<<blocks, kGemmThreads, kGemmLds, st>>>(
+          (const bf16*)zb, Vp, (int)Cc, (const bf16*)WT, Vp, (int)H, (int)(Vp / kBK), S, dHpart,
+          kGroupM);
+      if (c.dH_f32)
+        k_splitk_reduce<float><<<grid1(Cc * H, 1024), 256, 0, st>>>(dHpart, S, Cc * H,
+                                                                    (float*)c.dH + c0 * H);
+      else
+        k_splitk_reduce<bf16><<<grid1(Cc * H, 1024), 256, 0, st>>>(dHpart, S, Cc * H,
+                                                                   (bf16*)c.dH + c0 * H);
+    } else {
+      dim3 g((unsigned)cdiv(H, 64), (unsigned)cdiv(Cc, 64));
+      k_gemm_f32_nt<<<g, 256, 0, st>>>((const float*)zb, Vp, Cc, (const float*)WT, Vp, H, V, 1.f,
+                                       (float*)c.dH + c0 * H, H, 0);
+    }
+    // 5. dW += g^T h
+    if (bf) {
+      int mode = 0;
+      if (p.nchunks > 1) mode = ic == 0 ? 1 : (ic + 1 == p.nchunks ? 3 : 2);
+      const int blocks = (int)(cdiv(V, kBM) * cdiv(H, kBN));
+      auto kern = mode == 0 ? k_gemm_dw_bf16<0>
+                            : (mode == 1 ? k_gemm_dw_bf16<1> : (mode == 2 ? k_gemm_dw_bf16<2> : k_gemm_dw_bf16<3>));
+      kern<<<blocks, kGemmThreads, kGemmLds, st>>>((const bf16*)gT, p.Cp, (int)V, (const bf16*)hT,
+                                                   p.Cp, (int)H, (int)(Cpc / kBK), (bf16*)c.dW,
+                                                   dW32, kGroupM);
+    } else {
+      dim3 g((unsigned)cdiv(H, 64), (unsigned)cdiv(V, 64));
+      k_gemm_f32_nt<<<g, 256, 0, st>>>((const float*)gT, p.Cp, V, (const float*)hT, p.Cp, H, Cpc,
+                                       1.f, (float*)c.dW, H, ic == 0 ? 0 : 1);
+    }
+  }
+  return launch_status();
+}
+
+void zero_fill(void* p, int64_t n_elems, int esz, hipStream_t st) {
+  if (n_elems <= 0) return;
+  const unsigned g = (unsigned)std::min<int64_t>(cdiv(n_elems, 256), 65536);
+  if (esz == 2)
+    k_fill_u16<<<g, 256, 0, st>>>(static_cast<uint16_t*>(p), n_elems, 0);
+  else
+    k_fill_f32<<<g, 256, 0, st>>>(static_cast<float*>(p), n_elems, 0.f);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fldce_version(void) { return FLDCE_VERSION; }
+
+const char* fldce_status_string(int status) {
+  switch (status) {
+    case FLDCE_OK: return "ok";
+    case FLDCE_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case FLDCE_ERR_BAD_SHAPE: return "N, H, V out of range or shard outside the vocabulary";
+    case FLDCE_ERR_BAD_DTYPE: return "dtype must be FLDCE_DTYPE_F32 or FLDCE_DTYPE_BF16";
+    case FLDCE_ERR_BAD_ARGUMENT: return "reduction, label_smoothing or logit_scale out of range";
+    case FLDCE_ERR_WORKSPACE: return "workspace missing or smaller than the size query returns";
+    case FLDCE_ERR_ALIGNMENT: return "a pointer is not 16-byte aligned";
+    case FLDCE_ERR_HIP: return "a HIP kernel launch failed";
+    case FLDCE_ERR_UNSUPPORTED: return "shape not supported by the bf16 path (H must be a multiple of 64)";
+    default: return "unknown status";
+  }
+}
+
+int64_t fldce_default_chunk_rows(int64_t N, int64_t H, int64_t V) {
+  (void)H;
+  if (N < 0 || V <= 0) return 0;
+  return default_chunk(N, V, 2);
+}
+
+size_t fldce_workspace_size(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_rows) {
+  if (N < 0 || H <= 0 || V <= 0 || (dtype != 0 && dtype != 1)) return 0;
+  return make_plan(kFwdBwd, N, H, V, dtype, chunk_rows).total;
+}
+
+size_t fldce_shard_partials_workspace_size(int64_t N, int64_t H, int64_t V_local, int dtype) {
+  if (N < 0 || H <= 0 || V_local <= 0 || (dtype != 0 && dtype != 1)) return 0;
+  return make_plan(kShardPartials, N, H, V_local, dtype, 0).total;
+}
+
+size_t fldce_shard_bwd_workspace_size(int64_t N, int64_t H, int64_t V_local, int dtype,
+                                      int64_t chunk_rows) {
+  if (N < 0 || H <= 0 || V_local <= 0 || (dtype != 0 && dtype != 1)) return 0;
+  return make_plan(kShardBwd, N, H, V_local, dtype, chunk_rows).total;
+}
+
+int fldce_fwd_bwd(const void* h, const void* W, const int64_t* target, const float* p_mask,
+                  int64_t N, int64_t H, int64_t V, int dtype, int64_t ignore_index,
+                  float label_smoothing, float logit_scale, int reduction, int64_t total,
+                  float* loss, void* dH, void* dW, float* row_lse, float* row_loss,
+                  int64_t chunk_rows, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_common(h, W, target, N, H, V, dtype, logit_scale);
+  if (rc != FLDCE_OK) return rc;
+  if (!loss || !dW || (N > 0 && !dH)) return FLDCE_ERR_NULL_POINTER;
+  if (reduction != FLDCE_REDUCTION_SUM && reduction != FLDCE_REDUCTION_MEAN)
+    return FLDCE_ERR_BAD_ARGUMENT;
+  if (!(label_smoothing >= 0.f && label_smoothing <= 1.f)) return FLDCE_ERR_BAD_ARGUMENT;
+  if (chunk_rows < 0) return FLDCE_ERR_BAD_ARGUMENT;
+  if (!aligned16(h) || !aligned16(W) || !aligned16(target) || !aligned16(p_mask) || !aligned16(dH) ||
+      !aligned16(dW) || !aligned16(workspace))
+    return FLDCE_ERR_ALIGNMENT;
+  const Plan p = make_plan(kFwdBwd, N, H, V, dtype, chunk_rows);
+  if (!workspace || workspace_bytes < p.total) return FLDCE_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  set_gemm_attributes();
+  char* ws = static_cast<char*>(workspace);
+  float* D = reinterpret_cast<float*>(ws + p.oD);
+  const int esz = dtype == FLDCE_DTYPE_BF16 ? 2 : 4;
+  if (N == 0) {
+    zero_fill(loss, 1, 4, st);
+    zero_fill(dW, V * H, esz, st);
+    return launch_status();
+  }
+  k_divisor<<<1, 1024, 0, st>>>(target, N, ignore_index, reduction, total, D);
+  const bool smooth = label_smoothing > 0.f;
+  float* colpart = reinterpret_cast<float*>(ws + p.oColpart);
+  float* wsum = reinterpret_cast<float*>(ws + p.oWsum);
+  float* zt = reinterpret_cast<float*>(ws + p.oZt);
+  float* R = reinterpret_cast<float*>(ws + p.oR);
+  float* lse = row_lse ? row_lse : reinterpret_cast<float*>(ws + p.oLse);
+  float* rl = row_loss ? row_loss : reinterpret_cast<float*>(ws + p.oRloss);
+  Core c{h, W, target, p_mask, N, H, V, 0, V, dtype, ignore_index, label_smoothing, logit_scale,
+         nullptr, lse, rl, zt, smooth ? R : nullptr, D, dH, false, dW};
+  if (dtype == FLDCE_DTYPE_BF16) {
+    if (smooth) launch_colsum<bf16>((const bf16*)W, V, H, colpart, wsum, st);
+    k_rowdot<bf16><<<grid1(N, 4), 256, 0, st>>>((const bf16*)h, (const bf16*)W, H, target, 0, V,
+                                                 ignore_index, logit_scale, smooth ? wsum : nullptr,
+                                                 N, zt, smooth ? R : nullptr);
+    rc = run_core<bf16>(c, p, ws, st);
+  } else {
+    if (smooth) launch_colsum<float>((const float*)W, V, H, colpart, wsum, st);
+    k_rowdot<float><<<grid1(N, 4), 256, 0, st>>>((const float*)h, (const float*)W, H, target, 0, V,
+                                                  ignore_index, logit_scale,
+                                                  smooth ? wsum : nullptr, N, zt,
+                                                  smooth ? R : nullptr);
+    rc = run_core<float>(c, p, ws, st);
+  }
+  if (rc != FLDCE_OK) return rc;
+  k_loss_reduce<<<1, 1024, 0, st>>>(rl, N, D, loss);
+  return launch_status();
+}
+
+int fldce_shard_partials(const void* h, const void* W_local, const int64_t* target, int64_t N,
+                         int64_t H, int64_t V_local, int64_t vocab_start, int dtype,
+                         int64_t ignore_index, float logit_scale, float* row_max,
+                         float* row_sumexp, float* target_logit, float* row_sumlogit,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_common(h, W_local, target, N, H, V_local, dtype, logit_scale);
+  if (rc != FLDCE_OK) return rc;
+  if (N > 0 && (!row_max || !row_sumexp || !target_logit)) return FLDCE_ERR_NULL_POINTER;
+  if (vocab_start < 0) return FLDCE_ERR_BAD_SHAPE;
+  if (!aligned16(h) || !aligned16(W_local) || !aligned16(target) || !aligned16(workspace))
+    return FLDCE_ERR_ALIGNMENT;
+  const Plan p = make_plan(kShardPartials, N, H, V_local, dtype, 0);
+  if (!workspace || workspace_bytes < p.total) return FLDCE_ERR_WORKSPACE;
+  if (N == 0) return FLDCE_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  set_gemm_attributes();
+  char* ws = static_cast<char*>(workspace);
+  floatx2* part = reinterpret_cast<floatx2*>(ws + p.oPart);
+  float* colpart = reinterpret_cast<float*>(ws + p.oColpart);
+  float* wsum = reinterpret_cast<float*>(ws + p.oWsum);
+  const int64_t V = V_local;
+  if (dtype == FLDCE_DTYPE_BF16) {
+    const int blocks = (int)(cdiv(V, kBM) * cdiv(N, kBN));
+    k_logits_bf16<false, true><<<blocks, kGemmThreads, kGemmLds, st>>>(
+        (const bf16*)W_local, (const bf16*)h, (int)V, (int)N, (int)H, logit_scale, part, p.C,
+        nullptr, 0, kGroupM);
+    k_combine_rows<<<grid1(N, 32), 256, 0, st>>>(part, p.C, p.nT, N, 1, nullptr, nullptr, 0, nullptr,
+                                                 nullptr, 0.f, 1.f, 1.f, nullptr, nullptr, nullptr,
+                                                 nullptr, row_max, row_sumexp);
+    if (row_sumlogit) launch_colsum<bf16>((const bf16*)W_local, V, H, colpart, wsum, st);
+    k_rowdot<bf16><<<grid1(N, 4), 256, 0, st>>>((const bf16*)h, (const bf16*)W_local, H, target,
+                                                 vocab_start, V, ignore_index, logit_scale,
+                                                 row_sumlogit ? wsum : nullptr, N, target_logit,
+                                                 row_sumlogit);
+  } else {
+    float* zb = reinterpret_cast<float*>(ws + p.oZ);
+    for (int64_t c0 = 0; c0 < N; c0 += p.C) {
+      const int64_t Cc = std::min(p.C, N - c0);
+      dim3 g((unsigned)cdiv(V, 64), (unsigned)cdiv(Cc, 64));
+      k_gemm_f32_nt<<<g, 256, 0, st>>>((const float*)h + c0 * H, H, Cc, (const float*)W_local, H,
+                                       V, H, logit_scale, zb, p.Vp, 0);
+      dim3 g2((unsigned)cdiv(Cc, 64), (unsigned)p.nT);
+      k_row_partials_f32<<<g2, 64, 0, st>>>(zb, p.Vp, Cc, V, part, p.C);
+      k_combine_rows<<<grid1(Cc, 32), 256, 0, st>>>(part, p.C, p.nT, Cc, 1, nullptr, nullptr, 0,
+                                                    nullptr, nullptr, 0.f, 1.f, 1.f, nullptr,
+                                                    nullptr, nullptr, nullptr, row_max + c0,
+                                                    row_sumexp + c0);
+    }
+    if (row_sumlogit) launch_colsum<float>((const float*)W_local, V, H, colpart, wsum, st);
+    k_rowdot<float><<<grid1(N, 4), 256, 0, st>>>((const float*)h, (const float*)W_local, H, target,
+                                                  vocab_start, V, ignore_index, logit_scale,
+                                                  row_sumlogit ? wsum : nullptr, N, target_logit,
+                                                  row_sumlogit);
+  }
+  return launch_status();
+}
+
+int fldce_shard_bwd(const void* h, const void* W_local, const int64_t* target, const float* p_mask,
+                    const float* lse, int64_t N, int64_t H, int64_t V_local, int64_t vocab_start,
+                    int64_t V_global, int dtype, int64_t ignore_index, float label_smoothing,
+                    float logit_scale, int reduction, int64_t total, float* dH_partial,
+                    void* dW_local, int64_t chunk_rows, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  int rc = check_common(h, W_local, target, N, H, V_local, dtype, logit_scale);
+  if (rc != FLDCE_OK) return rc;
+  if (!dW_local || (N > 0 && (!dH_partial || !lse))) return FLDCE_ERR_NULL_POINTER;
+  if (vocab_start < 0 || V_global < vocab_start + V_local) return FLDCE_ERR_BAD_SHAPE;
+  if (reduction != FLDCE_REDUCTION_SUM && reduction != FLDCE_REDUCTION_MEAN)
+    return FLDCE_ERR_BAD_ARGUMENT;
+  if (!(label_smoothing >= 0.f && label_smoothing <= 1.f)) return FLDCE_ERR_BAD_ARGUMENT;
+  if (chunk_rows < 0) return FLDCE_ERR_BAD_ARGUMENT;
+  if (!aligned16(h) || !aligned16(W_local) || !aligned16(target) || !aligned16(p_mask) ||
+      !aligned16(lse) || !aligned16(dH_partial) || !aligned16(dW_local) || !aligned16(workspace))
+    return FLDCE_ERR_ALIGNMENT;
+  const Plan p = make_plan(kShardBwd, N, H, V_local, dtype, chunk_rows);
+  if (!workspace || workspace_bytes < p.total) return FLDCE_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  set_gemm_attributes();
+  const int esz = dtype == FLDCE_DTYPE_BF16 ? 2 : 4;
+  if (N == 0) {
+    zero_fill(dW_local, V_local * H, esz, st);
+    return launch_status();
+  }
+  char* ws = static_cast<char*>(workspace);
+  float* D = reinterpret_cast<float*>(ws + p.oD);
+  k_divisor<<<1, 1024, 0, st>>>(target, N, ignore_index, reduction, total, D);
+  Core c{h, W_local, target, p_mask, N, H, V_local, vocab_start, V_global, dtype, ignore_index,
+         label_smoothing, logit_scale, lse, nullptr, nullptr, nullptr, nullptr, D, dH_partial,
+         true, dW_local};
+  return dtype == FLDCE_DTYPE_BF16 ? run_core<bf16>(c, p, ws, st) : run_core<float>(c, p, ws, st);
+}
+
+}  // extern "C"

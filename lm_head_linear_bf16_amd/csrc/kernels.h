@@ -1,0 +1,380 @@
+// Memory-bound and per-row kernels of the fused LM-head cross-entropy, plus
+// the fp32 GEMM used when the inputs are float32.  All reductions run in a
+// fixed order (no floating-point atomics), so results repeat bit for bit.
+#pragma once
+
+#include "fldce_common.h"
+
+namespace fldce {
+
+// ---------------------------------------------------------------------------
+// Divisor of the "mean" reduction (model page, fused_linear_cross_entropy_-
+// forward: total = number of targets != ignore_index), computed on the device
+// so no host synchronisation is needed.  D = 1 for "sum"; the caller's total
+// when > 0; else max(count, 1).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void k_divisor(const int64_t* __restrict__ target, int64_t N,
+                                                  int64_t ignore, int reduction, int64_t total,
+                                                  float* __restrict__ D) {
+  __shared__ long long cnt[1024];
+  long long c = 0;
+  if (reduction == 1 && total <= 0)
+    for (int64_t i = threadIdx.x; i < N; i += 1024) c += (target[i] != ignore);
+  cnt[threadIdx.x] = c;
+  __syncthreads();
+  for (int o = 512; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) cnt[threadIdx.x] += cnt[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    float d = 1.f;
+    if (reduction == 1) d = total > 0 ? (float)total : (float)(cnt[0] > 0 ? cnt[0] : 1);
+    *D = d;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dst[c, r] = src[r, c] for r < R, c < Cn; dst[c, r] = 0 for R <= r < Rp.
+// 64 x 64 tiles through LDS.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ src, int64_t R, int64_t Cn,
+                                                   int64_t lds, T* __restrict__ dst, int64_t ldd,
+                                                   int64_t Rp) {
+  __shared__ float tile[64][65];
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int64_t r = r0 + ty + 4 * k, c = c0 + tx;
+    tile[ty + 4 * k][tx] = (r < R && c < Cn) ? to_f32(src[r * lds + c]) : 0.f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int64_t c = c0 + ty + 4 * k, r = r0 + tx;
+    if (c < Cn && r < Rp) dst[c * ldd + r] = from_f32<T>(tile[tx][ty + 4 * k]);
+  }
+}
+
+// Column sums of each 64-row slab of src [R, Cn]: colpart[slab, c] (fixed
+// order).  Used for sum_j W[j, :], which gives the row sums of the logits.
+template <typename T>
+__global__ __launch_bounds__(256) void k_colsum_slabs(const T* __restrict__ src, int64_t R,
+                                                      int64_t Cn, float* __restrict__ colpart) {
+  const int64_t c = (int64_t)blockIdx.y * 256 + threadIdx.x;
+  if (c >= Cn) return;
+  const int64_t r0 = (int64_t)blockIdx.x * 64, r1 = min(R, r0 + 64);
+  float s = 0.f;
+  for (int64_t r = r0; r < r1; ++r) s += to_f32(src[r * Cn + c]);
+  colpart[(int64_t)blockIdx.x * Cn + c] = s;
+}
+
+// out[c] = sum_b part[b, c], b ascending.
+__global__ __launch_bounds__(256) void k_colsum_finish(const float* __restrict__ part, int64_t nb,
+                                                       int64_t Cn, float* __restrict__ out) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= Cn) return;
+  float s = 0.f;
+  for (int64_t b = 0; b < nb; ++b) s += part[b * Cn + c];
+  out[c] = s;
+}
+
+// ---------------------------------------------------------------------------
+// Per-row dot products (one wave per row):
+//   zt[i] = s * <h_i, W[y_i - v0]>  if y_i != ignore and v0 <= y_i < v0 + Vl, else 0
+//   R[i]  = s * <h_i, wsum>         (wsum = column sums of W: sum_j z_ij)
+// The target logit is page 1's cross_entropy_kernel step 3 load of
+// logits[y]; the row sum feeds the label-smoothing term.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void k_rowdot(const T* __restrict__ h, const T* __restrict__ W,
+                                                int64_t H, const int64_t* __restrict__ target,
+                                                int64_t v0, int64_t Vl, int64_t ignore, float s,
+                                                const float* __restrict__ wsum, int64_t N,
+                                                float* __restrict__ zt, float* __restrict__ R) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= N) return;
+  const int64_t y = target[row];
+  const int64_t col = y - v0;
+  const bool in = (y != ignore) && col >= 0 && col < Vl;
+  float a = 0.f, b = 0.f;
+  const T* hr = h + row * H;
+  const T* wr = W + (in ? col : 0) * H;
+  for (int64_t k = lane; k < H; k += 64) {
+    const float x = to_f32(hr[k]);
+    if (in) a += x * to_f32(wr[k]);
+    if (wsum != nullptr) b += x * wsum[k];
+  }
+  a = wave_sum(a);
+  b = wave_sum(b);
+  if (lane == 0) {
+    if (zt != nullptr) zt[row] = in ? s * a : 0.f;
+    if (R != nullptr) R[row] = s * b;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 path: softmax partials over stored logits z [C, ldz]:
+// part[t * ldp + i] = (max, sum exp(z - max)) over columns [128 t, 128 t + 128) ∩ [0, V).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void k_row_partials_f32(const float* __restrict__ z, int64_t ldz,
+                                                         int64_t C, int64_t V,
+                                                         floatx2* __restrict__ part, int64_t ldp) {
+  const int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  const int64_t t = blockIdx.y;
+  if (i >= C) return;
+  const int64_t j0 = t * 128, j1 = min(V, j0 + 128);
+  const float* zr = z + i * ldz;
+  float m = -INFINITY;
+  for (int64_t j = j0; j < j1; ++j) m = fmaxf(m, zr[j]);
+  float sum = 0.f;
+  for (int64_t j = j0; j < j1; ++j) sum += fast_exp2((zr[j] - m) * kLog2e);
+  part[t * ldp + i] = floatx2{m, sum};
+}
+
+// ---------------------------------------------------------------------------
+// Combine the per-slab partials of each row in a fixed order (page 1: the
+// host-side logsumexp over the per-block results of logsumexp_fwd_kernel).
+// 256 threads = 32 rows x 8 slab groups.
+//
+// mode 0 (loss):  lse_i = M + log S, and with p_i, D, eps:
+//     l_i   = [(1-eps)(lse_i - zt_i) + eps(lse_i - R_i / Vg)] / p_i   (0 if ignored)
+//     coef_i = s / (p_i D)                                            (0 if ignored)
+//   (page 1, cross_entropy_kernel steps 4 and the label-smoothing combine;
+//    the whole smoothed CE is divided by p_i).  Writes lse[i], rloss[i],
+//   coef[i] (chunk-local).
+// mode 1 (shard): writes out_m[i] = M, out_s[i] = S (sum relative to M).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_combine_rows(
+    const floatx2* __restrict__ part, int64_t ldp, int64_t nT, int64_t C, int mode,
+    const int64_t* __restrict__ target, const float* __restrict__ p_mask, int64_t ignore,
+    const float* __restrict__ zt, const float* __restrict__ R, float eps, float Vg, float s,
+    const float* __restrict__ D, float* __restrict__ lse_out, float* __restrict__ rloss_out,
+    float* __restrict__ coef_out, float* __restrict__ out_m, float* __restrict__ out_s) {
+  __shared__ float sm[8][32], ss[8][32];
+  const int tx = threadIdx.x & 31, grp = threadIdx.x >> 5;
+  const int64_t i = (int64_t)blockIdx.x * 32 + tx;
+  float m = -INFINITY, sum = 0.f;
+  if (i < C)
+    for (int64_t t = grp; t < nT; t += 8) {
+      const floatx2 p = part[t * ldp + i];
+      lse_merge(m, sum, p[0], p[1]);
+    }
+  sm[grp][tx] = m;
+  ss[grp][tx] = sum;
+  __syncthreads();
+  if (grp != 0 || i >= C) return;
+  for (int g = 1; g < 8; ++g) lse_merge(m, sum, sm[g][tx], ss[g][tx]);
+  if (mode == 1) {
+    out_m[i] = m;
+    out_s[i] = sum;
+    return;
+  }
+  const float lse = m + logf(sum);
+  const bool valid = target[i] != ignore;
+  const float p = (p_mask != nullptr && valid) ? p_mask[i] : 1.f;
+  float l = 0.f, cf = 0.f;
+  if (valid) {
+    const float rs = (R != nullptr) ? R[i] : 0.f;
+    l = ((1.f - eps) * (lse - zt[i]) + eps * (lse - rs / Vg)) / p;
+    cf = s / (p * D[0]);
+  }
+  lse_out[i] = lse;
+  rloss_out[i] = l;
+  coef_out[i] = cf;
+}
+
+// coef_i = s / (p_i D), 0 on ignored rows (shard backward, lse given).
+__global__ __launch_bounds__(256) void k_coef_rows(const int64_t* __restrict__ target,
+                                                   const float* __restrict__ p_mask, int64_t ignore,
+                                                   int64_t C, float s, const float* __restrict__ D,
+                                                   float* __restrict__ coef) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= C) return;
+  const bool valid = target[i] != ignore;
+  const float p = (p_mask != nullptr && valid) ? p_mask[i] : 1.f;
+  coef[i] = valid ? s / (p * D[0]) : 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// dlogits (page 1, cross_entropy_kernel steps 5 and 6): for token i < C and
+// vocabulary column j < V of this shard,
+//   g_ij = coef_i (exp(z_ij - lse_i) - eps/Vg) - coef_i (1 - eps) [j == y_i - v0]
+// and exactly +0 on ignored rows (coef_i == 0), on j >= V and on i >= C.
+// Overwrites z [C, ldz] with g (in place) and writes g^T [ldz rows, ldt]
+// (token columns up to the grid's extent), both in T.  64 tokens x 64
+// columns per block; the grid covers ldz / 64 x ldt / 64 blocks.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
+  const floatx4 a = *(const floatx4*)p, b = *(const floatx4*)(p + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[e] = a[e];
+    v[e + 4] = b[e];
+  }
+}
+__device__ __forceinline__ void load8(const bf16* p, float (&v)[8]) {
+  const bf16x8 a = *(const bf16x8*)p;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (float)a[e];
+}
+__device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
+  *(floatx4*)p = floatx4{v[0], v[1], v[2], v[3]};
+  *(floatx4*)(p + 4) = floatx4{v[4], v[5], v[6], v[7]};
+}
+__device__ __forceinline__ void store8(bf16* p, const float (&v)[8]) {
+  bf16x8 a;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) a[e] = (bf16)v[e];
+  *(bf16x8*)p = a;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_gpass(T* __restrict__ z, int64_t ldz, int64_t C, int64_t V,
+                                               const float* __restrict__ lse,
+                                               const float* __restrict__ coef,
+                                               const int64_t* __restrict__ target, int64_t v0,
+                                               float eps, float Vg, T* __restrict__ gT, int64_t ldt) {
+  // Requires ldz % 64 == 0 (columns j0 .. j0+63 allocated) and ldt % 64 == 0.
+  __shared__ float tile[64][65];
+  const int64_t i0 = (int64_t)blockIdx.y * 64, j0 = (int64_t)blockIdx.x * 64;
+  const int tx = threadIdx.x & 7, ty = threadIdx.x >> 3;  // 8 threads x 8 columns per row
+  const float epsV = eps / Vg;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int li = ty + pass * 32;
+    const int64_t i = i0 + li;
+    float g[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) g[e] = 0.f;
+    if (i < C) {
+      const float cf = coef[i];
+      if (cf != 0.f) {
+        const float l2 = lse[i] * kLog2e;
+        const int64_t yc = target[i] - v0;
+        const float tgt = cf * (1.f - eps);
+        float zv[8];
+        load8(z + i * ldz + j0 + tx * 8, zv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int64_t j = j0 + tx * 8 + e;
+          float v = cf * (fast_exp2(__builtin_fmaf(zv[e], kLog2e, -l2)) - epsV);
+          if (j == yc) v -= tgt;
+          g[e] = (j < V) ? v : 0.f;
+        }
+      }
+      store8(z + i * ldz + j0 + tx * 8, g);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tile[li][tx * 8 + e] = g[e];
+  }
+  __syncthreads();
+  // transpose out: thread -> vocabulary row j0 + ty (+32), 8 tokens from i0 + tx * 8
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int lj = ty + pass * 32;
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = tile[tx * 8 + e][lj];
+    store8(gT + (j0 + lj) * ldt + i0 + tx * 8, v);
+  }
+}
+
+// out[e] = sum_{s < S} part[s * MN + e], s ascending; cast to Tout.
+template <typename Tout>
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ part, int S,
+                                                       int64_t MN, Tout* __restrict__ out) {
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= MN) return;
+  if (e + 4 <= MN) {
+    floatx4 acc = *(const floatx4*)(part + e);
+    for (int s = 1; s < S; ++s) acc += *(const floatx4*)(part + (int64_t)s * MN + e);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) out[e + k] = from_f32<Tout>(acc[k]);
+  } else {
+    for (int64_t k = e; k < MN; ++k) {
+      float a = part[k];
+      for (int s = 1; s < S; ++s) a += part[(int64_t)s * MN + k];
+      out[k] = from_f32<Tout>(a);
+    }
+  }
+}
+
+// loss = (sum_i rloss[i]) / D, float64 partial sums, fixed tree (page 1:
+// loss.sum() of the per-row losses).
+__global__ __launch_bounds__(1024) void k_loss_reduce(const float* __restrict__ rloss, int64_t N,
+                                                      const float* __restrict__ D,
+                                                      float* __restrict__ loss) {
+  __shared__ double sh[1024];
+  double a = 0.0;
+  for (int64_t i = threadIdx.x; i < N; i += 1024) a += (double)rloss[i];
+  sh[threadIdx.x] = a;
+  __syncthreads();
+  for (int o = 512; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) sh[threadIdx.x] += sh[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *loss = (float)(sh[0] / (double)D[0]);
+}
+
+__global__ __launch_bounds__(256) void k_fill_u16(uint16_t* __restrict__ p, int64_t n, uint16_t v) {
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) p[e] = v;
+}
+__global__ __launch_bounds__(256) void k_fill_f32(float* __restrict__ p, int64_t n, float v) {
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) p[e] = v;
+}
+
+// ---------------------------------------------------------------------------
+// fp32 NT GEMM (float32 inputs only): out[m, n] = alpha * sum_k A[m,k] B[n,k]
+// (+ out[m, n] if accumulate).  64 x 64 tiles, 4 x 4 per thread, any sizes.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_gemm_f32_nt(const float* __restrict__ A, int64_t lda,
+                                                     int64_t M, const float* __restrict__ B,
+                                                     int64_t ldb, int64_t N, int64_t K, float alpha,
+                                                     float* __restrict__ out, int64_t ldo,
+                                                     int accumulate) {
+  __shared__ float As[16][64 + 4], Bs[16][64 + 4];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int64_t m0 = (int64_t)blockIdx.y * 64, n0 = (int64_t)blockIdx.x * 64;
+  float acc[4][4] = {};
+  for (int64_t k0 = 0; k0 < K; k0 += 16) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = threadIdx.x + q * 256;  // 0..1023 -> row idx/16, k idx%16
+      const int r = idx >> 4, kk = idx & 15;
+      const int64_t ma = m0 + r, nb = n0 + r, k = k0 + kk;
+      As[kk][r] = (ma < M && k < K) ? A[ma * lda + k] : 0.f;
+      Bs[kk][r] = (nb < N && k < K) ? B[nb * ldb + k] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        a[u] = As[kk][ty * 4 + u];
+        b[u] = Bs[kk][tx * 4 + u];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[u][v] = __builtin_fmaf(a[u], b[v], acc[u][v]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t m = m0 + ty * 4 + u, n = n0 + tx * 4 + v;
+      if (m < M && n < N) {
+        float r = alpha * acc[u][v];
+        if (accumulate) r += out[m * ldo + n];
+        out[m * ldo + n] = r;
+      }
+    }
+}
+
+}  // namespace fldce

@@ -1,0 +1,225 @@
+"""Thin ctypes binding of libfldce.so (the C ABI in include/fldce.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+library.  PyTorch supplies device memory (inputs, outputs, workspace) and the
+current HIP stream.  If the library is missing the first call raises; there is
+no fallback implementation.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfldce.so")
+
+DTYPE_F32, DTYPE_BF16 = 0, 1
+REDUCTION_SUM, REDUCTION_MEAN = 0, 1
+
+_c_int, _c_i64, _c_f, _c_p, _c_sz = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+# name -> (restype, argtypes); every function the header declares
+_SIGNATURES = {
+    "fldce_version": (_c_int, []),
+    "fldce_status_string": (ctypes.c_char_p, [_c_int]),
+    "fldce_default_chunk_rows": (_c_i64, [_c_i64, _c_i64, _c_i64]),
+    "fldce_workspace_size": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_int, _c_i64]),
+    "fldce_fwd_bwd": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_int, _c_i64,
+                               _c_f, _c_f, _c_int, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64,
+                               _c_p, _c_sz, _c_p]),
+    "fldce_shard_partials_workspace_size": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_int]),
+    "fldce_shard_partials": (_c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_int,
+                                      _c_i64, _c_f, _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "fldce_shard_bwd_workspace_size": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_int, _c_i64]),
+    "fldce_shard_bwd": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64,
+                                 _c_i64, _c_int, _c_i64, _c_f, _c_f, _c_int, _c_i64, _c_p, _c_p,
+                                 _c_i64, _c_p, _c_sz, _c_p]),
+}
+
+_lib = None
+
+
+class FldceError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: status {status} ({status_string(status)})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfldce.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().fldce_status_string(status).decode()
+
+
+def fldce_version() -> int:
+    return lib().fldce_version()
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return DTYPE_F32
+    if t == torch.bfloat16:
+        return DTYPE_BF16
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def _reduction_code(r) -> int:
+    if r in ("sum", REDUCTION_SUM):
+        return REDUCTION_SUM
+    if r in ("mean", REDUCTION_MEAN):
+        return REDUCTION_MEAN
+    raise ValueError(f"reduction must be 'mean' or 'sum', got {r!r}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check(t: torch.Tensor, name: str, dtype=None) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _workspace(nbytes: int, dev, ws: Optional[torch.Tensor]) -> torch.Tensor:
+    if ws is not None:
+        if ws.numel() * ws.element_size() < nbytes:
+            raise ValueError(f"workspace too small: need {nbytes} bytes")
+        return ws
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+
+
+def fldce_default_chunk_rows(N: int, H: int, V: int) -> int:
+    return lib().fldce_default_chunk_rows(N, H, V)
+
+
+def fldce_workspace_size(N: int, H: int, V: int, dtype, chunk_rows: int = 0) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    return lib().fldce_workspace_size(N, H, V, code, chunk_rows)
+
+
+def fldce_shard_partials_workspace_size(N: int, H: int, V_local: int, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    return lib().fldce_shard_partials_workspace_size(N, H, V_local, code)
+
+
+def fldce_shard_bwd_workspace_size(N: int, H: int, V_local: int, dtype, chunk_rows: int = 0) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    return lib().fldce_shard_bwd_workspace_size(N, H, V_local, code, chunk_rows)
+
+
+def fldce_fwd_bwd(h: torch.Tensor, W: torch.Tensor, target: torch.Tensor,
+                  p_mask: Optional[torch.Tensor] = None, ignore_index: int = -100,
+                  label_smoothing: float = 0.0, logit_scale: float = 1.0,
+                  reduction="mean", total: int = 0, chunk_rows: int = 0,
+                  row_stats: bool = False, workspace: Optional[torch.Tensor] = None,
+                  out: Optional[dict] = None) -> dict:
+    """loss, dH, dW (and per-row lse / loss with row_stats) of the fused LM-head
+    cross-entropy.  h [N,H], W [V,H] (fp32 or bf16, same dtype), target int64
+    [N], p_mask fp32 [N] or None.  Outputs may be passed in ``out``."""
+    N, H = h.shape
+    V = W.shape[0]
+    _check(h, "h")
+    _check(W, "W", h.dtype)
+    _check(target, "target", torch.int64)
+    if p_mask is not None:
+        _check(p_mask, "p_mask", torch.float32)
+    dev = h.device
+    code = _dtype_code(h.dtype)
+    o = dict(out or {})
+    loss = o.get("loss") if o.get("loss") is not None else torch.empty(1, dtype=torch.float32, device=dev)
+    dH = o.get("dH") if o.get("dH") is not None else torch.empty_like(h)
+    dW = o.get("dW") if o.get("dW") is not None else torch.empty_like(W)
+    lse = rl = None
+    if row_stats:
+        lse = torch.empty(N, dtype=torch.float32, device=dev)
+        rl = torch.empty(N, dtype=torch.float32, device=dev)
+    nbytes = lib().fldce_workspace_size(N, H, V, code, chunk_rows)
+    ws = _workspace(nbytes, dev, workspace)
+    rc = lib().fldce_fwd_bwd(_ptr(h), _ptr(W), _ptr(target), _ptr(p_mask), N, H, V, code,
+                             ignore_index, label_smoothing, logit_scale,
+                             _reduction_code(reduction), total, _ptr(loss), _ptr(dH), _ptr(dW),
+                             _ptr(lse), _ptr(rl), chunk_rows, _ptr(ws), nbytes, _stream(dev))
+    if rc != 0:
+        raise FldceError(rc, "fldce_fwd_bwd")
+    r = dict(loss=loss, dH=dH, dW=dW)
+    if row_stats:
+        r.update(row_lse=lse, row_loss=rl)
+    return r
+
+
+def fldce_shard_partials(h: torch.Tensor, W_local: torch.Tensor, target: torch.Tensor,
+                         vocab_start: int, ignore_index: int = -100, logit_scale: float = 1.0,
+                         sumlogit: bool = True, workspace: Optional[torch.Tensor] = None) -> dict:
+    """Per-row (max, sum-exp, target logit, sum of logits) of one vocabulary shard."""
+    N, H = h.shape
+    V_local = W_local.shape[0]
+    _check(h, "h")
+    _check(W_local, "W_local", h.dtype)
+    _check(target, "target", torch.int64)
+    dev = h.device
+    code = _dtype_code(h.dtype)
+    f = lambda: torch.empty(N, dtype=torch.float32, device=dev)  # noqa: E731
+    m, S, t = f(), f(), f()
+    r = f() if sumlogit else None
+    nbytes = lib().fldce_shard_partials_workspace_size(N, H, V_local, code)
+    ws = _workspace(nbytes, dev, workspace)
+    rc = lib().fldce_shard_partials(_ptr(h), _ptr(W_local), _ptr(target), N, H, V_local,
+                                    vocab_start, code, ignore_index, logit_scale, _ptr(m),
+                                    _ptr(S), _ptr(t), _ptr(r), _ptr(ws), nbytes, _stream(dev))
+    if rc != 0:
+        raise FldceError(rc, "fldce_shard_partials")
+    return dict(row_max=m, row_sumexp=S, target_logit=t, row_sumlogit=r)
+
+
+def fldce_shard_bwd(h: torch.Tensor, W_local: torch.Tensor, target: torch.Tensor,
+                    p_mask: Optional[torch.Tensor], lse: torch.Tensor, vocab_start: int,
+                    V_global: int, ignore_index: int = -100, label_smoothing: float = 0.0,
+                    logit_scale: float = 1.0, reduction="mean", total: int = 0,
+                    chunk_rows: int = 0, workspace: Optional[torch.Tensor] = None) -> dict:
+    """dH_partial (fp32) and dW_local of one vocabulary shard given the global lse."""
+    N, H = h.shape
+    V_local = W_local.shape[0]
+    _check(h, "h")
+    _check(W_local, "W_local", h.dtype)
+    _check(target, "target", torch.int64)
+    _check(lse, "lse", torch.float32)
+    if p_mask is not None:
+        _check(p_mask, "p_mask", torch.float32)
+    dev = h.device
+    code = _dtype_code(h.dtype)
+    dHp = torch.empty((N, H), dtype=torch.float32, device=dev)
+    dWl = torch.empty_like(W_local)
+    nbytes = lib().fldce_shard_bwd_workspace_size(N, H, V_local, code, chunk_rows)
+    ws = _workspace(nbytes, dev, workspace)
+    rc = lib().fldce_shard_bwd(_ptr(h), _ptr(W_local), _ptr(target), _ptr(p_mask), _ptr(lse), N,
+                               H, V_local, vocab_start, V_global, code, ignore_index,
+                               label_smoothing, logit_scale, _reduction_code(reduction), total,
+                               _ptr(dHp), _ptr(dWl), chunk_rows, _ptr(ws), nbytes, _stream(dev))
+    if rc != 0:
+        raise FldceError(rc, "fldce_shard_bwd")
+    return dict(dH_partial=dHp, dW_local=dWl)

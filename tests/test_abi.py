@@ -1,0 +1,129 @@
+"""The C-ABI library loads, exports every symbol include/fldce.h declares, and
+rejects invalid arguments before touching the GPU.  CPU only: no compute call
+reaches a kernel here (every call below fails host-side validation)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from lm_head_linear_bf16_amd import fldce
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fldce.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fldce_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(fldce.LIB_PATH):
+        pytest.skip("libfldce.so not built")
+    return fldce.lib()
+
+
+def test_every_declared_symbol_is_exported_and_bound(L):
+    names = _declared()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in fldce._SIGNATURES, f"binding lacks {n}"
+        assert hasattr(fldce, n) or n in ("fldce_status_string",), f"python name {n}"
+
+
+def test_status_strings(L):
+    assert fldce.status_string(0) == "ok"
+    for s in range(-8, 0):
+        assert fldce.status_string(s) != "unknown status"
+    assert fldce.status_string(-99) == "unknown status"
+    assert fldce.fldce_version() == 1
+
+
+def test_workspace_queries(L):
+    a = fldce.fldce_workspace_size(8192, 2560, 151936, 1)
+    b = fldce.fldce_workspace_size(8192, 2560, 151936, 1, 1024)
+    assert a > b > 0
+    assert fldce.fldce_workspace_size(0, 64, 10, 1) > 0
+    assert fldce.fldce_workspace_size(-1, 64, 10, 1) == 0
+    assert fldce.fldce_workspace_size(10, 64, 10, 7) == 0
+    assert fldce.fldce_shard_partials_workspace_size(32768, 5120, 18992, 1) > 0
+    assert fldce.fldce_shard_bwd_workspace_size(32768, 5120, 18992, 1) > 0
+    assert fldce.fldce_default_chunk_rows(8192, 2560, 151936) == 8192
+    # a vocabulary too large for one chunk of all rows gets a multiple of 256
+    c = fldce.fldce_default_chunk_rows(1 << 20, 4096, 151936)
+    assert 0 < c < (1 << 20) and c % 256 == 0
+
+
+P = 0x10000          # fake, aligned "device" addresses: validation fails first
+BAD = 0x10001        # misaligned
+
+
+def _fwd(L, **kw):
+    a = dict(h=P, W=P, target=P, p_mask=None, N=16, H=64, V=100, dtype=1, ignore=-100, eps=0.0,
+             s=1.0, red=1, total=0, loss=P, dH=P, dW=P, lse=None, rl=None, chunk=0, ws=P,
+             wsb=1 << 40, stream=None)
+    a.update(kw)
+    return L.fldce_fwd_bwd(a["h"], a["W"], a["target"], a["p_mask"], a["N"], a["H"], a["V"],
+                           a["dtype"], a["ignore"], a["eps"], a["s"], a["red"], a["total"],
+                           a["loss"], a["dH"], a["dW"], a["lse"], a["rl"], a["chunk"], a["ws"],
+                           a["wsb"], a["stream"])
+
+
+def test_fwd_bwd_argument_checks(L):
+    assert _fwd(L, W=None) == -1
+    assert _fwd(L, h=None) == -1
+    assert _fwd(L, loss=None) == -1
+    assert _fwd(L, dtype=3) == -3
+    assert _fwd(L, N=-1) == -2
+    assert _fwd(L, V=0) == -2
+    assert _fwd(L, H=0) == -2
+    assert _fwd(L, red=2) == -4
+    assert _fwd(L, eps=-0.1) == -4
+    assert _fwd(L, eps=1.5) == -4
+    assert _fwd(L, eps=float("nan")) == -4
+    assert _fwd(L, s=0.0) == -4
+    assert _fwd(L, s=-1.0) == -4
+    assert _fwd(L, s=float("inf")) == -4
+    assert _fwd(L, chunk=-5) == -4
+    assert _fwd(L, h=BAD) == -6
+    assert _fwd(L, dW=BAD) == -6
+    assert _fwd(L, wsb=16) == -5
+    assert _fwd(L, ws=None) == -5
+    assert _fwd(L, H=100) == -8          # bf16 needs H % 64 == 0
+    assert _fwd(L, H=100, dtype=0, wsb=16) == -5   # fp32 takes any H (fails later on workspace)
+
+
+def test_shard_argument_checks(L):
+    f = L.fldce_shard_partials
+    assert f(P, P, P, 16, 64, 100, -1, 1, -100, 1.0, P, P, P, None, P, 1 << 40, None) == -2
+    assert f(P, P, P, 16, 64, 100, 0, 1, -100, 1.0, None, P, P, None, P, 1 << 40, None) == -1
+    assert f(P, P, P, 16, 64, 100, 0, 1, -100, 0.0, P, P, P, None, P, 1 << 40, None) == -4
+    assert f(P, P, P, 16, 64, 100, 0, 1, -100, 1.0, P, P, P, None, P, 8, None) == -5
+    b = L.fldce_shard_bwd
+    base = [P, P, P, None, P, 16, 64, 100, 0, 1000, 1, -100, 0.0, 1.0, 1, 0, P, P, 0, P, 1 << 40, None]
+
+    def call(**over):
+        a = list(base)
+        idx = dict(vocab_start=8, V_global=9, red=14, eps=12, lse=4, ws_bytes=20, dHp=16)
+        for k, v in over.items():
+            a[idx[k]] = v
+        return b(*a)
+    assert call(V_global=50) == -2        # shard [0, 100) outside a 50-row vocabulary
+    assert call(vocab_start=950) == -2
+    assert call(red=5) == -4
+    assert call(eps=2.0) == -4
+    assert call(lse=None) == -1
+    assert call(dHp=BAD) == -6
+    assert call(ws_bytes=1) == -5
+
+
+def test_binding_rejects_host_tensors():
+    torch = pytest.importorskip("torch")
+    h = torch.zeros(4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fldce.fldce_fwd_bwd(h, h, torch.zeros(4, dtype=torch.int64))

@@ -1,0 +1,224 @@
+"""HIP path vs the float64 oracle, element by element, at sizes the oracle
+finishes in seconds (several 256-wide tiles and ragged tails), through the C
+ABI.  Edge cases: vocabulary not a multiple of 64/128/256, token count not a
+multiple of the tile, several row chunks, all rows ignored, no rows, no
+p_mask, fp32 inputs with any H, vocabulary shards."""
+
+import numpy as np
+import pytest
+
+import oracle as O
+from lm_head_linear_bf16_amd import synth
+from _helpers import GRAD_RTOL, LOSS_RTOL, grad_err, host, say, to_dev, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(w, chunk_rows=0, p_none=False, target=None, p_mask=None, h=None, W=None):
+    torch = torch_cuda()
+    from lm_head_linear_bf16_amd import fldce
+    dev = torch.device("cuda:0")
+    if target is None:
+        target, p_mask = synth.targets(w)
+    h = h or synth.hidden(w)
+    W = W or synth.weight(w)
+    say(f"case {w.name}: N={w.N} H={w.H} V={w.V} {w.dtype} eps={w.label_smoothing} "
+        f"s={w.logit_scale} {w.reduction} total={w.total} chunk={chunk_rows}")
+    r = fldce.fldce_fwd_bwd(to_dev(h, dev), to_dev(W, dev), torch.from_numpy(target).to(dev),
+                            None if p_none else torch.from_numpy(p_mask).to(dev),
+                            label_smoothing=w.label_smoothing, logit_scale=w.logit_scale,
+                            reduction=w.reduction, total=w.total, chunk_rows=chunk_rows,
+                            row_stats=True)
+    torch.cuda.synchronize()
+    o = O.forward_backward(h.values, W.values, target, None if p_none else p_mask,
+                           label_smoothing=w.label_smoothing, logit_scale=w.logit_scale,
+                           reduction=w.reduction, total=w.total or None)
+    return r, o, target
+
+
+def _compare(w, r, o, target):
+    loss = float(r["loss"].item())
+    if o["loss"] == 0.0:
+        assert loss == 0.0
+    else:
+        assert abs(loss - o["loss"]) <= LOSS_RTOL[w.dtype] * abs(o["loss"]), (loss, o["loss"])
+    ig = target == -100
+    dH = host(r["dH"])
+    assert np.all(dH[ig] == 0.0), "ignored rows must have exactly zero dH"
+    assert not np.any(np.signbit(r["dH"].float().cpu().numpy()[ig])), "ignored dH rows are +0"
+    assert np.all(host(r["row_loss"])[ig] == 0.0)
+    if o["loss"] != 0.0:
+        assert grad_err(dH, o["dH"]) <= GRAD_RTOL[w.dtype]
+        assert grad_err(host(r["dW"]), o["dW"]) <= GRAD_RTOL[w.dtype]
+        valid = ~ig
+        np.testing.assert_allclose(host(r["row_lse"])[valid], o["lse"][valid], rtol=0,
+                                   atol=2e-3 if w.dtype == "bf16" else 2e-5)
+    else:
+        assert np.all(host(r["dW"]) == 0.0)
+
+
+CASES = [
+    synth.custom("ragged_bf16", 3, 100, 128, 1000),
+    synth.custom("smooth_sum_bf16", 3, 171, 192, 2053, label_smoothing=0.1, logit_scale=0.5,
+                 reduction="sum"),
+    synth.custom("count_mean_bf16", 2, 320, 256, 4099, label_smoothing=0.3, logit_scale=1.7,
+                 total_is_N=False),
+    synth.custom("block_pad_bf16", 4, 96, 128, 777, p_block=4, pad_tail=17, total_is_N=False),
+]
+
+
+@pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
+def test_bf16_small(w):
+    r, o, t = _run(w)
+    _compare(w, r, o, t)
+
+
+@pytest.mark.parametrize("chunk", [64, 256, 300])
+def test_bf16_chunked(chunk):
+    w = synth.custom("chunked_bf16", 7, 100, 128, 1500, label_smoothing=0.1, logit_scale=0.5)
+    r, o, t = _run(w, chunk_rows=chunk)
+    _compare(w, r, o, t)
+
+
+def test_fp32_tiny_workload():
+    w = synth.WORKLOADS["tiny"]
+    r, o, t = _run(w)
+    _compare(w, r, o, t)
+
+
+@pytest.mark.parametrize("chunk", [0, 32])
+def test_fp32_any_H(chunk):
+    w = synth.custom("fp32_odd", 1, 77, 50, 333, dtype="f32", label_smoothing=0.2,
+                     logit_scale=0.7, reduction="sum")
+    r, o, t = _run(w, chunk_rows=chunk)
+    _compare(w, r, o, t)
+
+
+def test_p_mask_none_is_ones():
+    w = synth.custom("nopmask_bf16", 2, 128, 128, 600)
+    r, o, t = _run(w, p_none=True)
+    _compare(w, r, o, t)
+
+
+def test_all_ignored():
+    w = synth.custom("all_ignored_bf16", 1, 200, 128, 500, total_is_N=False)
+    t = np.full(w.N, -100, dtype=np.int64)
+    p = np.zeros(w.N, dtype=np.float32)      # never read on ignored rows
+    r, o, _ = _run(w, target=t, p_mask=p)
+    assert o["loss"] == 0.0
+    _compare(w, r, o, t)
+
+
+def test_empty_batch():
+    torch = torch_cuda()
+    from lm_head_linear_bf16_amd import fldce
+    dev = torch.device("cuda:0")
+    say("case empty: N=0")
+    W = torch.randn(300, 128, device=dev).to(torch.bfloat16)
+    h = torch.empty(0, 128, device=dev, dtype=torch.bfloat16)
+    t = torch.empty(0, dtype=torch.int64, device=dev)
+    dW = torch.full_like(W, 7.0)
+    r = fldce.fldce_fwd_bwd(h, W, t, out={"dW": dW})
+    torch.cuda.synchronize()
+    assert r["loss"].item() == 0.0 and torch.all(r["dW"] == 0)
+
+
+def test_ignored_rows_do_not_leak():
+    """Changing h and p_mask of ignored rows leaves loss and dW bit-identical."""
+    torch = torch_cuda()
+    from lm_head_linear_bf16_amd import fldce
+    dev = torch.device("cuda:0")
+    w = synth.custom("leak_bf16", 2, 150, 128, 900, label_smoothing=0.1)
+    t, p = synth.targets(w)
+    h, W = synth.hidden(w), synth.weight(w)
+    say("case ignored-leak")
+    hd, Wd = to_dev(h, dev), to_dev(W, dev)
+    td, pd = torch.from_numpy(t).to(dev), torch.from_numpy(p).to(dev)
+    a = fldce.fldce_fwd_bwd(hd, Wd, td, pd, label_smoothing=0.1, total=w.N)
+    ig = torch.from_numpy(t == -100).to(dev)
+    h2 = hd.clone()
+    h2[ig] = 3.0
+    p2 = pd.clone()
+    p2[ig] = 0.0
+    b = fldce.fldce_fwd_bwd(h2, Wd, td, p2, label_smoothing=0.1, total=w.N)
+    torch.cuda.synchronize()
+    assert torch.equal(a["loss"], b["loss"])
+    assert torch.equal(a["dW"], b["dW"])
+    assert torch.equal(a["dH"], b["dH"])
+
+
+def test_deterministic_repeat():
+    torch = torch_cuda()
+    from lm_head_linear_bf16_amd import fldce
+    dev = torch.device("cuda:0")
+    w = synth.custom("repeat_bf16", 4, 200, 256, 3000, label_smoothing=0.1, logit_scale=0.5)
+    t, p = synth.targets(w)
+    args = (to_dev(synth.hidden(w), dev), to_dev(synth.weight(w), dev),
+            torch.from_numpy(t).to(dev), torch.from_numpy(p).to(dev))
+    say("case repeat")
+    a = fldce.fldce_fwd_bwd(*args, label_smoothing=0.1, logit_scale=0.5, total=w.N)
+    b = fldce.fldce_fwd_bwd(*args, label_smoothing=0.1, logit_scale=0.5, total=w.N)
+    torch.cuda.synchronize()
+    for k in ("loss", "dH", "dW"):
+        assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_vocab_shards_match_full_vocab(dtype):
+    """Three shards of a 1200-row vocabulary: partials vs the oracle's, host
+    combine vs the full-vocabulary oracle, shard backward vs the oracle's, and
+    the shard gradients reassemble the full dH and dW."""
+    torch = torch_cuda()
+    from lm_head_linear_bf16_amd import fldce
+    dev = torch.device("cuda:0")
+    w = synth.custom("shards_" + dtype, 3, 110, 128, 1200, dtype=dtype, shards=3,
+                     label_smoothing=0.1, logit_scale=0.5)
+    t, p = synth.targets(w)
+    h = synth.hidden(w)
+    Wfull = synth.weight(w)
+    hd, td, pd = to_dev(h, dev), torch.from_numpy(t).to(dev), torch.from_numpy(p).to(dev)
+    full = O.forward_backward(h.values, Wfull.values, t, p, label_smoothing=0.1, logit_scale=0.5,
+                              total=w.N)
+    parts = []
+    tol = 1e-5 if dtype == "f32" else 2e-3
+    for k in range(3):
+        Wk = synth.weight(w, shard=k)
+        v0 = k * w.V_local
+        say(f"case shard partials k={k} {dtype}")
+        r = fldce.fldce_shard_partials(hd, to_dev(Wk, dev), td, v0, logit_scale=0.5)
+        torch.cuda.synchronize()
+        m, S, tl, rs = (host(r[x]) for x in ("row_max", "row_sumexp", "target_logit", "row_sumlogit"))
+        om, oS, ot, orr = O.shard_partials(h.values, Wk.values, t, v0, 0.5)
+        np.testing.assert_allclose(m, om, atol=tol * 4, rtol=0)
+        np.testing.assert_allclose(np.log(S) + m, np.log(oS) + om, atol=tol * 4, rtol=0)
+        np.testing.assert_allclose(tl, ot, atol=tol * 4, rtol=0)
+        np.testing.assert_allclose(rs, orr, atol=tol * 40, rtol=tol)
+        assert np.all(tl[(t < v0) | (t >= v0 + w.V_local)] == 0.0)
+        parts.append((m, S, tl, rs))
+    lse, zt, zs = O.combine_shard_partials(parts)
+    np.testing.assert_allclose(lse, full["lse"], atol=tol * 4, rtol=0)
+    valid = t != -100
+    rl = O.row_losses(lse, zt, zs, w.V, p, valid, 0.1)
+    loss = O.loss_from_row_losses(rl, float(w.N))
+    assert abs(loss - full["loss"]) <= LOSS_RTOL[dtype] * abs(full["loss"])
+    # shard backward from the oracle's global lse
+    lse_d = torch.from_numpy(full["lse"].astype(np.float32)).to(dev)
+    dH = np.zeros_like(full["dH"])
+    dWs = []
+    for k in range(3):
+        Wk = synth.weight(w, shard=k)
+        v0 = k * w.V_local
+        say(f"case shard bwd k={k} {dtype}")
+        r = fldce.fldce_shard_bwd(hd, to_dev(Wk, dev), td, pd, lse_d, v0, w.V,
+                                  label_smoothing=0.1, logit_scale=0.5, total=w.N)
+        torch.cuda.synchronize()
+        odh, odw = O.shard_backward(h.values, Wk.values, t, p, full["lse"], v0, w.V, float(w.N),
+                                    0.1, 0.5)
+        gh, gw = host(r["dH_partial"]), host(r["dW_local"])
+        assert grad_err(gh, odh) <= GRAD_RTOL[dtype]
+        assert grad_err(gw, odw) <= GRAD_RTOL[dtype]
+        assert np.all(gh[~valid] == 0.0)
+        dH += gh
+        dWs.append(gw)
+    assert grad_err(dH, full["dH"]) <= GRAD_RTOL[dtype]
+    assert grad_err(np.concatenate(dWs), full["dW"]) <= GRAD_RTOL[dtype]
