@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Throughput of the fused LM-head cross-entropy forward+backward on one MI355X.
+
+One step = one fldce_fwd_bwd call over the whole batch: logits GEMM with the
+softmax-partials epilogue, per-row combine and loss, dlogits, dH = g W,
+dW = g^T h and the loss reduction (every stage of the path), with inputs,
+outputs and workspace resident in HBM before the timed region starts.
+
+Default workload: the headline masked-diffusion LM head, B=8 x L=1024
+(N=8192 tokens), H=2560, V=151936, bf16, label_smoothing 0.1, logit_scale
+0.5, per-sequence masking probability, mean over N ("sum/N").  Synthetic,
+seeded inputs (lm_head_linear_bf16_amd.synth).
+
+Prints ONE JSON line: tokens/s (value), TFLOP/s at 6*N*H*V, the fraction of
+the bf16 MFMA peak, the roofline entry of the dominant kernel (timed live with
+HIP events recorded on the library's stream inside the timed steps), and the
+float64 CPU oracle timed on a bounded row sample on this host.
+
+    python bench.py [--steps K] [--warmup W] [--workload headline] [--chunk-rows C]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 vector, published
+STAGE_FLOP_KERNELS = ("logits_gemm", "dH_gemm", "dW_gemm")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def src_hash() -> str:
+    d = hashlib.sha256()
+    cdir = os.path.join(ROOT, "lm_head_linear_bf16_amd", "csrc")
+    for name in sorted(os.listdir(cdir)):
+        with open(os.path.join(cdir, name), "rb") as f:
+            d.update(name.encode())
+            d.update(f.read())
+    return d.hexdigest()[:16]
+
+
+def traffic_entry(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    the kernels changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(kernel)
+    if not e or e.get("src_hash") != src_hash() or e.get("workload") != workload:
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(w, rows: int) -> dict:
+    """The float64 oracle on the first `rows` token rows of the same workload."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        threads = len(os.sched_getaffinity(0))
+    import oracle
+    from lm_head_linear_bf16_amd import synth
+    target, p_mask = synth.targets(w)
+    h = synth.hidden(w).values[:rows].astype(np.float64)
+    W = synth.weight(w).values.astype(np.float64)
+    t = target[:rows]
+    p = p_mask[:rows]
+    log(f"cpu baseline: oracle on {rows} rows, {threads} BLAS threads")
+    t0 = time.perf_counter()
+    oracle.forward_backward(h, W, t, p, label_smoothing=w.label_smoothing,
+                            logit_scale=w.logit_scale, reduction=w.reduction,
+                            total=w.total or None, row_block=1024)
+    dt = time.perf_counter() - t0
+    return {"value": rows / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {rows} of {w.N} token rows of the same workload (full vocabulary, "
+                      f"loss + dH + dW rows' contributions), float64 NumPy, {dt:.2f} s",
+            "seconds": dt}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="headline")
+    ap.add_argument("--chunk-rows", type=int, default=0)
+    ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", default="", help="comma-separated chunk sizes to time as well")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(vocabulary and sequence sharding are described, not built).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    from lm_head_linear_bf16_amd import fldce, synth
+
+    w = synth.WORKLOADS[args.workload]
+    N, H, V = w.N, w.H, w.V
+    dev = torch.device("cuda:0")
+    log(f"workload {w.name}: N={N} H={H} V={V} {w.dtype}; generating inputs")
+    target, p_mask = synth.targets(w)
+    hT, WT = synth.hidden(w), synth.weight(w)
+
+    def dev_t(t):
+        if t.bits is not None:
+            return torch.from_numpy(t.bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(t.values).to(dev)
+
+    h, W = dev_t(hT), dev_t(WT)
+    del hT, WT
+    tgt = torch.from_numpy(target).to(dev)
+    pm = torch.from_numpy(p_mask).to(dev)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def run_config(chunk_rows: int, steps: int, warmup: int):
+        out = dict(loss=torch.empty(1, dtype=torch.float32, device=dev),
+                   dH=torch.empty_like(h), dW=torch.empty_like(W))
+        nbytes = fldce.fldce_workspace_size(N, H, V, dt, chunk_rows)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        kw = dict(label_smoothing=w.label_smoothing, logit_scale=w.logit_scale,
+                  reduction=w.reduction, total=w.total, chunk_rows=chunk_rows,
+                  workspace=ws, out=out)
+        for _ in range(warmup):
+            fldce.fldce_fwd_bwd(h, W, tgt, pm, **kw)
+        torch.cuda.synchronize()
+        fldce.fldce_profile_begin()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fldce.fldce_fwd_bwd(h, W, tgt, pm, **kw)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        fldce.fldce_profile_end()
+        stages = {}
+        for s in range(fldce.fldce_profile_num_stages()):
+            ms, n = fldce.fldce_profile_read(s)
+            if n:
+                stages[fldce.fldce_profile_stage_name(s)] = dict(total_ms=ms, launches=n)
+        loss = float(out["loss"].item())
+        del ws
+        return (t1 - t0) * 1e3 / steps, stages, loss
+
+    C = args.chunk_rows or fldce.fldce_default_chunk_rows(N, H, V)
+    log(f"timing {args.steps} steps after {args.warmup} warmup (chunk_rows={C})")
+    ms, stages, loss = run_config(args.chunk_rows, args.steps, args.warmup)
+    flops = 6.0 * N * H * V
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    # dominant kernel: the GEMM stage with the largest time; each launch does
+    # 2 * C * H * V flops (C rows of the chunk), i.e. 2 N H V per step
+    dom = max((k for k in stages if k in STAGE_FLOP_KERNELS), key=lambda k: stages[k]["total_ms"])
+    d = stages[dom]
+    per_launch_flops = 2.0 * N * H * V * args.steps / d["launches"]
+    avg_ms = d["total_ms"] / d["launches"]
+    achieved = per_launch_flops / (avg_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": traffic_entry(dom, w.name), "avg_launch_ms": round(avg_ms, 4),
+                "flops_per_launch": per_launch_flops}
+    stage_ms = {k: round(v["total_ms"] / args.steps, 4) for k, v in stages.items()}
+    result = {
+        "metric": "fused LM-head CE fwd+bwd tokens/s and TFLOP/s (% bf16 MFMA peak), 1 GPU",
+        "value": round(N / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": (f"{w.name}: B={w.B} L={w.L} (N={N}) H={H} V={V} "
+                                f"eps={w.label_smoothing} s={w.logit_scale} reduction="
+                                + ("sum/N" if w.total_is_N else "mean over non-ignored")),
+                   "global_batch": w.B, "seq_len": w.L, "parallelism": "none (1 GPU)",
+                   "chunk_rows": int(C)},
+        "tflops": round(tflops, 2),
+        "pct_peak": round(100.0 * tflops / peak, 2),
+        "loss": loss,
+        "stage_ms_per_step": stage_ms,
+        "roofline": roofline,
+    }
+    if args.sweep:
+        sw = {}
+        for c in [int(x) for x in args.sweep.split(",") if x]:
+            log(f"sweep chunk_rows={c}")
+            m, _, _ = run_config(c, max(3, args.steps // 4), 1)
+            sw[str(c)] = {"ms_per_step": round(m, 3), "tflops": round(flops / (m * 1e-3) / 1e12, 1)}
+        result["chunk_sweep"] = sw
+    if not args.no_cpu_baseline:
+        del h, W
+        torch.cuda.empty_cache()
+        result["cpu_baseline"] = cpu_baseline(w, min(args.cpu_rows, N))
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -39,7 +39,9 @@
  * are not ignored (p_mask of ignored rows is never read as a divisor).
  *
  * Error behaviour: every entry point returns FLDCE_OK (0) or a negative
- * status; on error nothing has been enqueued and no output is touched.
+ * status.  Argument errors are found before anything is enqueued (no output
+ * is touched); FLDCE_ERR_HIP reports a failed launch, after which outputs
+ * may be partly written.
  * fldce_status_string() gives a static description.  No exception crosses the
  * ABI.  Results are deterministic: no floating-point atomics are used, every
  * reduction has a fixed order.
@@ -184,6 +186,29 @@ int fldce_shard_bwd(const void* h, const void* W_local, const int64_t* target,
                     int64_t total, float* dH_partial, void* dW_local,
                     int64_t chunk_rows, void* workspace,
                     size_t workspace_bytes, void* stream);
+
+/*
+ * Stage profiling (diagnostics).  While enabled, every call above records a
+ * pair of HIP events on its own stream around each stage, so stage times are
+ * those of the launches on the caller's stream.  fldce_profile_begin()
+ * enables recording and clears the totals; fldce_profile_end() disables it.
+ * fldce_profile_read() sums the elapsed times of the stage's launches since
+ * begin; call it after the stream has been synchronised.  Creating the event
+ * pool is the only resource the library ever creates itself, and only while
+ * profiling.  Not thread-safe: profile one thread at a time.
+ *
+ * Stages: 0 prep (divisor, W^T, column sums, target/row-sum dots),
+ * 1 h^T, 2 logits GEMM (+ softmax partials), 3 row combine, 4 dlogits,
+ * 5 dH GEMM, 6 dH split-K reduction, 7 dW GEMM, 8 loss reduction.
+ */
+int fldce_profile_num_stages(void);
+const char* fldce_profile_stage_name(int stage);
+int fldce_profile_begin(void);
+int fldce_profile_end(void);
+/* total_ms: summed duration; launches: number of timed launches (either may
+ * be NULL).  Returns FLDCE_OK, FLDCE_ERR_BAD_ARGUMENT for a bad stage, or
+ * FLDCE_ERR_HIP if an event query fails (stream not synchronised). */
+int fldce_profile_read(int stage, double* total_ms, int64_t* launches);
 
 #ifdef __cplusplus
 }

@@ -17,6 +17,7 @@
 #include <algorithm>
 #include <cmath>
 #include <mutex>
+#include <vector>
 
 #include "../../include/fldce.h"
 #include "fldce_common.h"
@@ -138,6 +139,49 @@ void set_gemm_attributes() {
   });
 }
 
+// ---------------------------------------------------------------------------
+// Stage profiling: event pairs recorded on the call's stream.
+// ---------------------------------------------------------------------------
+enum Stage { kPrep = 0, kHT, kLogits, kCombine, kDlogits, kDHGemm, kDHReduce, kDWGemm, kLoss, kNumStages };
+const char* const kStageNames[kNumStages] = {"prep", "h_transpose", "logits_gemm", "row_combine",
+                                             "dlogits", "dH_gemm", "dH_reduce", "dW_gemm", "loss"};
+
+struct Profiler {
+  bool on = false;
+  std::vector<hipEvent_t> ev[kNumStages];  // start/end pairs
+  size_t used[kNumStages] = {};
+  hipEvent_t get(int stage) {
+    auto& v = ev[stage];
+    if (used[stage] == v.size()) {
+      hipEvent_t e = nullptr;
+      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      v.push_back(e);
+    }
+    return v[used[stage]++];
+  }
+};
+Profiler g_prof;
+
+// Records a start event on construction and an end event on destruction.
+struct StageTimer {
+  int stage;
+  hipStream_t st;
+  bool active;
+  StageTimer(int s, hipStream_t stream) : stage(s), st(stream), active(g_prof.on) {
+    if (active) {
+      hipEvent_t e = g_prof.get(stage);
+      if (e) (void)hipEventRecord(e, st);
+      else active = false;
+    }
+  }
+  ~StageTimer() {
+    if (active) {
+      hipEvent_t e = g_prof.get(stage);
+      if (e) (void)hipEventRecord(e, st);
+    }
+  }
+};
+
 bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 int check_common(const void* h, const void* W, const int64_t* target, int64_t N, int64_t H,
@@ -207,15 +251,22 @@ int run_core(const Core& c, const Plan& p, char* ws, hipStream_t st) {
   const T* W = static_cast<const T*>(c.W);
   const int64_t H = c.H, V = c.V, Vp = p.Vp;
 
-  launch_transpose<T>(W, V, H, H, WT, Vp, Vp, st);
+  {
+    StageTimer tm(kPrep, st);
+    launch_transpose<T>(W, V, H, H, WT, Vp, Vp, st);
+  }
   for (int64_t ic = 0; ic < p.nchunks; ++ic) {
     const int64_t c0 = ic * p.C;
     const int64_t Cc = std::min(p.C, c.N - c0);
     const int64_t Cpc = round_up(Cc, 64);
     const T* hc = h + c0 * H;
-    launch_transpose<T>(hc, Cc, H, H, hT, p.Cp, Cpc, st);
+    {
+      StageTimer tm(kHT, st);
+      launch_transpose<T>(hc, Cc, H, H, hT, p.Cp, Cpc, st);
+    }
     // 1. logits
     if (bf) {
+      StageTimer tm(kLogits, st);
       const int blocks = (int)(cdiv(V, kBM) * cdiv(Cc, kBN));
       if (c.lse_in == nullptr)
         k_logits_bf16<true, true><<<blocks, kGemmThreads, kGemmLds, st>>>(
@@ -226,6 +277,7 @@ int run_core(const Core& c, const Plan& p, char* ws, hipStream_t st) {
             (const bf16*)W, (const bf16*)hc, (int)V, (int)Cc, (int)H, c.s, part, p.C, (bf16*)zb, Vp,
             kGroupM);
     } else {
+      StageTimer tm(kLogits, st);
       dim3 g((unsigned)cdiv(V, 64), (unsigned)cdiv(Cc, 64));
       k_gemm_f32_nt<<<g, 256, 0, st>>>((const float*)hc, H, Cc, (const float*)W, H, V, H, c.s,
                                        (float*)zb, Vp, 0);
@@ -237,18 +289,21 @@ int run_core(const Core& c, const Plan& p, char* ws, hipStream_t st) {
     // 2. per-row combine (or coefficients only, when lse is given)
     const float* lse_c;
     if (c.lse_in == nullptr) {
+      StageTimer tm(kCombine, st);
       k_combine_rows<<<grid1(Cc, 32), 256, 0, st>>>(
           part, p.C, p.nT, Cc, 0, c.target + c0, c.p_mask ? c.p_mask + c0 : nullptr, c.ignore,
           c.zt + c0, c.R ? c.R + c0 : nullptr, c.eps, (float)c.Vg, c.s, c.D, c.lse_out + c0,
           c.rloss_out + c0, coef, nullptr, nullptr);
       lse_c = c.lse_out + c0;
     } else {
+      StageTimer tm(kCombine, st);
       k_coef_rows<<<grid1(Cc, 256), 256, 0, st>>>(c.target + c0, c.p_mask ? c.p_mask + c0 : nullptr,
                                                    c.ignore, Cc, c.s, c.D, coef);
       lse_c = c.lse_in + c0;
     }
     // 3. dlogits, in place, plus g^T
     {
+      StageTimer tm(kDlogits, st);
       dim3 g((unsigned)(Vp / 64), (unsigned)(Cpc / 64));
       k_gpass<T><<<g, 256, 0, st>>>(zb, Vp, Cc, V, lse_c, coef, c.target + c0, c.v0, c.eps,
                                     (float)c.Vg, gT, p.Cp);
@@ -257,9 +312,13 @@ int run_core(const Core& c, const Plan& p, char* ws, hipStream_t st) {
     if (bf) {
       const int S = p.splits;
       const int blocks = (int)(cdiv(Cc, kBM) * cdiv(H, kBN) * S);
-      k_gemm_splitk_bf16<<<blocks, kGemmThreads, kGemmLds, st>>>(
-          (const bf16*)zb, Vp, (int)Cc, (const bf16*)WT, Vp, (int)H, (int)(Vp / kBK), S, dHpart,
-          kGroupM);
+      {
+        StageTimer tm(kDHGemm, st);
+        k_gemm_splitk_bf16<<<blocks, kGemmThreads, kGemmLds, st>>>(
+            (const bf16*)zb, Vp, (int)Cc, (const bf16*)WT, Vp, (int)H, (int)(Vp / kBK), S, dHpart,
+            kGroupM);
+      }
+      StageTimer tm(kDHReduce, st);
       if (c.dH_f32)
         k_splitk_reduce<float><<<grid1(Cc * H, 1024), 256, 0, st>>>(dHpart, S, Cc * H,
                                                                     (float*)c.dH + c0 * H);
@@ -267,12 +326,14 @@ int run_core(const Core& c, const Plan& p, char* ws, hipStream_t st) {
         k_splitk_reduce<bf16><<<grid1(Cc * H, 1024), 256, 0, st>>>(dHpart, S, Cc * H,
                                                                    (bf16*)c.dH + c0 * H);
     } else {
+      StageTimer tm(kDHGemm, st);
       dim3 g((unsigned)cdiv(H, 64), (unsigned)cdiv(Cc, 64));
       k_gemm_f32_nt<<<g, 256, 0, st>>>((const float*)zb, Vp, Cc, (const float*)WT, Vp, H, V, 1.f,
                                        (float*)c.dH + c0 * H, H, 0);
     }
     // 5. dW += g^T h
     if (bf) {
+      StageTimer tm(kDWGemm, st);
       int mode = 0;
       if (p.nchunks > 1) mode = ic == 0 ? 1 : (ic + 1 == p.nchunks ? 3 : 2);
       const int blocks = (int)(cdiv(V, kBM) * cdiv(H, kBN));
@@ -282,6 +343,7 @@ int run_core(const Core& c, const Plan& p, char* ws, hipStream_t st) {
                                                    p.Cp, (int)H, (int)(Cpc / kBK), (bf16*)c.dW,
                                                    dW32, kGroupM);
     } else {
+      StageTimer tm(kDWGemm, st);
       dim3 g((unsigned)cdiv(H, 64), (unsigned)cdiv(V, 64));
       k_gemm_f32_nt<<<g, 256, 0, st>>>((const float*)gT, p.Cp, V, (const float*)hT, p.Cp, H, Cpc,
                                        1.f, (float*)c.dW, H, ic == 0 ? 0 : 1);
@@ -369,7 +431,6 @@ int fldce_fwd_bwd(const void* h, const void* W, const int64_t* target, const flo
     zero_fill(dW, V * H, esz, st);
     return launch_status();
   }
-  k_divisor<<<1, 1024, 0, st>>>(target, N, ignore_index, reduction, total, D);
   const bool smooth = label_smoothing > 0.f;
   float* colpart = reinterpret_cast<float*>(ws + p.oColpart);
   float* wsum = reinterpret_cast<float*>(ws + p.oWsum);
@@ -379,22 +440,29 @@ int fldce_fwd_bwd(const void* h, const void* W, const int64_t* target, const flo
   float* rl = row_loss ? row_loss : reinterpret_cast<float*>(ws + p.oRloss);
   Core c{h, W, target, p_mask, N, H, V, 0, V, dtype, ignore_index, label_smoothing, logit_scale,
          nullptr, lse, rl, zt, smooth ? R : nullptr, D, dH, false, dW};
-  if (dtype == FLDCE_DTYPE_BF16) {
-    if (smooth) launch_colsum<bf16>((const bf16*)W, V, H, colpart, wsum, st);
-    k_rowdot<bf16><<<grid1(N, 4), 256, 0, st>>>((const bf16*)h, (const bf16*)W, H, target, 0, V,
-                                                 ignore_index, logit_scale, smooth ? wsum : nullptr,
-                                                 N, zt, smooth ? R : nullptr);
-    rc = run_core<bf16>(c, p, ws, st);
-  } else {
-    if (smooth) launch_colsum<float>((const float*)W, V, H, colpart, wsum, st);
-    k_rowdot<float><<<grid1(N, 4), 256, 0, st>>>((const float*)h, (const float*)W, H, target, 0, V,
-                                                  ignore_index, logit_scale,
-                                                  smooth ? wsum : nullptr, N, zt,
-                                                  smooth ? R : nullptr);
-    rc = run_core<float>(c, p, ws, st);
+  {
+    StageTimer tm(kPrep, st);
+    k_divisor<<<1, 1024, 0, st>>>(target, N, ignore_index, reduction, total, D);
+    if (dtype == FLDCE_DTYPE_BF16) {
+      if (smooth) launch_colsum<bf16>((const bf16*)W, V, H, colpart, wsum, st);
+      k_rowdot<bf16><<<grid1(N, 4), 256, 0, st>>>((const bf16*)h, (const bf16*)W, H, target, 0,
+                                                   V, ignore_index, logit_scale,
+                                                   smooth ? wsum : nullptr, N, zt,
+                                                   smooth ? R : nullptr);
+    } else {
+      if (smooth) launch_colsum<float>((const float*)W, V, H, colpart, wsum, st);
+      k_rowdot<float><<<grid1(N, 4), 256, 0, st>>>((const float*)h, (const float*)W, H, target,
+                                                    0, V, ignore_index, logit_scale,
+                                                    smooth ? wsum : nullptr, N, zt,
+                                                    smooth ? R : nullptr);
+    }
   }
+  rc = dtype == FLDCE_DTYPE_BF16 ? run_core<bf16>(c, p, ws, st) : run_core<float>(c, p, ws, st);
   if (rc != FLDCE_OK) return rc;
-  k_loss_reduce<<<1, 1024, 0, st>>>(rl, N, D, loss);
+  {
+    StageTimer tm(kLoss, st);
+    k_loss_reduce<<<1, 1024, 0, st>>>(rl, N, D, loss);
+  }
   return launch_status();
 }
 
@@ -421,12 +489,19 @@ int fldce_shard_partials(const void* h, const void* W_local, const int64_t* targ
   const int64_t V = V_local;
   if (dtype == FLDCE_DTYPE_BF16) {
     const int blocks = (int)(cdiv(V, kBM) * cdiv(N, kBN));
-    k_logits_bf16<false, true><<<blocks, kGemmThreads, kGemmLds, st>>>(
-        (const bf16*)W_local, (const bf16*)h, (int)V, (int)N, (int)H, logit_scale, part, p.C,
-        nullptr, 0, kGroupM);
-    k_combine_rows<<<grid1(N, 32), 256, 0, st>>>(part, p.C, p.nT, N, 1, nullptr, nullptr, 0, nullptr,
-                                                 nullptr, 0.f, 1.f, 1.f, nullptr, nullptr, nullptr,
-                                                 nullptr, row_max, row_sumexp);
+    {
+      StageTimer tm(kLogits, st);
+      k_logits_bf16<false, true><<<blocks, kGemmThreads, kGemmLds, st>>>(
+          (const bf16*)W_local, (const bf16*)h, (int)V, (int)N, (int)H, logit_scale, part, p.C,
+          nullptr, 0, kGroupM);
+    }
+    {
+      StageTimer tm(kCombine, st);
+      k_combine_rows<<<grid1(N, 32), 256, 0, st>>>(part, p.C, p.nT, N, 1, nullptr, nullptr, 0,
+                                                   nullptr, nullptr, 0.f, 1.f, 1.f, nullptr,
+                                                   nullptr, nullptr, nullptr, row_max, row_sumexp);
+    }
+    StageTimer tm(kPrep, st);
     if (row_sumlogit) launch_colsum<bf16>((const bf16*)W_local, V, H, colpart, wsum, st);
     k_rowdot<bf16><<<grid1(N, 4), 256, 0, st>>>((const bf16*)h, (const bf16*)W_local, H, target,
                                                  vocab_start, V, ignore_index, logit_scale,
@@ -483,11 +558,46 @@ int fldce_shard_bwd(const void* h, const void* W_local, const int64_t* target, c
   }
   char* ws = static_cast<char*>(workspace);
   float* D = reinterpret_cast<float*>(ws + p.oD);
-  k_divisor<<<1, 1024, 0, st>>>(target, N, ignore_index, reduction, total, D);
+  {
+    StageTimer tm(kPrep, st);
+    k_divisor<<<1, 1024, 0, st>>>(target, N, ignore_index, reduction, total, D);
+  }
   Core c{h, W_local, target, p_mask, N, H, V_local, vocab_start, V_global, dtype, ignore_index,
          label_smoothing, logit_scale, lse, nullptr, nullptr, nullptr, nullptr, D, dH_partial,
          true, dW_local};
   return dtype == FLDCE_DTYPE_BF16 ? run_core<bf16>(c, p, ws, st) : run_core<float>(c, p, ws, st);
+}
+
+int fldce_profile_num_stages(void) { return kNumStages; }
+
+const char* fldce_profile_stage_name(int stage) {
+  return (stage >= 0 && stage < kNumStages) ? kStageNames[stage] : nullptr;
+}
+
+int fldce_profile_begin(void) {
+  for (int s = 0; s < kNumStages; ++s) g_prof.used[s] = 0;
+  g_prof.on = true;
+  return FLDCE_OK;
+}
+
+int fldce_profile_end(void) {
+  g_prof.on = false;
+  return FLDCE_OK;
+}
+
+int fldce_profile_read(int stage, double* total_ms, int64_t* launches) {
+  if (stage < 0 || stage >= kNumStages) return FLDCE_ERR_BAD_ARGUMENT;
+  double sum = 0.0;
+  const size_t n = g_prof.used[stage] / 2;
+  for (size_t i = 0; i < n; ++i) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, g_prof.ev[stage][2 * i], g_prof.ev[stage][2 * i + 1]) != hipSuccess)
+      return FLDCE_ERR_HIP;
+    sum += ms;
+  }
+  if (total_ms) *total_ms = sum;
+  if (launches) *launches = (int64_t)n;
+  return FLDCE_OK;
 }
 
 }  // extern "C"

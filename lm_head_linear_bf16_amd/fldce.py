@@ -38,6 +38,12 @@ _SIGNATURES = {
     "fldce_shard_bwd": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64,
                                  _c_i64, _c_int, _c_i64, _c_f, _c_f, _c_int, _c_i64, _c_p, _c_p,
                                  _c_i64, _c_p, _c_sz, _c_p]),
+    "fldce_profile_num_stages": (_c_int, []),
+    "fldce_profile_stage_name": (ctypes.c_char_p, [_c_int]),
+    "fldce_profile_begin": (_c_int, []),
+    "fldce_profile_end": (_c_int, []),
+    "fldce_profile_read": (_c_int, [_c_int, ctypes.POINTER(ctypes.c_double),
+                                    ctypes.POINTER(ctypes.c_int64)]),
 }
 
 _lib = None
@@ -111,6 +117,31 @@ def _workspace(nbytes: int, dev, ws: Optional[torch.Tensor]) -> torch.Tensor:
             raise ValueError(f"workspace too small: need {nbytes} bytes")
         return ws
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+
+
+def fldce_profile_begin() -> None:
+    lib().fldce_profile_begin()
+
+
+def fldce_profile_end() -> None:
+    lib().fldce_profile_end()
+
+
+def fldce_profile_num_stages() -> int:
+    return lib().fldce_profile_num_stages()
+
+
+def fldce_profile_stage_name(stage: int) -> str:
+    return lib().fldce_profile_stage_name(stage).decode()
+
+
+def fldce_profile_read(stage: int):
+    """(total_ms, launches) of a stage since fldce_profile_begin (after a sync)."""
+    ms, n = ctypes.c_double(0.0), ctypes.c_int64(0)
+    rc = lib().fldce_profile_read(stage, ctypes.byref(ms), ctypes.byref(n))
+    if rc != 0:
+        raise FldceError(rc, "fldce_profile_read")
+    return ms.value, n.value
 
 
 def fldce_default_chunk_rows(N: int, H: int, V: int) -> int:

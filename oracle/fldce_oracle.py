@@ -225,15 +225,19 @@ def row_stats(h, W, target, rows: Sequence[int], logit_scale: float,
 
 
 def dH_rows(h, W, target, p_mask, lse_rows, rows, D, label_smoothing,
-            logit_scale, ignore_index=-100):
-    """dH for the given rows: g_rows W (needs only those rows' lse)."""
+            logit_scale, ignore_index=-100, V_global=None, vocab_start=0):
+    """dH for the given rows: g_rows W (needs only those rows' lse).  ``W`` may
+    be a vocabulary shard starting at ``vocab_start`` of a ``V_global`` vocab
+    (then this is the shard's dH_partial)."""
     h, W = _f64(h), _f64(W)
     rows = np.asarray(rows, dtype=np.int64)
     t = np.asarray(target, dtype=np.int64)[rows]
+    V_global = W.shape[0] if V_global is None else V_global
     valid = t != ignore_index
+    ins = valid & (t >= vocab_start) & (t < vocab_start + W.shape[0])
     z = scaled_logits(h[rows], W, logit_scale)
-    g = dlogits(z, lse_rows, np.where(valid, t, -1), np.asarray(p_mask)[rows], valid,
-                D, label_smoothing, logit_scale, W.shape[0])
+    g = dlogits(z, lse_rows, np.where(ins, t - vocab_start, -1), np.asarray(p_mask)[rows],
+                valid, D, label_smoothing, logit_scale, V_global)
     return g @ W
 
 

@@ -286,8 +286,11 @@ def test_sampled_helpers_match_full():
     vr = [0, 7, 49] + [int(v) for v in y[y >= 0][:2]]
     np.testing.assert_allclose(O.dW_rows(h, W, y, p, full["lse"], vr, N, 0.1, 0.5),
                                full["dW"][vr], rtol=1e-12, atol=1e-15)
-    # shard variant of dW_rows
+    # shard variants of dH_rows and dW_rows
     dh, dw = O.shard_backward(h, W[20:40], y, p, full["lse"], 20, V, N, 0.1, 0.5)
+    np.testing.assert_allclose(
+        O.dH_rows(h, W[20:40], y, p, full["lse"][rows], rows, N, 0.1, 0.5, V_global=V,
+                  vocab_start=20), dh[rows], rtol=1e-12, atol=1e-15)
     np.testing.assert_allclose(
         O.dW_rows(h, W[20:40], y, p, full["lse"], [0, 5, 19], N, 0.1, 0.5,
                   V_global=V, vocab_start=20),
