@@ -90,7 +90,7 @@ Plan make_plan(int mode, int64_t N, int64_t H, int64_t V, int dtype, int64_t chu
   p.nchunks = N > 0 ? cdiv(N, p.C) : 0;
   size_t cur = 0;
   p.oD = take(cur, 256);
-  p.oColpart = take(cur, (size_t)cdiv(V, 64) * H * 4);
+  p.oColpart = take(cur, (size_t)cdiv(V, kColSlab) * H * 4);
   p.oWsum = take(cur, (size_t)H * 4);
   p.oPart = take(cur, (size_t)p.nT * p.C * 8);
   if (mode == kShardPartials) {
@@ -204,15 +204,18 @@ template <typename T>
 void launch_transpose(const T* src, int64_t R, int64_t Cn, int64_t lds, T* dst, int64_t ldd,
                       int64_t Rp, hipStream_t st) {
   dim3 g((unsigned)cdiv(Rp, 64), (unsigned)cdiv(Cn, 64));
-  k_transpose<T><<<g, 256, 0, st>>>(src, R, Cn, lds, dst, ldd, Rp);
+  if constexpr (sizeof(T) == 2)
+    k_transpose_bf16<<<g, 256, 0, st>>>(src, R, Cn, lds, dst, ldd, Rp);
+  else
+    k_transpose<T><<<g, 256, 0, st>>>(src, R, Cn, lds, dst, ldd, Rp);
 }
 
 // wsum[c] = sum_j W[j, c] (two ordered passes).
 template <typename T>
 void launch_colsum(const T* W, int64_t V, int64_t H, float* colpart, float* wsum, hipStream_t st) {
-  dim3 g((unsigned)cdiv(V, 64), (unsigned)cdiv(H, 256));
+  dim3 g((unsigned)cdiv(V, kColSlab), (unsigned)cdiv(H, 256));
   k_colsum_slabs<T><<<g, 256, 0, st>>>(W, V, H, colpart);
-  k_colsum_finish<<<grid1(H, 256), 256, 0, st>>>(colpart, cdiv(V, 64), H, wsum);
+  k_colsum_finish<<<grid1(H, 256), 256, 0, st>>>(colpart, cdiv(V, kColSlab), H, wsum);
 }
 
 // Everything of the gradient path that fwd_bwd and shard_bwd share.

@@ -6,17 +6,22 @@
 // is not contiguous in the caller's layout are transposed once into the
 // workspace beforehand (W^T, h^T, g^T), so one main loop serves all three.
 //
-// Tiling (CDNA4: 64-wide waves, 160 KB LDS, v_mfma_f32_32x32x16_bf16):
-//   * block tile 256 x 256, K step 64, 256 threads = 4 waves in a 2 x 2 grid,
-//     each wave owns a 128 x 128 accumulator (16 MFMA tiles of 32 x 32 =
-//     256 fp32 per lane, held in AGPRs);
+// Tiling (CDNA4: 64-wide waves, 160 KB LDS, v_mfma_f32_16x16x32_bf16):
+//   * block tile 256 x 256, K step 64, 512 threads = 8 waves in a 2 (M) x 4
+//     (N) grid, each wave owning a 128 x 64 accumulator (8 x 4 MFMA tiles of
+//     16 x 16, 128 fp32 per lane), two waves per SIMD so one wave's waits are
+//     covered by the other's MFMAs;
 //   * two LDS stages of (256 + 256) x 64 bf16 = 64 KB each, filled with
-//     direct global->LDS 16-byte loads (no VGPR staging); the 16-byte chunk
-//     at column c of row r is stored at chunk position c ^ (r & 7) so the
-//     MFMA fragment reads (8 rows x 16 B per 8 lanes) are bank-conflict free;
-//   * fragments are double-buffered in registers across the four 16-wide K
-//     sub-steps; the barrier for the next stage sits before the last
-//     sub-step's MFMAs so the next tile's first fragment reads overlap them;
+//     direct global->LDS 16-byte loads (no VGPR staging).  The 16-byte chunk
+//     c of row r sits at chunk position c ^ ((r >> 1) & 7): the LDS serves a
+//     16-byte read to 16 lanes per cycle, and the 16 rows those lanes read
+//     then fall on 16 distinct bank groups (measured: no bank-conflict
+//     cycles);
+//   * each 32-wide K step reads the next step's fragments while it issues
+//     its MFMAs, one LDS read between two MFMAs (explicit scheduling groups);
+//     the stage barrier sits in the middle of the last step's MFMAs and the
+//     loop body has no branch, so the next tile's first reads and the global
+//     loads of the tile after overlap MFMA work;
 //   * blocks are renumbered so that consecutive logical tiles run on one XCD
 //     (the dispatcher deals block ids round-robin over the 8 XCDs) and tiles
 //     are walked in groups of `group_m` rows of tiles, so operand slabs are
@@ -31,17 +36,21 @@
 namespace fldce {
 
 constexpr int kBM = 256, kBN = 256, kBK = 64;
-constexpr int kGemmThreads = 256;
+constexpr int kWavesM = 2, kWavesN = 4, kWaves = kWavesM * kWavesN;
+constexpr int kGemmThreads = kWaves * 64;
+constexpr int kTM = kBM / kWavesM / 16, kTN = kBN / kWavesN / 16;  // 16x16 tiles per wave: 8 x 4
 constexpr int kABytes = kBM * kBK * 2;
 constexpr int kStageBytes = (kBM + kBN) * kBK * 2;
 constexpr int kGemmLds = 2 * kStageBytes;  // 128 KB
+constexpr int kRoundsA = kBM / (kWaves * 8), kRoundsB = kBN / (kWaves * 8);
 
 struct TileCoord {
   int tm, tn, split;
 };
 
-// Block id -> (tile row, tile column, split), XCD-aware and grouped.
-__device__ __forceinline__ TileCoord tile_coord(int tiles_m, int tiles_n, int splits, int group_m) {
+// Block id -> (tile row, tile column, split), XCD-aware and grouped.  The
+// grid must be exactly tiles_m * tiles_n * splits blocks.
+__device__ __forceinline__ TileCoord tile_coord(int tiles_m, int tiles_n, int group_m) {
   const int nblk = gridDim.x;
   const int bid = blockIdx.x;
   const int per = nblk / 8, rem = nblk % 8;
@@ -51,7 +60,6 @@ __device__ __forceinline__ TileCoord tile_coord(int tiles_m, int tiles_n, int sp
   TileCoord c;
   c.split = b / tiles;
   b -= c.split * tiles;
-  (void)splits;
   const int width = group_m * tiles_n;
   const int g = b / width;
   const int first_m = g * group_m;
@@ -62,93 +70,129 @@ __device__ __forceinline__ TileCoord tile_coord(int tiles_m, int tiles_n, int sp
   return c;
 }
 
+// 16-byte chunk position of logical chunk c (0..7) in LDS row r.
+__device__ __forceinline__ int lds_chunk(int c, int r) { return c ^ ((r >> 1) & 7); }
+
+// Scheduling groups: ND (MFMA, LDS read) pairs, then the remaining MFMAs.
+template <int I, int NM, int ND>
+__device__ __forceinline__ void interleave_groups() {
+  if constexpr (I < ND) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    interleave_groups<I + 1, NM, ND>();
+  } else if constexpr (NM > ND) {
+    __builtin_amdgcn_sched_group_barrier(0x008, NM - ND, 0);
+  }
+}
+
+typedef floatx4 Acc[kTM][kTN];
+
 // Main loop: acc[i][j] (wave sub-tile i along M, j along N) accumulates
 // A[m0 .. m0+255, k] * B[n0 .. n0+255, k] over K tiles [kt0, kt0 + nk).
 __device__ __forceinline__ void gemm_mainloop(const bf16* __restrict__ A, int64_t lda, int M, int m0,
                                               const bf16* __restrict__ B, int64_t ldb, int N, int n0,
-                                              int64_t kt0, int nk, char* smem, floatx16 (&acc)[4][4]) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-
+                                              int64_t kt0, int nk, char* smem, Acc& acc) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kTM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{};
+    for (int j = 0; j < kTN; ++j) acc[i][j] = floatx4{};
   if (nk <= 0) return;
 
-  // Per-thread source rows: wave w, round i fills LDS rows i*32 + w*8 .. +7,
-  // lane -> row (lane >> 3), chunk position (lane & 7) holding chunk c.
+  // Loads: wave w, round i fills LDS rows i*64 + w*8 .. +7; lane -> row
+  // (lane >> 3), chunk position (lane & 7), which holds the logical chunk
+  // lds_chunk(lane & 7, row) (the map is its own inverse).
   const int rr = lane >> 3;
-  const int c = (lane & 7) ^ rr;
-  const bf16* pA[8];
-  const bf16* pB[8];
+  const bf16* pA[kRoundsA];
+  const bf16* pB[kRoundsB];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = i * 32 + wave * 8 + rr;
-    pA[i] = A + (int64_t)min(m0 + r, M - 1) * lda + c * 8 + kt0 * kBK;
-    pB[i] = B + (int64_t)min(n0 + r, N - 1) * ldb + c * 8 + kt0 * kBK;
+  for (int i = 0; i < kRoundsA; ++i) {
+    const int r = i * kWaves * 8 + wave * 8 + rr;
+    pA[i] = A + (int64_t)min(m0 + r, M - 1) * lda + lds_chunk(lane & 7, r) * 8 + kt0 * kBK;
+  }
+#pragma unroll
+  for (int i = 0; i < kRoundsB; ++i) {
+    const int r = i * kWaves * 8 + wave * 8 + rr;
+    pB[i] = B + (int64_t)min(n0 + r, N - 1) * ldb + lds_chunk(lane & 7, r) * 8 + kt0 * kBK;
   }
   auto issue = [&](int stage, int t) {
     char* sA = smem + stage * kStageBytes + wave * 8 * 128;
     char* sB = sA + kABytes;
     const int64_t ko = (int64_t)t * kBK;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_global_load_lds(FLDCE_GPTR(pA[i] + ko), FLDCE_LPTR(sA + i * 32 * 128), 16, 0, 0);
+    for (int i = 0; i < kRoundsA; ++i)
+      __builtin_amdgcn_global_load_lds(FLDCE_GPTR(pA[i] + ko), FLDCE_LPTR(sA + i * kWaves * 8 * 128), 16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_global_load_lds(FLDCE_GPTR(pB[i] + ko), FLDCE_LPTR(sB + i * 32 * 128), 16, 0, 0);
+    for (int i = 0; i < kRoundsB; ++i)
+      __builtin_amdgcn_global_load_lds(FLDCE_GPTR(pB[i] + ko), FLDCE_LPTR(sB + i * kWaves * 8 * 128), 16, 0, 0);
   };
-  auto frags = [&](int stage, int ks, bf16x8(&a)[4], bf16x8(&b)[4]) {
-    const int pos = ((ks * 2 + (lane >> 5)) ^ (lane & 7)) << 4;
-    const char* sA = smem + stage * kStageBytes + (wm * 128 + (lane & 31)) * 128 + pos;
-    const char* sB = smem + stage * kStageBytes + kABytes + (wn * 128 + (lane & 31)) * 128 + pos;
+  // Fragments of v_mfma_f32_16x16x32_bf16: lane -> row (lane & 15), 8
+  // consecutive k at chunk (ks * 4 + (lane >> 4)) of the 64-wide tile.
+  const int offA = (wm * kTM * 16 + (lane & 15)) * 128;
+  const int offB = kABytes + (wn * kTN * 16 + (lane & 15)) * 128;
+  int posk[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8*)(sA + i * 32 * 128);
+  for (int ks = 0; ks < 2; ++ks) posk[ks] = lds_chunk(ks * 4 + (lane >> 4), lane & 15) << 4;
+  auto frags = [&](int stage, int ks, bf16x8(&a)[kTM], bf16x8(&b)[kTN]) {
+    const char* sA = smem + stage * kStageBytes + offA + posk[ks];
+    const char* sB = smem + stage * kStageBytes + offB + posk[ks];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = *(const bf16x8*)(sB + j * 32 * 128);
+    for (int i = 0; i < kTM; ++i) a[i] = *(const bf16x8*)(sA + i * 16 * 128);
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) b[j] = *(const bf16x8*)(sB + j * 16 * 128);
   };
-  auto mma = [&](const bf16x8(&a)[4], const bf16x8(&b)[4]) {
+  auto mma = [&](const bf16x8(&a)[kTM], const bf16x8(&b)[kTN], int i0, int i1) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kTM; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < kTN; ++j)
+        if (i * kTN + j >= i0 && i * kTN + j < i1)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
   };
-
-  bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
+  constexpr int NM = kTM * kTN, ND = kTM + kTN, NH = NM / 2;
+  bf16x8 fa0[kTM], fb0[kTN], fa1[kTM], fb1[kTN];
   issue(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();  // stage 0 landed in every wave
-  if (nk > 1) issue(1, 1);
+  issue(1, min(1, nk - 1));
   frags(0, 0, fa0, fb0);
   for (int t = 0; t < nk; ++t) {
     const int st = t & 1;
     frags(st, 1, fa1, fb1);
-    mma(fa0, fb0);
-    frags(st, 2, fa0, fb0);
-    mma(fa1, fb1);
-    frags(st, 3, fa1, fb1);
-    mma(fa0, fb0);
-    if (t + 1 < nk) {
-      __builtin_amdgcn_sched_barrier(0);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();  // stage st^1 landed in every wave; stage st fully read
-      __builtin_amdgcn_sched_barrier(0);
-      if (t + 2 < nk) issue(st, t + 2);
-      frags(st ^ 1, 0, fa0, fb0);
-    }
-    mma(fa1, fb1);
+    mma(fa0, fb0, 0, NM);
+    interleave_groups<0, NM, ND>();
+    __builtin_amdgcn_sched_barrier(0);
+    mma(fa1, fb1, 0, NH);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // tile t+1 landed in every wave; stage st fully read
+    __builtin_amdgcn_sched_barrier(0);
+    // After the last tile these re-load the last tile into the idle stage and
+    // read a landed stage; both results go unused (keeps the body branch-free).
+    issue(st, min(t + 2, nk - 1));
+    frags(st ^ 1, 0, fa0, fb0);
+    mma(fa1, fb1, NH, NM);
+    interleave_groups<0, NM - NH, ND>();
+    __builtin_amdgcn_sched_barrier(0);
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
+
+// Accumulator layout of v_mfma_f32_16x16x32_bf16: lane holds column
+// (lane & 15) and rows 4 * (lane >> 4) + r, r = 0..3, of each 16 x 16 tile.
+__device__ __forceinline__ int acc_row(int wm, int i, int lane, int r) {
+  return wm * kTM * 16 + i * 16 + (lane >> 4) * 4 + r;
+}
+__device__ __forceinline__ int acc_col(int wn, int j, int lane) { return wn * kTN * 16 + j * 16 + (lane & 15); }
 
 // ---------------------------------------------------------------------------
 // Logits GEMM with the softmax-partials epilogue, computed transposed:
 // A = W (rows = vocabulary, M = V), B = h chunk (rows = tokens, N = C), so
-// each lane holds 64 vocabulary values of 4 tokens and the per-token
-// reductions over the vocabulary are in-lane plus one exchange between the
-// two half-waves.
+// each lane holds 32 vocabulary values of each of its 4 tokens and the
+// per-token reductions over the vocabulary are in-lane plus two exchanges
+// among the 4 lanes that share a token.
 //
 // For each token and each 128-wide vocabulary slab (one wave's M range) it
 // writes part[slab * ldp + token] = (max_j z, sum_j exp(z - max)) with
@@ -160,64 +204,57 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_logits_bf16(
     floatx2* __restrict__ part, int64_t ldp, bf16* __restrict__ zbuf, int64_t ldz, int group_m) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int tiles_m = (int)cdiv(V, kBM), tiles_n = (int)cdiv(C, kBN);
-  const TileCoord tc = tile_coord(tiles_m, tiles_n, 1, group_m);
+  const TileCoord tc = tile_coord(tiles_m, tiles_n, group_m);
   const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
-  floatx16 acc[4][4];
+  Acc acc;
   gemm_mainloop(W, H, V, m0, h, H, C, n0, 0, H / kBK, smem, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int vbase = m0 + wm * 128;
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
+  const int vbase = m0 + wm * kTM * 16;
   if (vbase >= V) return;
-  const int tbase = n0 + wn * 128;
-  const bool full = vbase + 128 <= V;
+  const bool full = vbase + kTM * 16 <= V;
   const float sl = s * kLog2e;
-  const int half = (lane >> 5) * 4;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int tok = tbase + j * 32 + (lane & 31);
+  for (int j = 0; j < kTN; ++j) {
+    const int tok = n0 + acc_col(wn, j, lane);
     if (kPart) {
-    float mx = -INFINITY;
+      float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kTM; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = vbase + i * 32 + (r >> 2) * 8 + half + (r & 3);
-        if (full || row < V) mx = fmaxf(mx, acc[i][j][r]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float off = mx * sl;
-    float sum = 0.f;
+        for (int r = 0; r < 4; ++r)
+          if (full || m0 + acc_row(wm, i, lane, r) < V) mx = fmaxf(mx, acc[i][j][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float off = mx * sl;
+      float sum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kTM; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = vbase + i * 32 + (r >> 2) * 8 + half + (r & 3);
-        if (full || row < V) sum += fast_exp2(__builtin_fmaf(acc[i][j][r], sl, -off));
-      }
-    sum += __shfl_xor(sum, 32, 64);
-    if (lane < 32 && tok < C) part[(int64_t)(vbase / 128) * ldp + tok] = floatx2{mx * s, sum};
+        for (int r = 0; r < 4; ++r)
+          if (full || m0 + acc_row(wm, i, lane, r) < V)
+            sum += fast_exp2(__builtin_fmaf(acc[i][j][r], sl, -off));
+      sum += __shfl_xor(sum, 16, 64);
+      sum += __shfl_xor(sum, 32, 64);
+      if (lane < 16 && tok < C) part[(int64_t)(vbase / 128) * ldp + tok] = floatx2{mx * s, sum};
     }
     if (kStoreZ && tok < C) {
       bf16* zrow = zbuf + (int64_t)tok * ldz;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kTM; ++i) {
+        const int row0 = m0 + acc_row(wm, i, lane, 0);
+        bf16x4 v;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int row0 = vbase + i * 32 + g * 8 + half;
-          bf16x4 v;
-          v[0] = (bf16)(acc[i][j][g * 4 + 0] * s);
-          v[1] = (bf16)(acc[i][j][g * 4 + 1] * s);
-          v[2] = (bf16)(acc[i][j][g * 4 + 2] * s);
-          v[3] = (bf16)(acc[i][j][g * 4 + 3] * s);
-          if (full || row0 + 3 < V) {
-            *(bf16x4*)(zrow + row0) = v;
-          } else {
+        for (int r = 0; r < 4; ++r) v[r] = (bf16)(acc[i][j][r] * s);
+        if (full || row0 + 3 < V) {
+          *(bf16x4*)(zrow + row0) = v;
+        } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (row0 + e < V) zrow[row0 + e] = v[e];
-          }
+          for (int r = 0; r < 4; ++r)
+            if (row0 + r < V) zrow[row0 + r] = v[r];
         }
+      }
     }
   }
 }
@@ -231,24 +268,24 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_splitk_bf16(
     int k_tiles, int splits, float* __restrict__ out, int group_m) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int tiles_m = (int)cdiv(M, kBM), tiles_n = (int)cdiv(N, kBN);
-  const TileCoord tc = tile_coord(tiles_m, tiles_n, splits, group_m);
+  const TileCoord tc = tile_coord(tiles_m, tiles_n, group_m);
   const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
   const int kt0 = (int)((int64_t)k_tiles * tc.split / splits);
   const int kt1 = (int)((int64_t)k_tiles * (tc.split + 1) / splits);
-  floatx16 acc[4][4];
+  Acc acc;
   gemm_mainloop(A, lda, M, m0, B, ldb, N, n0, kt0, kt1 - kt0, smem, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
   float* o = out + (int64_t)tc.split * M * N;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kTM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = n0 + wn * 128 + j * 32 + (lane & 31);
+    for (int j = 0; j < kTN; ++j) {
+      const int col = n0 + acc_col(wn, j, lane);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+      for (int r = 0; r < 4; ++r) {
+        const int row = m0 + acc_row(wm, i, lane, r);
         if (row < M && col < N) o[(int64_t)row * N + col] = acc[i][j][r];
       }
     }
@@ -256,10 +293,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_splitk_bf16(
 
 // ---------------------------------------------------------------------------
 // dW GEMM: A = g^T [V, Cp], B = h^T [H, Cp]; out rows = vocabulary.
-// mode 0: out (bf16) = acc                      (single chunk)
-// mode 1: acc32 = acc                           (first of several chunks)
-// mode 2: acc32 += acc                          (middle chunk)
-// mode 3: out (bf16) = acc32 + acc              (last chunk)
+// kMode 0: out (bf16) = acc                      (single chunk)
+// kMode 1: acc32 = acc                           (first of several chunks)
+// kMode 2: acc32 += acc                          (middle chunk)
+// kMode 3: out (bf16) = acc32 + acc              (last chunk)
 // ---------------------------------------------------------------------------
 template <int kMode>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dw_bf16(
@@ -267,21 +304,21 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dw_bf16(
     int k_tiles, bf16* __restrict__ out, float* __restrict__ acc32, int group_m) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int tiles_m = (int)cdiv(M, kBM), tiles_n = (int)cdiv(N, kBN);
-  const TileCoord tc = tile_coord(tiles_m, tiles_n, 1, group_m);
+  const TileCoord tc = tile_coord(tiles_m, tiles_n, group_m);
   const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
-  floatx16 acc[4][4];
+  Acc acc;
   gemm_mainloop(A, lda, M, m0, B, ldb, N, n0, 0, k_tiles, smem, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kTM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = n0 + wn * 128 + j * 32 + (lane & 31);
+    for (int j = 0; j < kTN; ++j) {
+      const int col = n0 + acc_col(wn, j, lane);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+      for (int r = 0; r < 4; ++r) {
+        const int row = m0 + acc_row(wm, i, lane, r);
         if (row < M && col < N) {
           const int64_t e = (int64_t)row * N + col;
           const float v = acc[i][j][r];

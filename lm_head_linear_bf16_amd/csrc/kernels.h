@@ -57,17 +57,62 @@ __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ src, in
   }
 }
 
-// Column sums of each 64-row slab of src [R, Cn]: colpart[slab, c] (fixed
-// order).  Used for sum_j W[j, :], which gives the row sums of the logits.
+// Column sums of each kColSlab-row slab of src [R, Cn]: colpart[slab, c]
+// (fixed order).  Used for sum_j W[j, :], which gives the row sums of the
+// logits.  Threads run along columns, so each row read is coalesced.
+constexpr int kColSlab = 1024;
 template <typename T>
 __global__ __launch_bounds__(256) void k_colsum_slabs(const T* __restrict__ src, int64_t R,
                                                       int64_t Cn, float* __restrict__ colpart) {
   const int64_t c = (int64_t)blockIdx.y * 256 + threadIdx.x;
   if (c >= Cn) return;
-  const int64_t r0 = (int64_t)blockIdx.x * 64, r1 = min(R, r0 + 64);
+  const int64_t r0 = (int64_t)blockIdx.x * kColSlab, r1 = min(R, r0 + kColSlab);
   float s = 0.f;
   for (int64_t r = r0; r < r1; ++r) s += to_f32(src[r * Cn + c]);
   colpart[(int64_t)blockIdx.x * Cn + c] = s;
+}
+
+// bf16 transpose with 16-byte accesses: 64 x 64 tile, each thread moves
+// 8 consecutive elements in and 8 out.  Same contract as k_transpose.
+__global__ __launch_bounds__(256) void k_transpose_bf16(const bf16* __restrict__ src, int64_t R,
+                                                        int64_t Cn, int64_t lds,
+                                                        bf16* __restrict__ dst, int64_t ldd,
+                                                        int64_t Rp) {
+  __shared__ bf16 tile[64][64 + 8];
+  const int tx = threadIdx.x & 7, ty = threadIdx.x >> 3;  // 8 chunks x 32 rows
+  const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
+  const bool vec_in = (Cn % 8 == 0) && (lds % 8 == 0);
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int lr = ty + 32 * p;
+    const int64_t r = r0 + lr, c = c0 + tx * 8;
+    bf16x8 v;
+    if (r < R && vec_in && c + 8 <= Cn) {
+      v = *(const bf16x8*)(src + r * lds + c);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (r < R && c + e < Cn) ? src[r * lds + c + e] : (bf16)0.f;
+    }
+    *(bf16x8*)&tile[lr][tx * 8] = v;  // rows are 144 B: 16-byte aligned
+  }
+  __syncthreads();
+  const bool vec_out = (ldd % 8 == 0) && (Rp % 8 == 0);
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int lc = ty + 32 * p;
+    const int64_t c = c0 + lc, r = r0 + tx * 8;
+    if (c >= Cn) continue;
+    bf16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = tile[tx * 8 + e][lc];
+    if (vec_out && r + 8 <= Rp) {
+      *(bf16x8*)(dst + c * ldd + r) = v;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (r + e < Rp) dst[c * ldd + r + e] = v[e];
+    }
+  }
 }
 
 // out[c] = sum_b part[b, c], b ascending.
