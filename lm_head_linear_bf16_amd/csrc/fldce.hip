@@ -38,7 +38,7 @@ struct Plan {
   int64_t esz = 0;
   int splits = 1;
   size_t oD = 0, oWT = 0, oColpart = 0, oWsum = 0, oZt = 0, oR = 0, oLse = 0, oRloss = 0,
-         oCoef = 0, oPart = 0, oZ = 0, oGT = 0, oHT = 0, oDHpart = 0, oDW32 = 0;
+         oCoef = 0, oPart = 0, oZ = 0, oG = 0, oGT = 0, oHT = 0, oDHpart = 0, oDW32 = 0;
   size_t total = 0;
 };
 
@@ -65,7 +65,7 @@ int choose_splits(int64_t tiles, int64_t k_tiles) {
 
 int64_t default_chunk(int64_t N, int64_t V, int64_t esz) {
   const int64_t Vp = round_up(V, 64);
-  const int64_t per_row = 2 * esz * Vp;  // z/g [C, Vp] + g^T [Vp, C]
+  const int64_t per_row = (esz == 2 ? 3 : 2) * esz * Vp;  // z, g (bf16 only), g^T
   if (round_up(std::max<int64_t>(N, 1), 64) * per_row <= kZBudgetBytes) return std::max<int64_t>(N, 1);
   int64_t c = (kZBudgetBytes / per_row) / 256 * 256;
   return std::max<int64_t>(c, 256);
@@ -105,6 +105,7 @@ Plan make_plan(int mode, int64_t N, int64_t H, int64_t V, int dtype, int64_t chu
   p.oRloss = take(cur, (size_t)N * 4);
   p.oCoef = take(cur, (size_t)p.C * 4);
   p.oZ = take(cur, (size_t)p.Cp * p.Vp * p.esz);
+  if (bf) p.oG = take(cur, (size_t)p.Cp * p.Vp * p.esz);  // g row-major (z is blocked)
   p.oGT = take(cur, (size_t)p.Vp * p.Cp * p.esz);
   p.oHT = take(cur, (size_t)H * p.Cp * p.esz);
   if (bf) {
@@ -244,6 +245,7 @@ int run_core(const Core& c, const Plan& p, char* ws, hipStream_t st) {
   const bool bf = sizeof(T) == 2;
   T* WT = reinterpret_cast<T*>(ws + p.oWT);
   T* zb = reinterpret_cast<T*>(ws + p.oZ);
+  T* gb = bf ? reinterpret_cast<T*>(ws + p.oG) : zb;  // fp32: g overwrites z in place
   T* gT = reinterpret_cast<T*>(ws + p.oGT);
   T* hT = reinterpret_cast<T*>(ws + p.oHT);
   float* coef = reinterpret_cast<float*>(ws + p.oCoef);
@@ -308,8 +310,12 @@ int run_core(const Core& c, const Plan& p, char* ws, hipStream_t st) {
     {
       StageTimer tm(kDlogits, st);
       dim3 g((unsigned)(Vp / 64), (unsigned)(Cpc / 64));
-      k_gpass<T><<<g, 256, 0, st>>>(zb, Vp, Cc, V, lse_c, coef, c.target + c0, c.v0, c.eps,
-                                    (float)c.Vg, gT, p.Cp);
+      if (bf)
+        k_gpass_blk<<<g, 256, 0, st>>>((const bf16*)zb, Vp, Cc, V, lse_c, coef, c.target + c0, c.v0,
+                                       c.eps, (float)c.Vg, (bf16*)gb, (bf16*)gT, p.Cp);
+      else
+        k_gpass<T><<<g, 256, 0, st>>>(zb, Vp, Cc, V, lse_c, coef, c.target + c0, c.v0, c.eps,
+                                      (float)c.Vg, gT, p.Cp);
     }
     // 4. dH = g W
     if (bf) {
@@ -318,7 +324,7 @@ int run_core(const Core& c, const Plan& p, char* ws, hipStream_t st) {
       {
         StageTimer tm(kDHGemm, st);
         k_gemm_splitk_bf16<<<blocks, kGemmThreads, kGemmLds, st>>>(
-            (const bf16*)zb, Vp, (int)Cc, (const bf16*)WT, Vp, (int)H, (int)(Vp / kBK), S, dHpart,
+            (const bf16*)gb, Vp, (int)Cc, (const bf16*)WT, Vp, (int)H, (int)(Vp / kBK), S, dHpart,
             kGroupM);
       }
       StageTimer tm(kDHReduce, st);

@@ -196,7 +196,8 @@ __device__ __forceinline__ int acc_col(int wn, int j, int lane) { return wn * kT
 //
 // For each token and each 128-wide vocabulary slab (one wave's M range) it
 // writes part[slab * ldp + token] = (max_j z, sum_j exp(z - max)) with
-// z = s * a (kPart); with kStoreZ it stores z (bf16) into zbuf[token, vocab].
+// z = s * a (kPart); with kStoreZ it stores z (bf16) into zbuf in the
+// blocked layout below (ldz = padded vocabulary, a multiple of 64).
 // ---------------------------------------------------------------------------
 template <bool kStoreZ, bool kPart>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_logits_bf16(
@@ -240,19 +241,22 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_logits_bf16(
       if (lane < 16 && tok < C) part[(int64_t)(vbase / 128) * ldp + tok] = floatx2{mx * s, sum};
     }
     if (kStoreZ && tok < C) {
-      bf16* zrow = zbuf + (int64_t)tok * ldz;
+      // blocked layout: zblk(tok, v) = ((tok / 16) * (ldz / 4) + v / 4) * 64 + (tok % 16) * 4 + v % 4,
+      // so one store instruction (16 tokens x 16 vocabulary) writes 512 contiguous bytes
+      bf16* zt = zbuf + ((int64_t)(tok >> 4) * (ldz >> 2)) * 64 + (tok & 15) * 4;
 #pragma unroll
       for (int i = 0; i < kTM; ++i) {
         const int row0 = m0 + acc_row(wm, i, lane, 0);
         bf16x4 v;
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = (bf16)(acc[i][j][r] * s);
+        bf16* dst = zt + (int64_t)(row0 >> 2) * 64;
         if (full || row0 + 3 < V) {
-          *(bf16x4*)(zrow + row0) = v;
+          *(bf16x4*)dst = v;
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (row0 + r < V) zrow[row0 + r] = v[r];
+            if (row0 + r < V) dst[r] = v[r];
         }
       }
     }
