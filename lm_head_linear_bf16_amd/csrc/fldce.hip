@@ -5,13 +5,16 @@
 //
 // One chunk of C token rows (page 1, fused_linear_cross_entropy_forward: the
 // rows are processed in chunks to bound the [C, V] logits buffer):
-//   1. logits GEMM + softmax partials (+ z stored as bf16 / fp32)
+//   1. logits GEMM + softmax partials (+ z stored)
 //   2. per-row combine -> lse, per-row loss, coefficient s / (p_i D)
-//   3. dlogits pass: z -> g in place, and g^T for the dW GEMM
+//   3. dlogits pass: z -> g
 //   4. dH = g W     (split-K GEMM over the vocabulary + ordered reduction)
 //   5. dW += g^T h  (fp32 across chunks, rounded once at the end)
-// Before the loop: divisor D, W^T, column sums of W (label smoothing), target
+// Before the loop: divisor D, column sums of W (label smoothing), target
 // logits and row sums of z by per-row dot products.  After it: the loss.
+// bf16 GEMMs read W and g in their own layouts (one via the LDS transpose
+// read); only the chunk's h is copied transposed.  The fp32 path (float32
+// inputs) uses plain fp32 GEMMs over transposed copies.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -65,7 +68,7 @@ int choose_splits(int64_t tiles, int64_t k_tiles) {
 
 int64_t default_chunk(int64_t N, int64_t V, int64_t esz) {
   const int64_t Vp = round_up(V, 64);
-  const int64_t per_row = (esz == 2 ? 3 : 2) * esz * Vp;  // z, g (bf16 only), g^T
+  const int64_t per_row = 2 * esz * Vp;  // bf16: z and g; fp32: z/g and g^T
   if (round_up(std::max<int64_t>(N, 1), 64) * per_row <= kZBudgetBytes) return std::max<int64_t>(N, 1);
   int64_t c = (kZBudgetBytes / per_row) / 256 * 256;
   return std::max<int64_t>(c, 256);
@@ -98,15 +101,18 @@ Plan make_plan(int mode, int64_t N, int64_t H, int64_t V, int dtype, int64_t chu
     p.total = cur;
     return p;
   }
-  p.oWT = take(cur, (size_t)H * p.Vp * p.esz);
+  if (!bf) p.oWT = take(cur, (size_t)H * p.Vp * p.esz);
   p.oZt = take(cur, (size_t)N * 4);
   p.oR = take(cur, (size_t)N * 4);
   p.oLse = take(cur, (size_t)N * 4);
   p.oRloss = take(cur, (size_t)N * 4);
   p.oCoef = take(cur, (size_t)p.C * 4);
   p.oZ = take(cur, (size_t)p.Cp * p.Vp * p.esz);
-  if (bf) p.oG = take(cur, (size_t)p.Cp * p.Vp * p.esz);  // g row-major (z is blocked)
-  p.oGT = take(cur, (size_t)p.Vp * p.Cp * p.esz);
+  if (bf) {
+    p.oG = take(cur, (size_t)p.Cp * p.Vp * p.esz);  // g row-major (z is blocked)
+  } else {
+    p.oGT = take(cur, (size_t)p.Vp * p.Cp * p.esz);
+  }
   p.oHT = take(cur, (size_t)H * p.Cp * p.esz);
   if (bf) {
     const int64_t tiles = cdiv(p.C, kBM) * cdiv(H, kBN);
@@ -127,7 +133,7 @@ void set_gemm_attributes() {
                               hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
     (void)hipFuncSetAttribute((const void*)k_logits_bf16<false, true>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
-    (void)hipFuncSetAttribute((const void*)k_gemm_splitk_bf16,
+    (void)hipFuncSetAttribute((const void*)k_gemm_dh_bf16,
                               hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
     (void)hipFuncSetAttribute((const void*)k_gemm_dw_bf16<0>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
@@ -240,92 +246,69 @@ struct Core {
   void* dW;              // [V, H] W dtype
 };
 
-template <typename T>
-int run_core(const Core& c, const Plan& p, char* ws, hipStream_t st) {
-  const bool bf = sizeof(T) == 2;
-  T* WT = reinterpret_cast<T*>(ws + p.oWT);
-  T* zb = reinterpret_cast<T*>(ws + p.oZ);
-  T* gb = bf ? reinterpret_cast<T*>(ws + p.oG) : zb;  // fp32: g overwrites z in place
-  T* gT = reinterpret_cast<T*>(ws + p.oGT);
-  T* hT = reinterpret_cast<T*>(ws + p.oHT);
+// per-row stage of a chunk: lse/loss/coefficients (fwd_bwd) or coefficients
+// only (shard backward, lse given).  Returns the chunk's lse pointer.
+const float* run_rows(const Core& c, const Plan& p, const floatx2* part, float* coef, int64_t c0,
+                      int64_t Cc, hipStream_t st) {
+  StageTimer tm(kCombine, st);
+  if (c.lse_in == nullptr) {
+    k_combine_rows<<<grid1(Cc, 32), 256, 0, st>>>(
+        part, p.C, p.nT, Cc, 0, c.target + c0, c.p_mask ? c.p_mask + c0 : nullptr, c.ignore,
+        c.zt + c0, c.R ? c.R + c0 : nullptr, c.eps, (float)c.Vg, c.s, c.D, c.lse_out + c0,
+        c.rloss_out + c0, coef, nullptr, nullptr);
+    return c.lse_out + c0;
+  }
+  k_coef_rows<<<grid1(Cc, 256), 256, 0, st>>>(c.target + c0, c.p_mask ? c.p_mask + c0 : nullptr,
+                                               c.ignore, Cc, c.s, c.D, coef);
+  return c.lse_in + c0;
+}
+
+// bf16: W and g are read in place; only the chunk's h is transposed.
+int run_core_bf16(const Core& c, const Plan& p, char* ws, hipStream_t st) {
+  bf16* zb = reinterpret_cast<bf16*>(ws + p.oZ);
+  bf16* gb = reinterpret_cast<bf16*>(ws + p.oG);
+  bf16* hT = reinterpret_cast<bf16*>(ws + p.oHT);
   float* coef = reinterpret_cast<float*>(ws + p.oCoef);
   floatx2* part = reinterpret_cast<floatx2*>(ws + p.oPart);
   float* dHpart = reinterpret_cast<float*>(ws + p.oDHpart);
   float* dW32 = reinterpret_cast<float*>(ws + p.oDW32);
-  const T* h = static_cast<const T*>(c.h);
-  const T* W = static_cast<const T*>(c.W);
+  const bf16* h = static_cast<const bf16*>(c.h);
+  const bf16* W = static_cast<const bf16*>(c.W);
   const int64_t H = c.H, V = c.V, Vp = p.Vp;
-
-  {
-    StageTimer tm(kPrep, st);
-    launch_transpose<T>(W, V, H, H, WT, Vp, Vp, st);
-  }
   for (int64_t ic = 0; ic < p.nchunks; ++ic) {
     const int64_t c0 = ic * p.C;
     const int64_t Cc = std::min(p.C, c.N - c0);
     const int64_t Cpc = round_up(Cc, 64);
-    const T* hc = h + c0 * H;
+    const bf16* hc = h + c0 * H;
     {
       StageTimer tm(kHT, st);
-      launch_transpose<T>(hc, Cc, H, H, hT, p.Cp, Cpc, st);
+      launch_transpose<bf16>(hc, Cc, H, H, hT, p.Cp, Cpc, st);
     }
-    // 1. logits
-    if (bf) {
+    {  // 1. logits (+ softmax partials)
       StageTimer tm(kLogits, st);
       const int blocks = (int)(cdiv(V, kBM) * cdiv(Cc, kBN));
       if (c.lse_in == nullptr)
         k_logits_bf16<true, true><<<blocks, kGemmThreads, kGemmLds, st>>>(
-            (const bf16*)W, (const bf16*)hc, (int)V, (int)Cc, (int)H, c.s, part, p.C, (bf16*)zb, Vp,
-            kGroupM);
+            W, hc, (int)V, (int)Cc, (int)H, c.s, part, p.C, zb, Vp, kGroupM);
       else
         k_logits_bf16<true, false><<<blocks, kGemmThreads, kGemmLds, st>>>(
-            (const bf16*)W, (const bf16*)hc, (int)V, (int)Cc, (int)H, c.s, part, p.C, (bf16*)zb, Vp,
-            kGroupM);
-    } else {
-      StageTimer tm(kLogits, st);
-      dim3 g((unsigned)cdiv(V, 64), (unsigned)cdiv(Cc, 64));
-      k_gemm_f32_nt<<<g, 256, 0, st>>>((const float*)hc, H, Cc, (const float*)W, H, V, H, c.s,
-                                       (float*)zb, Vp, 0);
-      if (c.lse_in == nullptr) {
-        dim3 g2((unsigned)cdiv(Cc, 64), (unsigned)p.nT);
-        k_row_partials_f32<<<g2, 64, 0, st>>>((const float*)zb, Vp, Cc, V, part, p.C);
-      }
+            W, hc, (int)V, (int)Cc, (int)H, c.s, part, p.C, zb, Vp, kGroupM);
     }
-    // 2. per-row combine (or coefficients only, when lse is given)
-    const float* lse_c;
-    if (c.lse_in == nullptr) {
-      StageTimer tm(kCombine, st);
-      k_combine_rows<<<grid1(Cc, 32), 256, 0, st>>>(
-          part, p.C, p.nT, Cc, 0, c.target + c0, c.p_mask ? c.p_mask + c0 : nullptr, c.ignore,
-          c.zt + c0, c.R ? c.R + c0 : nullptr, c.eps, (float)c.Vg, c.s, c.D, c.lse_out + c0,
-          c.rloss_out + c0, coef, nullptr, nullptr);
-      lse_c = c.lse_out + c0;
-    } else {
-      StageTimer tm(kCombine, st);
-      k_coef_rows<<<grid1(Cc, 256), 256, 0, st>>>(c.target + c0, c.p_mask ? c.p_mask + c0 : nullptr,
-                                                   c.ignore, Cc, c.s, c.D, coef);
-      lse_c = c.lse_in + c0;
-    }
-    // 3. dlogits, in place, plus g^T
-    {
+    // 2. per-row combine
+    const float* lse_c = run_rows(c, p, part, coef, c0, Cc, st);
+    {  // 3. dlogits: blocked z -> row-major g, zero rows Cc .. Cpc-1
       StageTimer tm(kDlogits, st);
       dim3 g((unsigned)(Vp / 64), (unsigned)(Cpc / 64));
-      if (bf)
-        k_gpass_blk<<<g, 256, 0, st>>>((const bf16*)zb, Vp, Cc, V, lse_c, coef, c.target + c0, c.v0,
-                                       c.eps, (float)c.Vg, (bf16*)gb, (bf16*)gT, p.Cp);
-      else
-        k_gpass<T><<<g, 256, 0, st>>>(zb, Vp, Cc, V, lse_c, coef, c.target + c0, c.v0, c.eps,
-                                      (float)c.Vg, gT, p.Cp);
+      k_gpass_blk<<<g, 256, 0, st>>>(zb, Vp, Cc, V, lse_c, coef, c.target + c0, c.v0, c.eps,
+                                     (float)c.Vg, gb);
     }
-    // 4. dH = g W
-    if (bf) {
+    {  // 4. dH = g W (split over the vocabulary, ordered reduction)
       const int S = p.splits;
       const int blocks = (int)(cdiv(Cc, kBM) * cdiv(H, kBN) * S);
       {
         StageTimer tm(kDHGemm, st);
-        k_gemm_splitk_bf16<<<blocks, kGemmThreads, kGemmLds, st>>>(
-            (const bf16*)gb, Vp, (int)Cc, (const bf16*)WT, Vp, (int)H, (int)(Vp / kBK), S, dHpart,
-            kGroupM);
+        k_gemm_dh_bf16<<<blocks, kGemmThreads, kGemmLds, st>>>(gb, Vp, (int)Cc, W, (int)V, (int)H,
+                                                               (int)(Vp / kBK), S, dHpart, kGroupM);
       }
       StageTimer tm(kDHReduce, st);
       if (c.dH_f32)
@@ -334,31 +317,78 @@ int run_core(const Core& c, const Plan& p, char* ws, hipStream_t st) {
       else
         k_splitk_reduce<bf16><<<grid1(Cc * H, 1024), 256, 0, st>>>(dHpart, S, Cc * H,
                                                                    (bf16*)c.dH + c0 * H);
-    } else {
-      StageTimer tm(kDHGemm, st);
-      dim3 g((unsigned)cdiv(H, 64), (unsigned)cdiv(Cc, 64));
-      k_gemm_f32_nt<<<g, 256, 0, st>>>((const float*)zb, Vp, Cc, (const float*)WT, Vp, H, V, 1.f,
-                                       (float*)c.dH + c0 * H, H, 0);
     }
-    // 5. dW += g^T h
-    if (bf) {
+    {  // 5. dW += g^T h
       StageTimer tm(kDWGemm, st);
       int mode = 0;
       if (p.nchunks > 1) mode = ic == 0 ? 1 : (ic + 1 == p.nchunks ? 3 : 2);
       const int blocks = (int)(cdiv(V, kBM) * cdiv(H, kBN));
       auto kern = mode == 0 ? k_gemm_dw_bf16<0>
                             : (mode == 1 ? k_gemm_dw_bf16<1> : (mode == 2 ? k_gemm_dw_bf16<2> : k_gemm_dw_bf16<3>));
-      kern<<<blocks, kGemmThreads, kGemmLds, st>>>((const bf16*)gT, p.Cp, (int)V, (const bf16*)hT,
-                                                   p.Cp, (int)H, (int)(Cpc / kBK), (bf16*)c.dW,
-                                                   dW32, kGroupM);
-    } else {
-      StageTimer tm(kDWGemm, st);
-      dim3 g((unsigned)cdiv(H, 64), (unsigned)cdiv(V, 64));
-      k_gemm_f32_nt<<<g, 256, 0, st>>>((const float*)gT, p.Cp, V, (const float*)hT, p.Cp, H, Cpc,
-                                       1.f, (float*)c.dW, H, ic == 0 ? 0 : 1);
+      kern<<<blocks, kGemmThreads, kGemmLds, st>>>(gb, Vp, (int)Cpc, (int)V, hT, p.Cp, (int)H,
+                                                   (bf16*)c.dW, dW32, kGroupM);
     }
   }
   return launch_status();
+}
+
+// fp32 inputs: plain fp32 GEMMs over transposed copies.
+int run_core_f32(const Core& c, const Plan& p, char* ws, hipStream_t st) {
+  float* WT = reinterpret_cast<float*>(ws + p.oWT);
+  float* zb = reinterpret_cast<float*>(ws + p.oZ);  // z, then g in place
+  float* gT = reinterpret_cast<float*>(ws + p.oGT);
+  float* hT = reinterpret_cast<float*>(ws + p.oHT);
+  float* coef = reinterpret_cast<float*>(ws + p.oCoef);
+  floatx2* part = reinterpret_cast<floatx2*>(ws + p.oPart);
+  const float* h = static_cast<const float*>(c.h);
+  const float* W = static_cast<const float*>(c.W);
+  const int64_t H = c.H, V = c.V, Vp = p.Vp;
+  {
+    StageTimer tm(kPrep, st);
+    launch_transpose<float>(W, V, H, H, WT, Vp, Vp, st);
+  }
+  for (int64_t ic = 0; ic < p.nchunks; ++ic) {
+    const int64_t c0 = ic * p.C;
+    const int64_t Cc = std::min(p.C, c.N - c0);
+    const int64_t Cpc = round_up(Cc, 64);
+    const float* hc = h + c0 * H;
+    {
+      StageTimer tm(kHT, st);
+      launch_transpose<float>(hc, Cc, H, H, hT, p.Cp, Cpc, st);
+    }
+    {
+      StageTimer tm(kLogits, st);
+      dim3 g((unsigned)cdiv(V, 64), (unsigned)cdiv(Cc, 64));
+      k_gemm_f32_nt<<<g, 256, 0, st>>>(hc, H, Cc, W, H, V, H, c.s, zb, Vp, 0);
+      if (c.lse_in == nullptr) {
+        dim3 g2((unsigned)cdiv(Cc, 64), (unsigned)p.nT);
+        k_row_partials_f32<<<g2, 64, 0, st>>>(zb, Vp, Cc, V, part, p.C);
+      }
+    }
+    const float* lse_c = run_rows(c, p, part, coef, c0, Cc, st);
+    {
+      StageTimer tm(kDlogits, st);
+      dim3 g((unsigned)(Vp / 64), (unsigned)(Cpc / 64));
+      k_gpass<float><<<g, 256, 0, st>>>(zb, Vp, Cc, V, lse_c, coef, c.target + c0, c.v0, c.eps,
+                                        (float)c.Vg, gT, p.Cp);
+    }
+    {
+      StageTimer tm(kDHGemm, st);
+      dim3 g((unsigned)cdiv(H, 64), (unsigned)cdiv(Cc, 64));
+      k_gemm_f32_nt<<<g, 256, 0, st>>>(zb, Vp, Cc, WT, Vp, H, V, 1.f, (float*)c.dH + c0 * H, H, 0);
+    }
+    {
+      StageTimer tm(kDWGemm, st);
+      dim3 g((unsigned)cdiv(H, 64), (unsigned)cdiv(V, 64));
+      k_gemm_f32_nt<<<g, 256, 0, st>>>(gT, p.Cp, V, hT, p.Cp, H, Cpc, 1.f, (float*)c.dW, H,
+                                       ic == 0 ? 0 : 1);
+    }
+  }
+  return launch_status();
+}
+
+int run_core(const Core& c, const Plan& p, char* ws, hipStream_t st) {
+  return c.dtype == FLDCE_DTYPE_BF16 ? run_core_bf16(c, p, ws, st) : run_core_f32(c, p, ws, st);
 }
 
 void zero_fill(void* p, int64_t n_elems, int esz, hipStream_t st) {
@@ -466,7 +496,7 @@ int fldce_fwd_bwd(const void* h, const void* W, const int64_t* target, const flo
                                                     smooth ? R : nullptr);
     }
   }
-  rc = dtype == FLDCE_DTYPE_BF16 ? run_core<bf16>(c, p, ws, st) : run_core<float>(c, p, ws, st);
+  rc = run_core(c, p, ws, st);
   if (rc != FLDCE_OK) return rc;
   {
     StageTimer tm(kLoss, st);
@@ -574,7 +604,7 @@ int fldce_shard_bwd(const void* h, const void* W_local, const int64_t* target, c
   Core c{h, W_local, target, p_mask, N, H, V_local, vocab_start, V_global, dtype, ignore_index,
          label_smoothing, logit_scale, lse, nullptr, nullptr, nullptr, nullptr, D, dH_partial,
          true, dW_local};
-  return dtype == FLDCE_DTYPE_BF16 ? run_core<bf16>(c, p, ws, st) : run_core<float>(c, p, ws, st);
+  return run_core(c, p, ws, st);
 }
 
 int fldce_profile_num_stages(void) { return kNumStages; }

@@ -1,10 +1,11 @@
 // bf16 MFMA GEMM core for gfx950 and the three contractions of the fused
 // LM-head cross-entropy built on it.
 //
-// Every GEMM here is "NT": C[m, n] = sum_k A[m, k] * B[n, k] with both A and
-// B row-major and K contiguous, bf16 in, fp32 accumulate.  Operands whose K
-// is not contiguous in the caller's layout are transposed once into the
-// workspace beforehand (W^T, h^T, g^T), so one main loop serves all three.
+// Every GEMM here computes C[m, n] = sum_k A(m, k) B(n, k), bf16 in, fp32
+// accumulate, with each operand read in its natural row-major layout: either
+// K contiguous (h and W for the logits, g for dH) or K as the row index (W
+// for dH, g and h for dW), the latter transposed on its way out of LDS by
+// the gfx950 transpose read.  No operand is transposed in memory.
 //
 // Tiling (CDNA4: 64-wide waves, 160 KB LDS, v_mfma_f32_16x16x32_bf16):
 //   * block tile 256 x 256, K step 64, 512 threads = 8 waves in a 2 (M) x 4
@@ -86,12 +87,115 @@ __device__ __forceinline__ void interleave_groups() {
 }
 
 typedef floatx4 Acc[kTM][kTN];
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Operand tiles.  Tile<false>: the operand is row-major with K contiguous
+// (rows = the M or N index); its LDS tile is 256 rows x 64 K (128 B rows,
+// 16-byte chunk c of row r at position lds_chunk(c, r)); a fragment is one
+// 16-byte LDS read.
+//
+// Tile<true>: the operand is row-major with K as the ROW index (e.g. W [V, H]
+// as the K = V operand of dH, or g [C, V] and h [C, H] as the K = C operands
+// of dW); its LDS tile is 64 K-rows x 256 columns (512 B rows, 32-byte
+// segment s of row r at position s ^ tr_swz(r)) and a fragment is gathered
+// with two ds_read_b64_tr_b16.  Within each 16-lane group that instruction
+// returns, to lane i, element (i mod 4) of the 8-byte reads of lanes
+// i/4, 4 + i/4, 8 + i/4, 12 + i/4; when those lanes read rows k..k+3 at
+// columns 4*(lane mod 4), lane i receives column i of rows k..k+3, i.e. four
+// consecutive K of its own row, which is the MFMA operand layout.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int tr_swz(int r) { return (r & 3) | (((r >> 3) & 1) << 2); }
+
+template <bool kTr>
+struct Tile;
+
+template <>
+struct Tile<false> {
+  static constexpr int kReads = 1;  // LDS reads per fragment
+  const bf16* p[4];
+  // rows = number of valid rows (M or N); r0 = first row of the tile
+  __device__ __forceinline__ void init(const bf16* X, int64_t ldx, int rows, int cols, int r0,
+                                       int64_t k_begin, int lane, int wave) {
+    (void)cols;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = i * kWaves * 8 + wave * 8 + (lane >> 3);
+      p[i] = X + (int64_t)min(r0 + r, rows - 1) * ldx + lds_chunk(lane & 7, r) * 8 + k_begin;
+    }
+  }
+  __device__ __forceinline__ void issue(char* tile, int t, int wave) const {
+    char* s = tile + wave * 8 * 128;
+    const int64_t ko = (int64_t)t * kBK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(FLDCE_GPTR(p[i] + ko), FLDCE_LPTR(s + i * kWaves * 8 * 128), 16, 0, 0);
+  }
+  // fragments for 16-row sub-tiles at rows off + 16 t
+  template <int T>
+  __device__ __forceinline__ void frags(const char* tile, int ks, int off, int lane, bf16x8 (&f)[T]) const {
+    const char* b = tile + (off + (lane & 15)) * 128 + (lds_chunk(ks * 4 + (lane >> 4), lane & 15) << 4);
+#pragma unroll
+    for (int t = 0; t < T; ++t) f[t] = *(const bf16x8*)(b + t * 16 * 128);
+  }
+};
+
+template <>
+struct Tile<true> {
+  static constexpr int kReads = 2;
+  const bf16* p[4];  // column pointers (row 0 of the source)
+  int64_t ldx;
+  int krows, k_begin;
+  // rows = number of valid K rows of the source; cols = valid columns;
+  // r0 = first column of the tile; k_begin = first K row
+  __device__ __forceinline__ void init(const bf16* X, int64_t ld, int rows, int cols, int c0,
+                                       int64_t kb, int lane, int wave) {
+    ldx = ld;
+    krows = rows;
+    k_begin = (int)kb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = i * 16 + wave * 2 + (lane >> 5);  // LDS row this lane fills
+      const int pos = lane & 31;                       // 16-byte unit in the 512 B row
+      const int u = (((pos >> 1) ^ tr_swz(r)) << 1) | (pos & 1);
+      p[i] = X + min(c0 + u * 8, cols - 8);
+    }
+  }
+  __device__ __forceinline__ void issue(char* tile, int t, int wave) const {
+    char* s = tile + wave * 2 * 512;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = min(k_begin + t * kBK + i * 16 + wave * 2 + (lane >> 5), krows - 1);
+      __builtin_amdgcn_global_load_lds(FLDCE_GPTR(p[i] + (int64_t)row * ldx), FLDCE_LPTR(s + i * 16 * 512), 16,
+                                       0, 0);
+    }
+  }
+  template <int T>
+  __device__ __forceinline__ void frags(const char* tile, int ks, int off, int lane, bf16x8 (&f)[T]) const {
+    const int grp = lane >> 4, s4 = lane & 15;
+    const int fsw = tr_swz(grp * 8 + (s4 >> 2));
+    const char* b = tile + (ks * 32 + grp * 8 + (s4 >> 2)) * 512 + (s4 & 3) * 8;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const char* q = b + (((off >> 4) + t) ^ fsw) * 32;
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4i16 __attribute__((address_space(3)))*)(q));
+      const v4i16 hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4i16 __attribute__((address_space(3)))*)(q + 4 * 512));
+      f[t] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  }
+};
 
 // Main loop: acc[i][j] (wave sub-tile i along M, j along N) accumulates
-// A[m0 .. m0+255, k] * B[n0 .. n0+255, k] over K tiles [kt0, kt0 + nk).
-__device__ __forceinline__ void gemm_mainloop(const bf16* __restrict__ A, int64_t lda, int M, int m0,
-                                              const bf16* __restrict__ B, int64_t ldb, int N, int n0,
-                                              int64_t kt0, int nk, char* smem, Acc& acc) {
+// sum_k A(m, k) B(n, k) for m in [m0, m0+256), n in [n0, n0+256) over K tiles
+// [kt0, kt0 + nk).  For a normal operand X_rows/X_cols are (valid rows,
+// unused); for a transposed one (valid K rows, valid columns).
+template <bool kATr, bool kBTr>
+__device__ __forceinline__ void gemm_mainloop(const bf16* __restrict__ A, int64_t lda, int a_rows,
+                                              int a_cols, int m0, const bf16* __restrict__ B,
+                                              int64_t ldb, int b_rows, int b_cols, int n0, int64_t kt0,
+                                              int nk, char* smem, Acc& acc) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / kWavesN, wn = wave % kWavesN;
@@ -101,47 +205,17 @@ __device__ __forceinline__ void gemm_mainloop(const bf16* __restrict__ A, int64_
     for (int j = 0; j < kTN; ++j) acc[i][j] = floatx4{};
   if (nk <= 0) return;
 
-  // Loads: wave w, round i fills LDS rows i*64 + w*8 .. +7; lane -> row
-  // (lane >> 3), chunk position (lane & 7), which holds the logical chunk
-  // lds_chunk(lane & 7, row) (the map is its own inverse).
-  const int rr = lane >> 3;
-  const bf16* pA[kRoundsA];
-  const bf16* pB[kRoundsB];
-#pragma unroll
-  for (int i = 0; i < kRoundsA; ++i) {
-    const int r = i * kWaves * 8 + wave * 8 + rr;
-    pA[i] = A + (int64_t)min(m0 + r, M - 1) * lda + lds_chunk(lane & 7, r) * 8 + kt0 * kBK;
-  }
-#pragma unroll
-  for (int i = 0; i < kRoundsB; ++i) {
-    const int r = i * kWaves * 8 + wave * 8 + rr;
-    pB[i] = B + (int64_t)min(n0 + r, N - 1) * ldb + lds_chunk(lane & 7, r) * 8 + kt0 * kBK;
-  }
+  Tile<kATr> ta;
+  Tile<kBTr> tb;
+  ta.init(A, lda, a_rows, a_cols, m0, kt0 * kBK, lane, wave);
+  tb.init(B, ldb, b_rows, b_cols, n0, kt0 * kBK, lane, wave);
   auto issue = [&](int stage, int t) {
-    char* sA = smem + stage * kStageBytes + wave * 8 * 128;
-    char* sB = sA + kABytes;
-    const int64_t ko = (int64_t)t * kBK;
-#pragma unroll
-    for (int i = 0; i < kRoundsA; ++i)
-      __builtin_amdgcn_global_load_lds(FLDCE_GPTR(pA[i] + ko), FLDCE_LPTR(sA + i * kWaves * 8 * 128), 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < kRoundsB; ++i)
-      __builtin_amdgcn_global_load_lds(FLDCE_GPTR(pB[i] + ko), FLDCE_LPTR(sB + i * kWaves * 8 * 128), 16, 0, 0);
+    ta.issue(smem + stage * kStageBytes, t, wave);
+    tb.issue(smem + stage * kStageBytes + kABytes, t, wave);
   };
-  // Fragments of v_mfma_f32_16x16x32_bf16: lane -> row (lane & 15), 8
-  // consecutive k at chunk (ks * 4 + (lane >> 4)) of the 64-wide tile.
-  const int offA = (wm * kTM * 16 + (lane & 15)) * 128;
-  const int offB = kABytes + (wn * kTN * 16 + (lane & 15)) * 128;
-  int posk[2];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) posk[ks] = lds_chunk(ks * 4 + (lane >> 4), lane & 15) << 4;
   auto frags = [&](int stage, int ks, bf16x8(&a)[kTM], bf16x8(&b)[kTN]) {
-    const char* sA = smem + stage * kStageBytes + offA + posk[ks];
-    const char* sB = smem + stage * kStageBytes + offB + posk[ks];
-#pragma unroll
-    for (int i = 0; i < kTM; ++i) a[i] = *(const bf16x8*)(sA + i * 16 * 128);
-#pragma unroll
-    for (int j = 0; j < kTN; ++j) b[j] = *(const bf16x8*)(sB + j * 16 * 128);
+    ta.template frags<kTM>(smem + stage * kStageBytes, ks, wm * kTM * 16, lane, a);
+    tb.template frags<kTN>(smem + stage * kStageBytes + kABytes, ks, wn * kTN * 16, lane, b);
   };
   auto mma = [&](const bf16x8(&a)[kTM], const bf16x8(&b)[kTN], int i0, int i1) {
 #pragma unroll
@@ -151,7 +225,9 @@ __device__ __forceinline__ void gemm_mainloop(const bf16* __restrict__ A, int64_
         if (i * kTN + j >= i0 && i * kTN + j < i1)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
   };
-  constexpr int NM = kTM * kTN, ND = kTM + kTN, NH = NM / 2;
+  constexpr int NM = kTM * kTN, NH = NM / 2;
+  constexpr int ND = kTM * Tile<kATr>::kReads + kTN * Tile<kBTr>::kReads;
+  constexpr int ND1 = ND < NM ? ND : NM, ND2 = ND < NM - NH ? ND : NM - NH;
   bf16x8 fa0[kTM], fb0[kTN], fa1[kTM], fb1[kTN];
   issue(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -162,7 +238,7 @@ __device__ __forceinline__ void gemm_mainloop(const bf16* __restrict__ A, int64_
     const int st = t & 1;
     frags(st, 1, fa1, fb1);
     mma(fa0, fb0, 0, NM);
-    interleave_groups<0, NM, ND>();
+    interleave_groups<0, NM, ND1>();
     __builtin_amdgcn_sched_barrier(0);
     mma(fa1, fb1, 0, NH);
     __builtin_amdgcn_sched_barrier(0);
@@ -174,7 +250,7 @@ __device__ __forceinline__ void gemm_mainloop(const bf16* __restrict__ A, int64_
     issue(st, min(t + 2, nk - 1));
     frags(st ^ 1, 0, fa0, fb0);
     mma(fa1, fb1, NH, NM);
-    interleave_groups<0, NM - NH, ND>();
+    interleave_groups<0, NM - NH, ND2>();
     __builtin_amdgcn_sched_barrier(0);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -208,7 +284,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_logits_bf16(
   const TileCoord tc = tile_coord(tiles_m, tiles_n, group_m);
   const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
   Acc acc;
-  gemm_mainloop(W, H, V, m0, h, H, C, n0, 0, H / kBK, smem, acc);
+  gemm_mainloop<false, false>(W, H, V, 0, m0, h, H, C, 0, n0, 0, H / kBK, smem, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN;
@@ -264,24 +340,26 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_logits_bf16(
 }
 
 // ---------------------------------------------------------------------------
-// Split-K GEMM with fp32 output: out[split][m][n] = sum over this split's K
-// tiles.  Used for dH = g W (A = g [C, Vp], B = W^T [H, Vp]).
+// dH = g W, split over K = vocabulary: out[split][m][n] (fp32) for this
+// split's K tiles.  A = g [M = C tokens, ldg] (K contiguous); B = W read as
+// K rows (vocabulary rows of W [V, H], transposed in LDS).  Rows of W past
+// V are clamped: g is zero in those columns.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_splitk_bf16(
-    const bf16* __restrict__ A, int64_t lda, int M, const bf16* __restrict__ B, int64_t ldb, int N,
+__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dh_bf16(
+    const bf16* __restrict__ g, int64_t ldg, int M, const bf16* __restrict__ W, int V, int H,
     int k_tiles, int splits, float* __restrict__ out, int group_m) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
-  const int tiles_m = (int)cdiv(M, kBM), tiles_n = (int)cdiv(N, kBN);
+  const int tiles_m = (int)cdiv(M, kBM), tiles_n = (int)cdiv(H, kBN);
   const TileCoord tc = tile_coord(tiles_m, tiles_n, group_m);
   const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
   const int kt0 = (int)((int64_t)k_tiles * tc.split / splits);
   const int kt1 = (int)((int64_t)k_tiles * (tc.split + 1) / splits);
   Acc acc;
-  gemm_mainloop(A, lda, M, m0, B, ldb, N, n0, kt0, kt1 - kt0, smem, acc);
+  gemm_mainloop<false, true>(g, ldg, M, 0, m0, W, H, V, H, n0, kt0, kt1 - kt0, smem, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN;
-  float* o = out + (int64_t)tc.split * M * N;
+  float* o = out + (int64_t)tc.split * M * H;
 #pragma unroll
   for (int i = 0; i < kTM; ++i)
 #pragma unroll
@@ -290,13 +368,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_splitk_bf16(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = m0 + acc_row(wm, i, lane, r);
-        if (row < M && col < N) o[(int64_t)row * N + col] = acc[i][j][r];
+        if (row < M && col < H) o[(int64_t)row * H + col] = acc[i][j][r];
       }
     }
 }
 
 // ---------------------------------------------------------------------------
-// dW GEMM: A = g^T [V, Cp], B = h^T [H, Cp]; out rows = vocabulary.
+// dW = g^T h over K = the chunk's tokens.  A = g [Kp token rows, ldg] read as
+// K rows (vocabulary columns, transposed in LDS); B = h^T [H, ldh] with the
+// chunk's tokens contiguous (a 2 * H * Kp byte copy made per chunk: reading
+// both operands transposed measured ~8% slower than one).  g rows and h^T
+// columns C..Kp-1 are zero.
 // kMode 0: out (bf16) = acc                      (single chunk)
 // kMode 1: acc32 = acc                           (first of several chunks)
 // kMode 2: acc32 += acc                          (middle chunk)
@@ -304,14 +386,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_splitk_bf16(
 // ---------------------------------------------------------------------------
 template <int kMode>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dw_bf16(
-    const bf16* __restrict__ A, int64_t lda, int M, const bf16* __restrict__ B, int64_t ldb, int N,
-    int k_tiles, bf16* __restrict__ out, float* __restrict__ acc32, int group_m) {
+    const bf16* __restrict__ g, int64_t ldg, int Kp, int V, const bf16* __restrict__ hT,
+    int64_t ldh, int H, bf16* __restrict__ out, float* __restrict__ acc32, int group_m) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
-  const int tiles_m = (int)cdiv(M, kBM), tiles_n = (int)cdiv(N, kBN);
+  const int tiles_m = (int)cdiv(V, kBM), tiles_n = (int)cdiv(H, kBN);
   const TileCoord tc = tile_coord(tiles_m, tiles_n, group_m);
   const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
   Acc acc;
-  gemm_mainloop(A, lda, M, m0, B, ldb, N, n0, 0, k_tiles, smem, acc);
+  gemm_mainloop<true, false>(g, ldg, Kp, (int)ldg, m0, hT, ldh, H, 0, n0, 0, Kp / kBK, smem, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN;
@@ -323,8 +405,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dw_bf16(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = m0 + acc_row(wm, i, lane, r);
-        if (row < M && col < N) {
-          const int64_t e = (int64_t)row * N + col;
+        if (row < V && col < H) {
+          const int64_t e = (int64_t)row * H + col;
           const float v = acc[i][j][r];
           if (kMode == 0) out[e] = (bf16)v;
           else if (kMode == 1) acc32[e] = v;

@@ -330,17 +330,17 @@ __global__ __launch_bounds__(256) void k_gpass(T* __restrict__ z, int64_t ldz, i
 // ---------------------------------------------------------------------------
 // dlogits for the bf16 path (same formula as k_gpass), reading z from the
 // blocked layout the logits GEMM writes: element (token t, column v) at
-// ((t / 16) * (ldz / 4) + v / 4) * 64 + (t % 16) * 4 + v % 4.  Writes g
-// row-major [C, ldz] (dH operand) and g^T [ldz, ldt] (dW operand).  One
-// block = 64 tokens x 64 columns; every global access is 16 bytes.
+// ((t / 16) * (ldz / 4) + v / 4) * 64 + (t % 16) * 4 + v % 4, and writing g
+// row-major [rows, ldz] for both backward GEMMs.  Rows C .. (grid rows) - 1
+// and columns >= V are written as zeros.  One block = 64 tokens x 64
+// columns; every global access is 16 bytes.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_gpass_blk(const bf16* __restrict__ zblk, int64_t ldz,
                                                    int64_t C, int64_t V,
                                                    const float* __restrict__ lse,
                                                    const float* __restrict__ coef,
                                                    const int64_t* __restrict__ target, int64_t v0,
-                                                   float eps, float Vg, bf16* __restrict__ g,
-                                                   bf16* __restrict__ gT, int64_t ldt) {
+                                                   float eps, float Vg, bf16* __restrict__ g) {
   __shared__ bf16 tile[64][64 + 8];  // [token][column]
   const int tid = threadIdx.x;
   const int64_t i0 = (int64_t)blockIdx.y * 64, j0 = (int64_t)blockIdx.x * 64;
@@ -348,13 +348,13 @@ __global__ __launch_bounds__(256) void k_gpass_blk(const bf16* __restrict__ zblk
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     const int idx = tid + 256 * p;
-    const int tb = idx >> 7;          // token block (16 tokens) within the tile
-    const int u = idx & 127;          // 16-byte unit within the block's 2 KB run
+    const int tb = idx >> 7;           // token block (16 tokens) within the tile
+    const int u = idx & 127;           // 16-byte unit within the block's 2 KB run
     const int vb = u >> 3, w = u & 7;  // column block (4 columns), unit within the 128 B chunk
     const int tl0 = tb * 16 + w * 2;   // this unit holds tokens tl0, tl0 + 1 x 4 columns
-    float gv[8];
+    bf16x4 out[2];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) gv[e] = 0.f;
+    for (int q = 0; q < 2; ++q) out[q] = bf16x4{};
     float cf[2], l2[2], tg[2];
     int64_t yc[2];
     bool any = false;
@@ -373,28 +373,23 @@ __global__ __launch_bounds__(256) void k_gpass_blk(const bf16* __restrict__ zblk
       for (int e = 0; e < 8; ++e) {
         const int q = e >> 2;
         const int64_t j = j0 + vb * 4 + (e & 3);
+        float v = 0.f;
         if (cf[q] != 0.f && j < V) {
-          float v = cf[q] * (fast_exp2(__builtin_fmaf((float)zv[e], kLog2e, -l2[q])) - epsV);
+          v = cf[q] * (fast_exp2(__builtin_fmaf((float)zv[e], kLog2e, -l2[q])) - epsV);
           if (j == yc[q]) v -= tg[q];
-          gv[e] = v;
         }
+        out[q][e & 3] = (bf16)v;
       }
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) tile[tl0 + (e >> 2)][vb * 4 + (e & 3)] = (bf16)gv[e];
+    for (int q = 0; q < 2; ++q) *(bf16x4*)&tile[tl0 + q][vb * 4] = out[q];
   }
   __syncthreads();
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     const int unit = tid + 256 * p;
     const int r = unit >> 3, c = unit & 7;
-    // g row-major: token row r, columns c*8 .. c*8+7
-    if (i0 + r < C) *(bf16x8*)(g + (i0 + r) * ldz + j0 + c * 8) = *(const bf16x8*)&tile[r][c * 8];
-    // g^T: column row r, tokens c*8 .. c*8+7
-    bf16x8 t;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) t[e] = tile[c * 8 + e][r];
-    *(bf16x8*)(gT + (j0 + r) * ldt + i0 + c * 8) = t;
+    *(bf16x8*)(g + (i0 + r) * ldz + j0 + c * 8) = *(const bf16x8*)&tile[r][c * 8];
   }
 }
 

@@ -15,7 +15,8 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libfldce.so")
+# FLDCE_LIB may point at another build of the same library (A/B timing)
+LIB_PATH = os.environ.get("FLDCE_LIB") or os.path.join(_HERE, "libfldce.so")
 
 DTYPE_F32, DTYPE_BF16 = 0, 1
 REDUCTION_SUM, REDUCTION_MEAN = 0, 1
