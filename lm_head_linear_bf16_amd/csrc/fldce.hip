@@ -41,7 +41,8 @@ struct Plan {
   int64_t esz = 0;
   int splits = 1;
   size_t oD = 0, oWT = 0, oColpart = 0, oWsum = 0, oZt = 0, oR = 0, oLse = 0, oRloss = 0,
-         oCoef = 0, oPart = 0, oZ = 0, oG = 0, oGT = 0, oHT = 0, oDHpart = 0, oDW32 = 0;
+         oCoef = 0, oPart = 0, oRpart = 0, oZ = 0, oG = 0, oGT = 0, oHT = 0, oDHpart = 0,
+         oDW32 = 0;
   size_t total = 0;
 };
 
@@ -96,6 +97,7 @@ Plan make_plan(int mode, int64_t N, int64_t H, int64_t V, int dtype, int64_t chu
   p.oColpart = take(cur, (size_t)cdiv(V, kColSlab) * H * 4);
   p.oWsum = take(cur, (size_t)H * 4);
   p.oPart = take(cur, (size_t)p.nT * p.C * 8);
+  p.oRpart = take(cur, (size_t)p.nT * p.C * 4);  // per-slab row sums of z (label smoothing)
   if (mode == kShardPartials) {
     if (!bf) p.oZ = take(cur, (size_t)p.C * p.Vp * 4);
     p.total = cur;
@@ -220,6 +222,14 @@ void launch_transpose(const T* src, int64_t R, int64_t Cn, int64_t lds, T* dst, 
 // wsum[c] = sum_j W[j, c] (two ordered passes).
 template <typename T>
 void launch_colsum(const T* W, int64_t V, int64_t H, float* colpart, float* wsum, hipStream_t st) {
+  if constexpr (sizeof(T) == 2) {
+    if (H % 8 == 0) {
+      dim3 g((unsigned)cdiv(V, kColSlab), (unsigned)cdiv(H, 256 * 8));
+      k_colsum_slabs_bf16<<<g, 256, 0, st>>>(W, V, H, colpart);
+      k_colsum_finish<<<grid1(H, 256), 256, 0, st>>>(colpart, cdiv(V, kColSlab), H, wsum);
+      return;
+    }
+  }
   dim3 g((unsigned)cdiv(V, kColSlab), (unsigned)cdiv(H, 256));
   k_colsum_slabs<T><<<g, 256, 0, st>>>(W, V, H, colpart);
   k_colsum_finish<<<grid1(H, 256), 256, 0, st>>>(colpart, cdiv(V, kColSlab), H, wsum);
@@ -239,7 +249,8 @@ struct Core {
   float* lse_out;        // fwd_bwd: per-row lse  [N]
   float* rloss_out;      // fwd_bwd: per-row loss [N]
   const float* zt;       // fwd_bwd: target logits [N]
-  const float* R;        // fwd_bwd: row sums of z [N] or nullptr
+  const float* R;        // fwd_bwd fp32: row sums of z [N] or nullptr
+  float* rpart;          // fwd_bwd bf16: per-slab row sums from the logits epilogue, or nullptr
   const float* D;
   void* dH;              // [N, H]: h dtype (fwd_bwd) or fp32 (shard)
   bool dH_f32;
@@ -253,9 +264,9 @@ const float* run_rows(const Core& c, const Plan& p, const floatx2* part, float* 
   StageTimer tm(kCombine, st);
   if (c.lse_in == nullptr) {
     k_combine_rows<<<grid1(Cc, 32), 256, 0, st>>>(
-        part, p.C, p.nT, Cc, 0, c.target + c0, c.p_mask ? c.p_mask + c0 : nullptr, c.ignore,
-        c.zt + c0, c.R ? c.R + c0 : nullptr, c.eps, (float)c.Vg, c.s, c.D, c.lse_out + c0,
-        c.rloss_out + c0, coef, nullptr, nullptr);
+        part, c.rpart, p.C, p.nT, Cc, 0, c.target + c0, c.p_mask ? c.p_mask + c0 : nullptr,
+        c.ignore, c.zt + c0, c.R ? c.R + c0 : nullptr, c.eps, (float)c.Vg, c.s, c.D,
+        c.lse_out + c0, c.rloss_out + c0, coef, nullptr, nullptr, nullptr);
     return c.lse_out + c0;
   }
   k_coef_rows<<<grid1(Cc, 256), 256, 0, st>>>(c.target + c0, c.p_mask ? c.p_mask + c0 : nullptr,
@@ -289,16 +300,16 @@ int run_core_bf16(const Core& c, const Plan& p, char* ws, hipStream_t st) {
       const int blocks = (int)(cdiv(V, kBM) * cdiv(Cc, kBN));
       if (c.lse_in == nullptr)
         k_logits_bf16<true, true><<<blocks, kGemmThreads, kGemmLds, st>>>(
-            W, hc, (int)V, (int)Cc, (int)H, c.s, part, p.C, zb, Vp, kGroupM);
+            W, hc, (int)V, (int)Cc, (int)H, c.s, part, c.rpart, p.C, zb, Vp, kGroupM);
       else
         k_logits_bf16<true, false><<<blocks, kGemmThreads, kGemmLds, st>>>(
-            W, hc, (int)V, (int)Cc, (int)H, c.s, part, p.C, zb, Vp, kGroupM);
+            W, hc, (int)V, (int)Cc, (int)H, c.s, part, nullptr, p.C, zb, Vp, kGroupM);
     }
     // 2. per-row combine
     const float* lse_c = run_rows(c, p, part, coef, c0, Cc, st);
     {  // 3. dlogits: blocked z -> row-major g, zero rows Cc .. Cpc-1
       StageTimer tm(kDlogits, st);
-      dim3 g((unsigned)(Vp / 64), (unsigned)(Cpc / 64));
+      dim3 g((unsigned)cdiv(Vp, kGpassCols), (unsigned)(Cpc / 64));
       k_gpass_blk<<<g, 256, 0, st>>>(zb, Vp, Cc, V, lse_c, coef, c.target + c0, c.v0, c.eps,
                                      (float)c.Vg, gb);
     }
@@ -477,17 +488,19 @@ int fldce_fwd_bwd(const void* h, const void* W, const int64_t* target, const flo
   float* R = reinterpret_cast<float*>(ws + p.oR);
   float* lse = row_lse ? row_lse : reinterpret_cast<float*>(ws + p.oLse);
   float* rl = row_loss ? row_loss : reinterpret_cast<float*>(ws + p.oRloss);
+  const bool bf = dtype == FLDCE_DTYPE_BF16;
+  float* rpart = reinterpret_cast<float*>(ws + p.oRpart);
+  // row sums of z: bf16 from the logits epilogue, fp32 from <h_i, sum_j W_j>
   Core c{h, W, target, p_mask, N, H, V, 0, V, dtype, ignore_index, label_smoothing, logit_scale,
-         nullptr, lse, rl, zt, smooth ? R : nullptr, D, dH, false, dW};
+         nullptr, lse, rl, zt, (smooth && !bf) ? R : nullptr, (smooth && bf) ? rpart : nullptr, D,
+         dH, false, dW};
   {
     StageTimer tm(kPrep, st);
     k_divisor<<<1, 1024, 0, st>>>(target, N, ignore_index, reduction, total, D);
-    if (dtype == FLDCE_DTYPE_BF16) {
-      if (smooth) launch_colsum<bf16>((const bf16*)W, V, H, colpart, wsum, st);
+    if (bf) {
       k_rowdot<bf16><<<grid1(N, 4), 256, 0, st>>>((const bf16*)h, (const bf16*)W, H, target, 0,
-                                                   V, ignore_index, logit_scale,
-                                                   smooth ? wsum : nullptr, N, zt,
-                                                   smooth ? R : nullptr);
+                                                   V, ignore_index, logit_scale, nullptr, N, zt,
+                                                   nullptr);
     } else {
       if (smooth) launch_colsum<float>((const float*)W, V, H, colpart, wsum, st);
       k_rowdot<float><<<grid1(N, 4), 256, 0, st>>>((const float*)h, (const float*)W, H, target,
@@ -523,6 +536,7 @@ int fldce_shard_partials(const void* h, const void* W_local, const int64_t* targ
   set_gemm_attributes();
   char* ws = static_cast<char*>(workspace);
   floatx2* part = reinterpret_cast<floatx2*>(ws + p.oPart);
+  float* rpart = reinterpret_cast<float*>(ws + p.oRpart);
   float* colpart = reinterpret_cast<float*>(ws + p.oColpart);
   float* wsum = reinterpret_cast<float*>(ws + p.oWsum);
   const int64_t V = V_local;
@@ -531,21 +545,20 @@ int fldce_shard_partials(const void* h, const void* W_local, const int64_t* targ
     {
       StageTimer tm(kLogits, st);
       k_logits_bf16<false, true><<<blocks, kGemmThreads, kGemmLds, st>>>(
-          (const bf16*)W_local, (const bf16*)h, (int)V, (int)N, (int)H, logit_scale, part, p.C,
-          nullptr, 0, kGroupM);
+          (const bf16*)W_local, (const bf16*)h, (int)V, (int)N, (int)H, logit_scale, part,
+          row_sumlogit ? rpart : nullptr, p.C, nullptr, 0, kGroupM);
     }
     {
       StageTimer tm(kCombine, st);
-      k_combine_rows<<<grid1(N, 32), 256, 0, st>>>(part, p.C, p.nT, N, 1, nullptr, nullptr, 0,
-                                                   nullptr, nullptr, 0.f, 1.f, 1.f, nullptr,
-                                                   nullptr, nullptr, nullptr, row_max, row_sumexp);
+      k_combine_rows<<<grid1(N, 32), 256, 0, st>>>(
+          part, row_sumlogit ? rpart : nullptr, p.C, p.nT, N, 1, nullptr, nullptr, 0, nullptr,
+          nullptr, 0.f, 1.f, 1.f, nullptr, nullptr, nullptr, nullptr, row_max, row_sumexp,
+          row_sumlogit);
     }
     StageTimer tm(kPrep, st);
-    if (row_sumlogit) launch_colsum<bf16>((const bf16*)W_local, V, H, colpart, wsum, st);
     k_rowdot<bf16><<<grid1(N, 4), 256, 0, st>>>((const bf16*)h, (const bf16*)W_local, H, target,
                                                  vocab_start, V, ignore_index, logit_scale,
-                                                 row_sumlogit ? wsum : nullptr, N, target_logit,
-                                                 row_sumlogit);
+                                                 nullptr, N, target_logit, nullptr);
   } else {
     float* zb = reinterpret_cast<float*>(ws + p.oZ);
     for (int64_t c0 = 0; c0 < N; c0 += p.C) {
@@ -555,10 +568,9 @@ int fldce_shard_partials(const void* h, const void* W_local, const int64_t* targ
                                        V, H, logit_scale, zb, p.Vp, 0);
       dim3 g2((unsigned)cdiv(Cc, 64), (unsigned)p.nT);
       k_row_partials_f32<<<g2, 64, 0, st>>>(zb, p.Vp, Cc, V, part, p.C);
-      k_combine_rows<<<grid1(Cc, 32), 256, 0, st>>>(part, p.C, p.nT, Cc, 1, nullptr, nullptr, 0,
-                                                    nullptr, nullptr, 0.f, 1.f, 1.f, nullptr,
-                                                    nullptr, nullptr, nullptr, row_max + c0,
-                                                    row_sumexp + c0);
+      k_combine_rows<<<grid1(Cc, 32), 256, 0, st>>>(
+          part, nullptr, p.C, p.nT, Cc, 1, nullptr, nullptr, 0, nullptr, nullptr, 0.f, 1.f, 1.f,
+          nullptr, nullptr, nullptr, nullptr, row_max + c0, row_sumexp + c0, nullptr);
     }
     if (row_sumlogit) launch_colsum<float>((const float*)W_local, V, H, colpart, wsum, st);
     k_rowdot<float><<<grid1(N, 4), 256, 0, st>>>((const float*)h, (const float*)W_local, H, target,
@@ -602,8 +614,8 @@ int fldce_shard_bwd(const void* h, const void* W_local, const int64_t* target, c
     k_divisor<<<1, 1024, 0, st>>>(target, N, ignore_index, reduction, total, D);
   }
   Core c{h, W_local, target, p_mask, N, H, V_local, vocab_start, V_global, dtype, ignore_index,
-         label_smoothing, logit_scale, lse, nullptr, nullptr, nullptr, nullptr, D, dH_partial,
-         true, dW_local};
+         label_smoothing, logit_scale, lse, nullptr, nullptr, nullptr, nullptr, nullptr, D,
+         dH_partial, true, dW_local};
   return run_core(c, p, ws, st);
 }
 

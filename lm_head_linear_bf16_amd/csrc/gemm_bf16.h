@@ -272,13 +272,15 @@ __device__ __forceinline__ int acc_col(int wn, int j, int lane) { return wn * kT
 //
 // For each token and each 128-wide vocabulary slab (one wave's M range) it
 // writes part[slab * ldp + token] = (max_j z, sum_j exp(z - max)) with
-// z = s * a (kPart); with kStoreZ it stores z (bf16) into zbuf in the
-// blocked layout below (ldz = padded vocabulary, a multiple of 64).
+// z = s * a, and rpart[slab * ldp + token] = sum_j z when rpart != nullptr
+// (kPart); with kStoreZ it stores z (bf16) into zbuf in the blocked layout
+// below (ldz = padded vocabulary, a multiple of 64).
 // ---------------------------------------------------------------------------
 template <bool kStoreZ, bool kPart>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_logits_bf16(
     const bf16* __restrict__ W, const bf16* __restrict__ h, int V, int C, int H, float s,
-    floatx2* __restrict__ part, int64_t ldp, bf16* __restrict__ zbuf, int64_t ldz, int group_m) {
+    floatx2* __restrict__ part, float* __restrict__ rpart, int64_t ldp, bf16* __restrict__ zbuf,
+    int64_t ldz, int group_m) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int tiles_m = (int)cdiv(V, kBM), tiles_n = (int)cdiv(C, kBN);
   const TileCoord tc = tile_coord(tiles_m, tiles_n, group_m);
@@ -315,6 +317,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_logits_bf16(
       sum += __shfl_xor(sum, 16, 64);
       sum += __shfl_xor(sum, 32, 64);
       if (lane < 16 && tok < C) part[(int64_t)(vbase / 128) * ldp + tok] = floatx2{mx * s, sum};
+      if (rpart != nullptr) {  // row sum of the logits (label-smoothing term)
+        float rs = 0.f;
+#pragma unroll
+        for (int i = 0; i < kTM; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (full || m0 + acc_row(wm, i, lane, r) < V) rs += acc[i][j][r];
+        rs += __shfl_xor(rs, 16, 64);
+        rs += __shfl_xor(rs, 32, 64);
+        if (lane < 16 && tok < C) rpart[(int64_t)(vbase / 128) * ldp + tok] = rs * s;
+      }
     }
     if (kStoreZ && tok < C) {
       // blocked layout: zblk(tok, v) = ((tok / 16) * (ldz / 4) + v / 4) * 64 + (tok % 16) * 4 + v % 4,

@@ -72,6 +72,23 @@ __global__ __launch_bounds__(256) void k_colsum_slabs(const T* __restrict__ src,
   colpart[(int64_t)blockIdx.x * Cn + c] = s;
 }
 
+// bf16 variant with 16-byte loads: each thread sums 8 adjacent columns
+// (Cn % 8 == 0); a wave reads 1 KB of a row per step.
+__global__ __launch_bounds__(256) void k_colsum_slabs_bf16(const bf16* __restrict__ src, int64_t R,
+                                                           int64_t Cn, float* __restrict__ colpart) {
+  const int64_t c = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 8;
+  if (c >= Cn) return;
+  const int64_t r0 = (int64_t)blockIdx.x * kColSlab, r1 = min(R, r0 + kColSlab);
+  float s[8] = {};
+  for (int64_t r = r0; r < r1; ++r) {
+    const bf16x8 v = *(const bf16x8*)(src + r * Cn + c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e] += (float)v[e];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) colpart[(int64_t)blockIdx.x * Cn + c + e] = s[e];
+}
+
 // bf16 transpose with 16-byte accesses: 64 x 64 tile, each thread moves
 // 8 consecutive elements in and 8 out.  Same contract as k_transpose.
 __global__ __launch_bounds__(256) void k_transpose_bf16(const bf16* __restrict__ src, int64_t R,
@@ -184,37 +201,47 @@ __global__ __launch_bounds__(64) void k_row_partials_f32(const float* __restrict
 // host-side logsumexp over the per-block results of logsumexp_fwd_kernel).
 // 256 threads = 32 rows x 8 slab groups.
 //
+// R_i (the row sum of the logits) is R[i] when R != nullptr, else the sum of
+// rpart over the slabs when rpart != nullptr (fixed order), else 0.
 // mode 0 (loss):  lse_i = M + log S, and with p_i, D, eps:
 //     l_i   = [(1-eps)(lse_i - zt_i) + eps(lse_i - R_i / Vg)] / p_i   (0 if ignored)
 //     coef_i = s / (p_i D)                                            (0 if ignored)
 //   (page 1, cross_entropy_kernel steps 4 and the label-smoothing combine;
 //    the whole smoothed CE is divided by p_i).  Writes lse[i], rloss[i],
 //   coef[i] (chunk-local).
-// mode 1 (shard): writes out_m[i] = M, out_s[i] = S (sum relative to M).
+// mode 1 (shard): writes out_m[i] = M, out_s[i] = S (sum relative to M) and,
+// when out_r != nullptr, out_r[i] = R_i.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_combine_rows(
-    const floatx2* __restrict__ part, int64_t ldp, int64_t nT, int64_t C, int mode,
-    const int64_t* __restrict__ target, const float* __restrict__ p_mask, int64_t ignore,
-    const float* __restrict__ zt, const float* __restrict__ R, float eps, float Vg, float s,
-    const float* __restrict__ D, float* __restrict__ lse_out, float* __restrict__ rloss_out,
-    float* __restrict__ coef_out, float* __restrict__ out_m, float* __restrict__ out_s) {
-  __shared__ float sm[8][32], ss[8][32];
+    const floatx2* __restrict__ part, const float* __restrict__ rpart, int64_t ldp, int64_t nT,
+    int64_t C, int mode, const int64_t* __restrict__ target, const float* __restrict__ p_mask,
+    int64_t ignore, const float* __restrict__ zt, const float* __restrict__ R, float eps, float Vg,
+    float s, const float* __restrict__ D, float* __restrict__ lse_out,
+    float* __restrict__ rloss_out, float* __restrict__ coef_out, float* __restrict__ out_m,
+    float* __restrict__ out_s, float* __restrict__ out_r) {
+  __shared__ float sm[8][32], ss[8][32], sr[8][32];
   const int tx = threadIdx.x & 31, grp = threadIdx.x >> 5;
   const int64_t i = (int64_t)blockIdx.x * 32 + tx;
-  float m = -INFINITY, sum = 0.f;
+  float m = -INFINITY, sum = 0.f, rsum = 0.f;
   if (i < C)
     for (int64_t t = grp; t < nT; t += 8) {
       const floatx2 p = part[t * ldp + i];
       lse_merge(m, sum, p[0], p[1]);
+      if (rpart != nullptr) rsum += rpart[t * ldp + i];
     }
   sm[grp][tx] = m;
   ss[grp][tx] = sum;
+  sr[grp][tx] = rsum;
   __syncthreads();
   if (grp != 0 || i >= C) return;
-  for (int g = 1; g < 8; ++g) lse_merge(m, sum, sm[g][tx], ss[g][tx]);
+  for (int g = 1; g < 8; ++g) {
+    lse_merge(m, sum, sm[g][tx], ss[g][tx]);
+    rsum += sr[g][tx];
+  }
   if (mode == 1) {
     out_m[i] = m;
     out_s[i] = sum;
+    if (out_r != nullptr) out_r[i] = rsum;
     return;
   }
   const float lse = m + logf(sum);
@@ -222,7 +249,7 @@ __global__ __launch_bounds__(256) void k_combine_rows(
   const float p = (p_mask != nullptr && valid) ? p_mask[i] : 1.f;
   float l = 0.f, cf = 0.f;
   if (valid) {
-    const float rs = (R != nullptr) ? R[i] : 0.f;
+    const float rs = (R != nullptr) ? R[i] : rsum;
     l = ((1.f - eps) * (lse - zt[i]) + eps * (lse - rs / Vg)) / p;
     cf = s / (p * D[0]);
   }
@@ -332,64 +359,77 @@ __global__ __launch_bounds__(256) void k_gpass(T* __restrict__ z, int64_t ldz, i
 // blocked layout the logits GEMM writes: element (token t, column v) at
 // ((t / 16) * (ldz / 4) + v / 4) * 64 + (t % 16) * 4 + v % 4, and writing g
 // row-major [rows, ldz] for both backward GEMMs.  Rows C .. (grid rows) - 1
-// and columns >= V are written as zeros.  One block = 64 tokens x 64
-// columns; every global access is 16 bytes.
+// and columns >= V are written as zeros.
+//
+// One block = 64 tokens x 256 columns, 256 threads.  Thread -> two fixed
+// tokens (their lse, coefficient and target stay in registers) and eight
+// 16-byte units of z (a wave reads 1 KB contiguous per step); g goes out
+// through LDS as 512-byte row segments.
 // ---------------------------------------------------------------------------
+constexpr int kGpassCols = 256;
 __global__ __launch_bounds__(256) void k_gpass_blk(const bf16* __restrict__ zblk, int64_t ldz,
                                                    int64_t C, int64_t V,
                                                    const float* __restrict__ lse,
                                                    const float* __restrict__ coef,
                                                    const int64_t* __restrict__ target, int64_t v0,
                                                    float eps, float Vg, bf16* __restrict__ g) {
-  __shared__ bf16 tile[64][64 + 8];  // [token][column]
+  __shared__ bf16 tile[64][kGpassCols + 8];  // [token][column]
   const int tid = threadIdx.x;
-  const int64_t i0 = (int64_t)blockIdx.y * 64, j0 = (int64_t)blockIdx.x * 64;
+  const int64_t i0 = (int64_t)blockIdx.y * 64, j0 = (int64_t)blockIdx.x * kGpassCols;
+  const int64_t nvb = min((int64_t)kGpassCols / 4, (ldz - j0) / 4);  // column blocks in range
   const float epsV = eps / Vg;
+  const int tb = tid >> 6, vbo = (tid >> 3) & 7, w = tid & 7;
+  const int tl0 = tb * 16 + w * 2;  // tokens tl0, tl0 + 1 of the tile
+  float cf[2], l2[2], tg[2];
+  int64_t yc[2];
+  bool any = false;
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int idx = tid + 256 * p;
-    const int tb = idx >> 7;           // token block (16 tokens) within the tile
-    const int u = idx & 127;           // 16-byte unit within the block's 2 KB run
-    const int vb = u >> 3, w = u & 7;  // column block (4 columns), unit within the 128 B chunk
-    const int tl0 = tb * 16 + w * 2;   // this unit holds tokens tl0, tl0 + 1 x 4 columns
-    bf16x4 out[2];
+  for (int q = 0; q < 2; ++q) {
+    const int64_t i = i0 + tl0 + q;
+    cf[q] = (i < C) ? coef[i] : 0.f;
+    l2[q] = (cf[q] != 0.f) ? lse[i] * kLog2e : 0.f;
+    yc[q] = (cf[q] != 0.f) ? target[i] - v0 - j0 : -1;  // column within this tile
+    tg[q] = cf[q] * (1.f - eps);
+    any |= cf[q] != 0.f;
+  }
+  const bf16* zsrc = zblk + ((i0 / 16 + tb) * (ldz >> 2) + j0 / 4) * 64 + w * 8;
+  constexpr int kSteps = kGpassCols / 32;
+  bf16x8 zin[kSteps];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) out[q] = bf16x4{};
-    float cf[2], l2[2], tg[2];
-    int64_t yc[2];
-    bool any = false;
+  for (int p = 0; p < kSteps; ++p) {  // all loads in flight before any math
+    const int vb = vbo + 8 * p;
+    zin[p] = (any && vb < nvb) ? *(const bf16x8*)(zsrc + (int64_t)vb * 64) : bf16x8{};
+  }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int64_t i = i0 + tl0 + q;
-      cf[q] = (i < C) ? coef[i] : 0.f;
-      l2[q] = (cf[q] != 0.f) ? lse[i] * kLog2e : 0.f;
-      yc[q] = (cf[q] != 0.f) ? target[i] - v0 : -1;
-      tg[q] = cf[q] * (1.f - eps);
-      any |= cf[q] != 0.f;
-    }
+  for (int p = 0; p < kSteps; ++p) {
+    const int vb = vbo + 8 * p;  // column block (4 columns) within the tile
+    bf16x4 out[2] = {bf16x4{}, bf16x4{}};
     if (any) {
-      const bf16x8 zv = *(const bf16x8*)(zblk + ((i0 / 16 + tb) * (ldz >> 2) + j0 / 4 + vb) * 64 + w * 8);
+      const bf16x8 zv = zin[p];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int q = e >> 2;
-        const int64_t j = j0 + vb * 4 + (e & 3);
+        const int jl = vb * 4 + (e & 3);
         float v = 0.f;
-        if (cf[q] != 0.f && j < V) {
+        if (cf[q] != 0.f && j0 + jl < V) {
           v = cf[q] * (fast_exp2(__builtin_fmaf((float)zv[e], kLog2e, -l2[q])) - epsV);
-          if (j == yc[q]) v -= tg[q];
+          if (jl == yc[q]) v -= tg[q];
         }
         out[q][e & 3] = (bf16)v;
       }
     }
+    if (vb < nvb) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) *(bf16x4*)&tile[tl0 + q][vb * 4] = out[q];
+      for (int q = 0; q < 2; ++q) *(bf16x4*)&tile[tl0 + q][vb * 4] = out[q];
+    }
   }
   __syncthreads();
+  const int units = (int)nvb / 2;  // 16-byte units per token row in range
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
+  for (int p = 0; p < 8; ++p) {
     const int unit = tid + 256 * p;
-    const int r = unit >> 3, c = unit & 7;
-    *(bf16x8*)(g + (i0 + r) * ldz + j0 + c * 8) = *(const bf16x8*)&tile[r][c * 8];
+    const int r = unit >> 5, c = unit & 31;
+    if (c < units) *(bf16x8*)(g + (i0 + r) * ldz + j0 + c * 8) = *(const bf16x8*)&tile[r][c * 8];
   }
 }
 
