@@ -65,6 +65,70 @@ def traffic_entry(kernel: str, workload: str):
     return e.get("bytes_per_launch")
 
 
+def _counter_per_kernel(path: str, counter: str) -> dict:
+    """{kernel short name: [value per dispatch (KiB)]} from a rocprofv3 counter CSV."""
+    import csv
+    out: dict = {}
+    per_dispatch: dict = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Dispatch_Id"], r["Kernel_Name"])
+            per_dispatch[key] = per_dispatch.get(key, 0.0) + float(r["Counter_Value"])
+    for (_, name), v in sorted(per_dispatch.items(), key=lambda kv: int(kv[0][0])):
+        out.setdefault(name, []).append(v)
+    return out
+
+
+STAGE_KERNELS = {"logits_gemm": "k_logits_bf16", "dH_gemm": "k_gemm_dh_bf16",
+                 "dW_gemm": "k_gemm_dw_bf16", "dlogits": "k_gpass_blk"}
+
+
+def traffic_summary(fetch_csv: str, write_csv: str, workload: str, calib_mib: int) -> int:
+    """FETCH_SIZE / WRITE_SIZE per launch of each stage kernel, scaled by the
+    ratio of the calibration copy's known bytes to what the same counter read
+    for it; writes profiles/traffic.json and profiles/<workload>_traffic.md."""
+    fetch = _counter_per_kernel(fetch_csv, "FETCH_SIZE")
+    write = _counter_per_kernel(write_csv, "WRITE_SIZE")
+    calib = [k for k in fetch if "copy" in k.lower() or "elementwise" in k.lower()]
+    if not calib:
+        print("no calibration copy kernel found in the counter file", file=sys.stderr)
+        return 1
+    known_kib = calib_mib * 1024.0
+    cf = known_kib / max(fetch[calib[0]])
+    cw = known_kib / max(write[calib[0]])
+    out = {}
+    lines = [f"# HBM traffic per launch, {workload} workload",
+             "",
+             "FETCH_SIZE and WRITE_SIZE (KiB per dispatch) from two rocprofv3 --pmc runs of",
+             f"`bench.py --workload {workload} --steps 2 --warmup 1 --no-cpu-baseline --calib-copy-mib {calib_mib}`,",
+             f"scaled by the calibration copy of {calib_mib} MiB (read scale {cf:.4f}, write scale {cw:.4f}).",
+             "",
+             "| stage | kernel | fetch GB/launch | write GB/launch | launches |",
+             "|---|---|---|---|---|"]
+    for stage, kname in STAGE_KERNELS.items():
+        fk = [k for k in fetch if kname in k]
+        wk = [k for k in write if kname in k]
+        if not fk or not wk:
+            continue
+        fv = [v for k in fk for v in fetch[k]]
+        wv = [v for k in wk for v in write[k]]
+        fb = sum(fv) / len(fv) * 1024 * cf
+        wb = sum(wv) / len(wv) * 1024 * cw
+        out[stage] = {"workload": workload, "src_hash": src_hash(), "fetch_bytes": fb,
+                      "write_bytes": wb, "bytes_per_launch": fb + wb, "launches": len(fv),
+                      "read_scale": cf, "write_scale": cw}
+        lines.append(f"| {stage} | {kname} | {fb / 1e9:.3f} | {wb / 1e9:.3f} | {len(fv)} |")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    with open(os.path.join(ROOT, "profiles", f"{workload}_traffic.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    return 0
+
+
 def cpu_baseline(w, rows: int) -> dict:
     """The float64 oracle on the first `rows` token rows of the same workload."""
     import numpy as np
@@ -103,7 +167,16 @@ def main() -> int:
     ap.add_argument("--cpu-rows", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", default="", help="comma-separated chunk sizes to time as well")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one device copy of this many MiB first (counter calibration)")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a "
+                         "run with --calib-copy-mib into profiles/traffic.json and exit")
+    ap.add_argument("--calib-mib", type=int, default=1024, help="size of that calibration copy")
     args = ap.parse_args()
+    if args.traffic_summary:
+        return traffic_summary(args.traffic_summary[0], args.traffic_summary[1], args.workload,
+                               args.calib_mib)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -127,6 +200,12 @@ def main() -> int:
             return torch.from_numpy(t.bits.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(t.values).to(dev)
 
+    if args.calib_copy_mib:
+        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     h, W = dev_t(hT), dev_t(WT)
     del hT, WT
     tgt = torch.from_numpy(target).to(dev)
