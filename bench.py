@@ -11,8 +11,10 @@ Default workload: the headline masked-diffusion LM head, B=8 x L=1024
 0.5, per-sequence masking probability, mean over N ("sum/N").  Synthetic,
 seeded inputs (lm_head_linear_bf16_amd.synth).
 
-Prints ONE JSON line: tokens/s (value), TFLOP/s at 6*N*H*V, the fraction of
-the bf16 MFMA peak, the roofline entry of the dominant kernel (timed live with
+Prints ONE JSON line: tokens/s (value; all N tokens), executed TFLOP/s
+(6 * rows multiplied * H * V: the bf16 path multiplies only rows whose target
+is not ignore_index, the rest are exactly zero) and its fraction of the bf16
+MFMA peak, the dense-equivalent 6*N*H*V rate, the roofline entry of the dominant kernel (timed live with
 HIP events recorded on the library's stream inside the timed steps), and the
 float64 CPU oracle timed on a bounded row sample on this host.
 
@@ -240,17 +242,22 @@ def main() -> int:
         del ws
         return (t1 - t0) * 1e3 / steps, stages, loss
 
+    n_valid = int(np.count_nonzero(target != synth.IGNORE_INDEX))
     C = args.chunk_rows or fldce.fldce_default_chunk_rows(N, H, V)
     log(f"timing {args.steps} steps after {args.warmup} warmup (chunk_rows={C})")
     ms, stages, loss = run_config(args.chunk_rows, args.steps, args.warmup)
-    flops = 6.0 * N * H * V
+    # bf16 multiplies only rows whose target != ignore_index (the others are
+    # exactly zero); fp32 multiplies every row
+    rows_mult = n_valid if w.dtype == "bf16" else N
+    flops = 6.0 * rows_mult * H * V          # executed
+    flops_nominal = 6.0 * N * H * V          # a dense pass over every row
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
-    # dominant kernel: the GEMM stage with the largest time; each launch does
-    # 2 * C * H * V flops (C rows of the chunk), i.e. 2 N H V per step
+    # dominant kernel: the GEMM stage with the largest time; per step it does
+    # 2 * rows * H * V flops over all its launches (one per chunk)
     dom = max((k for k in stages if k in STAGE_FLOP_KERNELS), key=lambda k: stages[k]["total_ms"])
     d = stages[dom]
-    per_launch_flops = 2.0 * N * H * V * args.steps / d["launches"]
+    per_launch_flops = 2.0 * rows_mult * H * V * args.steps / d["launches"]
     avg_ms = d["total_ms"] / d["launches"]
     achieved = per_launch_flops / (avg_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
@@ -278,6 +285,8 @@ def main() -> int:
                    "chunk_rows": int(C)},
         "tflops": round(tflops, 2),
         "pct_peak": round(100.0 * tflops / peak, 2),
+        "rows_multiplied": rows_mult,
+        "tflops_nominal_6NHV": round(flops_nominal / (ms * 1e-3) / 1e12, 2),
         "loss": loss,
         "stage_ms_per_step": stage_ms,
         "roofline": roofline,
@@ -287,7 +296,8 @@ def main() -> int:
         for c in [int(x) for x in args.sweep.split(",") if x]:
             log(f"sweep chunk_rows={c}")
             m, _, _ = run_config(c, max(3, args.steps // 4), 1)
-            sw[str(c)] = {"ms_per_step": round(m, 3), "tflops": round(flops / (m * 1e-3) / 1e12, 1)}
+            sw[str(c)] = {"ms_per_step": round(m, 3), "tflops": round(flops / (m * 1e-3) / 1e12, 1),
+                          "tokens_per_s": round(N / (m * 1e-3), 1)}
         result["chunk_sweep"] = sw
     if not args.no_cpu_baseline:
         del h, W

@@ -42,7 +42,7 @@ struct Plan {
   int splits = 1;
   size_t oD = 0, oWT = 0, oColpart = 0, oWsum = 0, oZt = 0, oR = 0, oLse = 0, oRloss = 0,
          oCoef = 0, oPart = 0, oRpart = 0, oZ = 0, oG = 0, oGT = 0, oHT = 0, oDHpart = 0,
-         oDW32 = 0;
+         oDW32 = 0, oRows = 0, oCount = 0, oLsec = 0, oTcol = 0;
   size_t total = 0;
 };
 
@@ -94,6 +94,8 @@ Plan make_plan(int mode, int64_t N, int64_t H, int64_t V, int dtype, int64_t chu
   p.nchunks = N > 0 ? cdiv(N, p.C) : 0;
   size_t cur = 0;
   p.oD = take(cur, 256);
+  p.oCount = take(cur, 256);
+  p.oRows = take(cur, (size_t)std::max<int64_t>(N, 1) * 4);  // compacted row indices
   p.oColpart = take(cur, (size_t)cdiv(V, kColSlab) * H * 4);
   p.oWsum = take(cur, (size_t)H * 4);
   p.oPart = take(cur, (size_t)p.nT * p.C * 8);
@@ -109,6 +111,8 @@ Plan make_plan(int mode, int64_t N, int64_t H, int64_t V, int dtype, int64_t chu
   p.oLse = take(cur, (size_t)N * 4);
   p.oRloss = take(cur, (size_t)N * 4);
   p.oCoef = take(cur, (size_t)p.C * 4);
+  p.oLsec = take(cur, (size_t)p.C * 4);
+  p.oTcol = take(cur, (size_t)p.C * 4);
   p.oZ = take(cur, (size_t)p.Cp * p.Vp * p.esz);
   if (bf) {
     p.oG = take(cur, (size_t)p.Cp * p.Vp * p.esz);  // g row-major (z is blocked)
@@ -252,82 +256,102 @@ struct Core {
   const float* R;        // fwd_bwd fp32: row sums of z [N] or nullptr
   float* rpart;          // fwd_bwd bf16: per-slab row sums from the logits epilogue, or nullptr
   const float* D;
+  const int* rows;       // bf16: compacted row indices (target != ignore), device
+  const int* count;      // bf16: their number, device
   void* dH;              // [N, H]: h dtype (fwd_bwd) or fp32 (shard)
   bool dH_f32;
   void* dW;              // [V, H] W dtype
 };
 
 // per-row stage of a chunk: lse/loss/coefficients (fwd_bwd) or coefficients
-// only (shard backward, lse given).  Returns the chunk's lse pointer.
-const float* run_rows(const Core& c, const Plan& p, const floatx2* part, float* coef, int64_t c0,
-                      int64_t Cc, hipStream_t st) {
+// only (shard backward, lse given).  Chunk-local lse / target columns go to
+// lsec / tcol (bf16 path).  Returns the lse pointer the fp32 dlogits reads.
+const float* run_rows(const Core& c, const Plan& p, const floatx2* part, float* coef, float* lsec,
+                      int* tcol, int64_t c0, int64_t cmax, hipStream_t st) {
   StageTimer tm(kCombine, st);
   if (c.lse_in == nullptr) {
-    k_combine_rows<<<grid1(Cc, 32), 256, 0, st>>>(
-        part, c.rpart, p.C, p.nT, Cc, 0, c.target + c0, c.p_mask ? c.p_mask + c0 : nullptr,
-        c.ignore, c.zt + c0, c.R ? c.R + c0 : nullptr, c.eps, (float)c.Vg, c.s, c.D,
-        c.lse_out + c0, c.rloss_out + c0, coef, nullptr, nullptr, nullptr);
+    k_combine_rows<<<grid1(cmax, 32), 256, 0, st>>>(
+        part, c.rpart, p.C, p.nT, cmax, c.rows, c.count, c0, 0, c.target, c.p_mask, c.ignore,
+        c.zt, c.R, c.eps, (float)c.Vg, c.s, c.D, c.lse_out, c.rloss_out, coef, lsec, tcol, c.v0,
+        nullptr, nullptr, nullptr);
     return c.lse_out + c0;
   }
-  k_coef_rows<<<grid1(Cc, 256), 256, 0, st>>>(c.target + c0, c.p_mask ? c.p_mask + c0 : nullptr,
-                                               c.ignore, Cc, c.s, c.D, coef);
+  k_coef_rows<<<grid1(cmax, 256), 256, 0, st>>>(c.target, c.p_mask, c.ignore, cmax, c.rows,
+                                                 c.count, c0, c.s, c.D, coef, c.lse_in, lsec, tcol,
+                                                 c.v0);
   return c.lse_in + c0;
 }
 
-// bf16: W and g are read in place; only the chunk's h is transposed.
+// bf16: only rows with target != ignore_index are multiplied (compacted on
+// the device; kernels read the count, so there is no host synchronisation);
+// W and g are read in place, only the chunk's h is copied transposed.
 int run_core_bf16(const Core& c, const Plan& p, char* ws, hipStream_t st) {
   bf16* zb = reinterpret_cast<bf16*>(ws + p.oZ);
   bf16* gb = reinterpret_cast<bf16*>(ws + p.oG);
   bf16* hT = reinterpret_cast<bf16*>(ws + p.oHT);
   float* coef = reinterpret_cast<float*>(ws + p.oCoef);
+  float* lsec = reinterpret_cast<float*>(ws + p.oLsec);
+  int* tcol = reinterpret_cast<int*>(ws + p.oTcol);
   floatx2* part = reinterpret_cast<floatx2*>(ws + p.oPart);
   float* dHpart = reinterpret_cast<float*>(ws + p.oDHpart);
   float* dW32 = reinterpret_cast<float*>(ws + p.oDW32);
   const bf16* h = static_cast<const bf16*>(c.h);
   const bf16* W = static_cast<const bf16*>(c.W);
   const int64_t H = c.H, V = c.V, Vp = p.Vp;
+  {
+    StageTimer tm(kPrep, st);
+    if (c.dH_f32)
+      k_zero_ignored_rows<float><<<(unsigned)c.N, 256, 0, st>>>(c.target, c.N, c.ignore,
+                                                               (float*)c.dH, H);
+    else
+      k_zero_ignored_rows<bf16><<<(unsigned)c.N, 256, 0, st>>>(c.target, c.N, c.ignore,
+                                                              (bf16*)c.dH, H);
+  }
   for (int64_t ic = 0; ic < p.nchunks; ++ic) {
     const int64_t c0 = ic * p.C;
-    const int64_t Cc = std::min(p.C, c.N - c0);
-    const int64_t Cpc = round_up(Cc, 64);
-    const bf16* hc = h + c0 * H;
+    const int64_t cmax = std::min(p.C, c.N - c0);  // rows of the chunk if none were ignored
+    const int64_t Cpc = round_up(cmax, 64);
     {
       StageTimer tm(kHT, st);
-      launch_transpose<bf16>(hc, Cc, H, H, hT, p.Cp, Cpc, st);
+      dim3 g((unsigned)(Cpc / 64), (unsigned)cdiv(H, 64));
+      k_transpose_gather_bf16<<<g, 256, 0, st>>>(h, c.rows, c.count, c0, cmax, H, hT, p.Cp, Cpc);
     }
     {  // 1. logits (+ softmax partials)
       StageTimer tm(kLogits, st);
-      const int blocks = (int)(cdiv(V, kBM) * cdiv(Cc, kBN));
+      const int blocks = (int)(cdiv(V, kBM) * cdiv(cmax, kBN));
       if (c.lse_in == nullptr)
         k_logits_bf16<true, true><<<blocks, kGemmThreads, kGemmLds, st>>>(
-            W, hc, (int)V, (int)Cc, (int)H, c.s, part, c.rpart, p.C, zb, Vp, kGroupM);
+            W, h, (int)V, (int)cmax, (int)H, c.s, c.rows, c.count, c0, part, c.rpart, p.C, zb, Vp,
+            kGroupM);
       else
         k_logits_bf16<true, false><<<blocks, kGemmThreads, kGemmLds, st>>>(
-            W, hc, (int)V, (int)Cc, (int)H, c.s, part, nullptr, p.C, zb, Vp, kGroupM);
+            W, h, (int)V, (int)cmax, (int)H, c.s, c.rows, c.count, c0, part, nullptr, p.C, zb, Vp,
+            kGroupM);
     }
     // 2. per-row combine
-    const float* lse_c = run_rows(c, p, part, coef, c0, Cc, st);
-    {  // 3. dlogits: blocked z -> row-major g, zero rows Cc .. Cpc-1
+    run_rows(c, p, part, coef, lsec, tcol, c0, cmax, st);
+    {  // 3. dlogits: blocked z -> row-major g, zero rows up to the padded count
       StageTimer tm(kDlogits, st);
       dim3 g((unsigned)cdiv(Vp, kGpassCols), (unsigned)(Cpc / 64));
-      k_gpass_blk<<<g, 256, 0, st>>>(zb, Vp, Cc, V, lse_c, coef, c.target + c0, c.v0, c.eps,
+      k_gpass_blk<<<g, 256, 0, st>>>(zb, Vp, cmax, c.count, c0, V, lsec, coef, tcol, c.eps,
                                      (float)c.Vg, gb);
     }
-    {  // 4. dH = g W (split over the vocabulary, ordered reduction)
+    {  // 4. dH = g W (split over the vocabulary, ordered reduction, scattered rows)
       const int S = p.splits;
-      const int blocks = (int)(cdiv(Cc, kBM) * cdiv(H, kBN) * S);
+      const int blocks = (int)(cdiv(cmax, kBM) * cdiv(H, kBN) * S);
       {
         StageTimer tm(kDHGemm, st);
-        k_gemm_dh_bf16<<<blocks, kGemmThreads, kGemmLds, st>>>(gb, Vp, (int)Cc, W, (int)V, (int)H,
-                                                               (int)(Vp / kBK), S, dHpart, kGroupM);
+        k_gemm_dh_bf16<<<blocks, kGemmThreads, kGemmLds, st>>>(gb, Vp, (int)cmax, c.count, c0, W,
+                                                               (int)V, (int)H, (int)(Vp / kBK), S,
+                                                               dHpart, kGroupM);
       }
       StageTimer tm(kDHReduce, st);
       if (c.dH_f32)
-        k_splitk_reduce<float><<<grid1(Cc * H, 1024), 256, 0, st>>>(dHpart, S, Cc * H,
-                                                                    (float*)c.dH + c0 * H);
+        k_splitk_scatter<float><<<(unsigned)cmax, 256, 0, st>>>(dHpart, S, cmax, H, c.rows,
+                                                                c.count, c0, (float*)c.dH);
       else
-        k_splitk_reduce<bf16><<<grid1(Cc * H, 1024), 256, 0, st>>>(dHpart, S, Cc * H,
-                                                                   (bf16*)c.dH + c0 * H);
+        k_splitk_scatter<bf16><<<(unsigned)cmax, 256, 0, st>>>(dHpart, S, cmax, H, c.rows,
+                                                               c.count, c0, (bf16*)c.dH);
     }
     {  // 5. dW += g^T h
       StageTimer tm(kDWGemm, st);
@@ -336,8 +360,8 @@ int run_core_bf16(const Core& c, const Plan& p, char* ws, hipStream_t st) {
       const int blocks = (int)(cdiv(V, kBM) * cdiv(H, kBN));
       auto kern = mode == 0 ? k_gemm_dw_bf16<0>
                             : (mode == 1 ? k_gemm_dw_bf16<1> : (mode == 2 ? k_gemm_dw_bf16<2> : k_gemm_dw_bf16<3>));
-      kern<<<blocks, kGemmThreads, kGemmLds, st>>>(gb, Vp, (int)Cpc, (int)V, hT, p.Cp, (int)H,
-                                                   (bf16*)c.dW, dW32, kGroupM);
+      kern<<<blocks, kGemmThreads, kGemmLds, st>>>(gb, Vp, (int)cmax, c.count, c0, (int)V, hT,
+                                                   p.Cp, (int)H, (bf16*)c.dW, dW32, kGroupM);
     }
   }
   return launch_status();
@@ -376,7 +400,7 @@ int run_core_f32(const Core& c, const Plan& p, char* ws, hipStream_t st) {
         k_row_partials_f32<<<g2, 64, 0, st>>>(zb, Vp, Cc, V, part, p.C);
       }
     }
-    const float* lse_c = run_rows(c, p, part, coef, c0, Cc, st);
+    const float* lse_c = run_rows(c, p, part, coef, nullptr, nullptr, c0, Cc, st);
     {
       StageTimer tm(kDlogits, st);
       dim3 g((unsigned)(Vp / 64), (unsigned)(Cpc / 64));
@@ -491,13 +515,18 @@ int fldce_fwd_bwd(const void* h, const void* W, const int64_t* target, const flo
   const bool bf = dtype == FLDCE_DTYPE_BF16;
   float* rpart = reinterpret_cast<float*>(ws + p.oRpart);
   // row sums of z: bf16 from the logits epilogue, fp32 from <h_i, sum_j W_j>
+  int* rows = reinterpret_cast<int*>(ws + p.oRows);
+  int* count = reinterpret_cast<int*>(ws + p.oCount);
   Core c{h, W, target, p_mask, N, H, V, 0, V, dtype, ignore_index, label_smoothing, logit_scale,
          nullptr, lse, rl, zt, (smooth && !bf) ? R : nullptr, (smooth && bf) ? rpart : nullptr, D,
-         dH, false, dW};
+         bf ? rows : nullptr, bf ? count : nullptr, dH, false, dW};
   {
     StageTimer tm(kPrep, st);
     k_divisor<<<1, 1024, 0, st>>>(target, N, ignore_index, reduction, total, D);
     if (bf) {
+      k_compact_rows<<<1, 1024, 0, st>>>(target, N, ignore_index, rows, count);
+      k_ignored_rows_init<<<grid1(N, 256), 256, 0, st>>>(target, N, ignore_index, lse, 0.f, rl, 0.f,
+                                                         nullptr, 0.f);
       k_rowdot<bf16><<<grid1(N, 4), 256, 0, st>>>((const bf16*)h, (const bf16*)W, H, target, 0,
                                                    V, ignore_index, logit_scale, nullptr, N, zt,
                                                    nullptr);
@@ -540,20 +569,30 @@ int fldce_shard_partials(const void* h, const void* W_local, const int64_t* targ
   float* colpart = reinterpret_cast<float*>(ws + p.oColpart);
   float* wsum = reinterpret_cast<float*>(ws + p.oWsum);
   const int64_t V = V_local;
+  int* rows = reinterpret_cast<int*>(ws + p.oRows);
+  int* count = reinterpret_cast<int*>(ws + p.oCount);
   if (dtype == FLDCE_DTYPE_BF16) {
+    // rows with target == ignore_index are skipped: (-inf, 0, 0, 0)
+    {
+      StageTimer tm(kPrep, st);
+      k_compact_rows<<<1, 1024, 0, st>>>(target, N, ignore_index, rows, count);
+      k_ignored_rows_init<<<grid1(N, 256), 256, 0, st>>>(target, N, ignore_index, row_max,
+                                                         -INFINITY, row_sumexp, 0.f, row_sumlogit,
+                                                         0.f);
+    }
     const int blocks = (int)(cdiv(V, kBM) * cdiv(N, kBN));
     {
       StageTimer tm(kLogits, st);
       k_logits_bf16<false, true><<<blocks, kGemmThreads, kGemmLds, st>>>(
-          (const bf16*)W_local, (const bf16*)h, (int)V, (int)N, (int)H, logit_scale, part,
-          row_sumlogit ? rpart : nullptr, p.C, nullptr, 0, kGroupM);
+          (const bf16*)W_local, (const bf16*)h, (int)V, (int)N, (int)H, logit_scale, rows, count,
+          0, part, row_sumlogit ? rpart : nullptr, p.C, nullptr, 0, kGroupM);
     }
     {
       StageTimer tm(kCombine, st);
       k_combine_rows<<<grid1(N, 32), 256, 0, st>>>(
-          part, row_sumlogit ? rpart : nullptr, p.C, p.nT, N, 1, nullptr, nullptr, 0, nullptr,
-          nullptr, 0.f, 1.f, 1.f, nullptr, nullptr, nullptr, nullptr, row_max, row_sumexp,
-          row_sumlogit);
+          part, row_sumlogit ? rpart : nullptr, p.C, p.nT, N, rows, count, 0, 1, nullptr, nullptr,
+          0, nullptr, nullptr, 0.f, 1.f, 1.f, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+          0, row_max, row_sumexp, row_sumlogit);
     }
     StageTimer tm(kPrep, st);
     k_rowdot<bf16><<<grid1(N, 4), 256, 0, st>>>((const bf16*)h, (const bf16*)W_local, H, target,
@@ -569,14 +608,18 @@ int fldce_shard_partials(const void* h, const void* W_local, const int64_t* targ
       dim3 g2((unsigned)cdiv(Cc, 64), (unsigned)p.nT);
       k_row_partials_f32<<<g2, 64, 0, st>>>(zb, p.Vp, Cc, V, part, p.C);
       k_combine_rows<<<grid1(Cc, 32), 256, 0, st>>>(
-          part, nullptr, p.C, p.nT, Cc, 1, nullptr, nullptr, 0, nullptr, nullptr, 0.f, 1.f, 1.f,
-          nullptr, nullptr, nullptr, nullptr, row_max + c0, row_sumexp + c0, nullptr);
+          part, nullptr, p.C, p.nT, Cc, nullptr, nullptr, c0, 1, nullptr, nullptr, 0, nullptr,
+          nullptr, 0.f, 1.f, 1.f, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, row_max,
+          row_sumexp, nullptr);
     }
     if (row_sumlogit) launch_colsum<float>((const float*)W_local, V, H, colpart, wsum, st);
     k_rowdot<float><<<grid1(N, 4), 256, 0, st>>>((const float*)h, (const float*)W_local, H, target,
                                                   vocab_start, V, ignore_index, logit_scale,
                                                   row_sumlogit ? wsum : nullptr, N, target_logit,
                                                   row_sumlogit);
+    // same convention as the bf16 path for rows whose target is ignore_index
+    k_ignored_rows_init<<<grid1(N, 256), 256, 0, st>>>(target, N, ignore_index, row_max, -INFINITY,
+                                                       row_sumexp, 0.f, row_sumlogit, 0.f);
   }
   return launch_status();
 }
@@ -613,9 +656,16 @@ int fldce_shard_bwd(const void* h, const void* W_local, const int64_t* target, c
     StageTimer tm(kPrep, st);
     k_divisor<<<1, 1024, 0, st>>>(target, N, ignore_index, reduction, total, D);
   }
+  const bool bf = dtype == FLDCE_DTYPE_BF16;
+  int* rows = reinterpret_cast<int*>(ws + p.oRows);
+  int* count = reinterpret_cast<int*>(ws + p.oCount);
+  if (bf) {
+    StageTimer tm(kPrep, st);
+    k_compact_rows<<<1, 1024, 0, st>>>(target, N, ignore_index, rows, count);
+  }
   Core c{h, W_local, target, p_mask, N, H, V_local, vocab_start, V_global, dtype, ignore_index,
          label_smoothing, logit_scale, lse, nullptr, nullptr, nullptr, nullptr, nullptr, D,
-         dH_partial, true, dW_local};
+         bf ? rows : nullptr, bf ? count : nullptr, dH_partial, true, dW_local};
   return run_core(c, p, ws, st);
 }
 

@@ -47,18 +47,26 @@ constexpr int kRoundsA = kBM / (kWaves * 8), kRoundsB = kBN / (kWaves * 8);
 
 struct TileCoord {
   int tm, tn, split;
+  bool active;
 };
 
 // Block id -> (tile row, tile column, split), XCD-aware and grouped.  The
-// grid must be exactly tiles_m * tiles_n * splits blocks.
-__device__ __forceinline__ TileCoord tile_coord(int tiles_m, int tiles_n, int group_m) {
-  const int nblk = gridDim.x;
+// dispatcher deals block ids round-robin over the 8 XCDs, so XCD x runs the
+// blocks bid = x, x + 8, ...; the work items (tiles_m x tiles_n x splits,
+// tiles_m possibly fewer than the grid was sized for, known only on the
+// device) are cut into 8 contiguous ranges, one per XCD, so every XCD gets
+// the same share and neighbouring tiles share its L2.  Within the order,
+// tiles go in groups of `group_m` tile rows.  Blocks without an item are
+// inactive.
+__device__ __forceinline__ TileCoord tile_coord(int tiles_m, int tiles_n, int splits, int group_m) {
   const int bid = blockIdx.x;
-  const int per = nblk / 8, rem = nblk % 8;
   const int x = bid % 8, idx = bid / 8;
-  int b = (x < rem) ? x * (per + 1) + idx : rem * (per + 1) + (x - rem) * per + idx;
   const int tiles = tiles_m * tiles_n;
-  TileCoord c;
+  const int A = tiles * splits;
+  const int per = A / 8, rem = A % 8;
+  TileCoord c{0, 0, 0, idx < per + (x < rem ? 1 : 0)};
+  if (!c.active) return c;
+  int b = x * per + min(x, rem) + idx;
   c.split = b / tiles;
   b -= c.split * tiles;
   const int width = group_m * tiles_n;
@@ -114,14 +122,18 @@ template <>
 struct Tile<false> {
   static constexpr int kReads = 1;  // LDS reads per fragment
   const bf16* p[4];
-  // rows = number of valid rows (M or N); r0 = first row of the tile
+  // rows = number of valid rows (M or N); r0 = first row of the tile.  With
+  // gidx, tile row q is source row gidx[goff + q] (a gather), else goff + q.
   __device__ __forceinline__ void init(const bf16* X, int64_t ldx, int rows, int cols, int r0,
-                                       int64_t k_begin, int lane, int wave) {
+                                       int64_t k_begin, int lane, int wave,
+                                       const int* gidx = nullptr, int64_t goff = 0) {
     (void)cols;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = i * kWaves * 8 + wave * 8 + (lane >> 3);
-      p[i] = X + (int64_t)min(r0 + r, rows - 1) * ldx + lds_chunk(lane & 7, r) * 8 + k_begin;
+      const int64_t q = min(r0 + r, rows - 1);
+      const int64_t src = gidx != nullptr ? (int64_t)gidx[goff + q] : goff + q;
+      p[i] = X + src * ldx + lds_chunk(lane & 7, r) * 8 + k_begin;
     }
   }
   __device__ __forceinline__ void issue(char* tile, int t, int wave) const {
@@ -149,7 +161,8 @@ struct Tile<true> {
   // rows = number of valid K rows of the source; cols = valid columns;
   // r0 = first column of the tile; k_begin = first K row
   __device__ __forceinline__ void init(const bf16* X, int64_t ld, int rows, int cols, int c0,
-                                       int64_t kb, int lane, int wave) {
+                                       int64_t kb, int lane, int wave, const int* = nullptr,
+                                       int64_t = 0) {
     ldx = ld;
     krows = rows;
     k_begin = (int)kb;
@@ -195,7 +208,8 @@ template <bool kATr, bool kBTr>
 __device__ __forceinline__ void gemm_mainloop(const bf16* __restrict__ A, int64_t lda, int a_rows,
                                               int a_cols, int m0, const bf16* __restrict__ B,
                                               int64_t ldb, int b_rows, int b_cols, int n0, int64_t kt0,
-                                              int nk, char* smem, Acc& acc) {
+                                              int nk, char* smem, Acc& acc,
+                                              const int* b_gidx = nullptr, int64_t b_goff = 0) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / kWavesN, wn = wave % kWavesN;
@@ -208,7 +222,7 @@ __device__ __forceinline__ void gemm_mainloop(const bf16* __restrict__ A, int64_
   Tile<kATr> ta;
   Tile<kBTr> tb;
   ta.init(A, lda, a_rows, a_cols, m0, kt0 * kBK, lane, wave);
-  tb.init(B, ldb, b_rows, b_cols, n0, kt0 * kBK, lane, wave);
+  tb.init(B, ldb, b_rows, b_cols, n0, kt0 * kBK, lane, wave, b_gidx, b_goff);
   auto issue = [&](int stage, int t) {
     ta.issue(smem + stage * kStageBytes, t, wave);
     tb.issue(smem + stage * kStageBytes + kABytes, t, wave);
@@ -276,17 +290,28 @@ __device__ __forceinline__ int acc_col(int wn, int j, int lane) { return wn * kT
 // (kPart); with kStoreZ it stores z (bf16) into zbuf in the blocked layout
 // below (ldz = padded vocabulary, a multiple of 64).
 // ---------------------------------------------------------------------------
+//
+// Token rows: chunk token j (< the chunk's row count, read from `count` when
+// it is not null) is row rows[c0 + j] of h when rows != nullptr (compacted
+// chunk), else row c0 + j.  The grid covers cmax tokens; tiles past the
+// count exit at once.
 template <bool kStoreZ, bool kPart>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_logits_bf16(
-    const bf16* __restrict__ W, const bf16* __restrict__ h, int V, int C, int H, float s,
+    const bf16* __restrict__ W, const bf16* __restrict__ h, int V, int cmax, int H, float s,
+    const int* __restrict__ rows, const int* __restrict__ count, int64_t c0,
     floatx2* __restrict__ part, float* __restrict__ rpart, int64_t ldp, bf16* __restrict__ zbuf,
     int64_t ldz, int group_m) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
-  const int tiles_m = (int)cdiv(V, kBM), tiles_n = (int)cdiv(C, kBN);
-  const TileCoord tc = tile_coord(tiles_m, tiles_n, group_m);
+  int C = cmax;
+  if (count != nullptr) {
+    const int64_t n = (int64_t)*count - c0;
+    C = n < 0 ? 0 : (n < cmax ? (int)n : cmax);
+  }
+  const TileCoord tc = tile_coord((int)cdiv(V, kBM), (int)cdiv(C, kBN), 1, group_m);
+  if (!tc.active) return;
   const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
   Acc acc;
-  gemm_mainloop<false, false>(W, H, V, 0, m0, h, H, C, 0, n0, 0, H / kBK, smem, acc);
+  gemm_mainloop<false, false>(W, H, V, 0, m0, h, H, C, 0, n0, 0, H / kBK, smem, acc, rows, c0);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN;
@@ -358,17 +383,25 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_logits_bf16(
 // K rows (vocabulary rows of W [V, H], transposed in LDS).  Rows of W past
 // V are clamped: g is zero in those columns.
 // ---------------------------------------------------------------------------
+// M = chunk tokens: the grid covers M (upper bound); the tokens that exist
+// are min(*count - c0, M) when count != nullptr.
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dh_bf16(
-    const bf16* __restrict__ g, int64_t ldg, int M, const bf16* __restrict__ W, int V, int H,
-    int k_tiles, int splits, float* __restrict__ out, int group_m) {
+    const bf16* __restrict__ g, int64_t ldg, int M, const int* __restrict__ count, int64_t c0,
+    const bf16* __restrict__ W, int V, int H, int k_tiles, int splits, float* __restrict__ out,
+    int group_m) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
-  const int tiles_m = (int)cdiv(M, kBM), tiles_n = (int)cdiv(H, kBN);
-  const TileCoord tc = tile_coord(tiles_m, tiles_n, group_m);
+  int Me = M;
+  if (count != nullptr) {
+    const int64_t n = (int64_t)*count - c0;
+    Me = n < 0 ? 0 : (n < M ? (int)n : M);
+  }
+  const TileCoord tc = tile_coord((int)cdiv(Me, kBM), (int)cdiv(H, kBN), splits, group_m);
+  if (!tc.active) return;
   const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
   const int kt0 = (int)((int64_t)k_tiles * tc.split / splits);
   const int kt1 = (int)((int64_t)k_tiles * (tc.split + 1) / splits);
   Acc acc;
-  gemm_mainloop<false, true>(g, ldg, M, 0, m0, W, H, V, H, n0, kt0, kt1 - kt0, smem, acc);
+  gemm_mainloop<false, true>(g, ldg, Me, 0, m0, W, H, V, H, n0, kt0, kt1 - kt0, smem, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN;
@@ -381,7 +414,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dh_bf16(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = m0 + acc_row(wm, i, lane, r);
-        if (row < M && col < H) o[(int64_t)row * H + col] = acc[i][j][r];
+        if (row < Me && col < H) o[(int64_t)row * H + col] = acc[i][j][r];
       }
     }
 }
@@ -397,16 +430,26 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dh_bf16(
 // kMode 2: acc32 += acc                          (middle chunk)
 // kMode 3: out (bf16) = acc32 + acc              (last chunk)
 // ---------------------------------------------------------------------------
+// The chunk's tokens: Kp = the padded count (multiple of 64), or, when
+// count != nullptr, min(*count - c0, cmax) rounded up to 64.
 template <int kMode>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dw_bf16(
-    const bf16* __restrict__ g, int64_t ldg, int Kp, int V, const bf16* __restrict__ hT,
-    int64_t ldh, int H, bf16* __restrict__ out, float* __restrict__ acc32, int group_m) {
+    const bf16* __restrict__ g, int64_t ldg, int cmax, const int* __restrict__ count, int64_t c0,
+    int V, const bf16* __restrict__ hT, int64_t ldh, int H, bf16* __restrict__ out,
+    float* __restrict__ acc32, int group_m) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
-  const int tiles_m = (int)cdiv(V, kBM), tiles_n = (int)cdiv(H, kBN);
-  const TileCoord tc = tile_coord(tiles_m, tiles_n, group_m);
+  const TileCoord tc = tile_coord((int)cdiv(V, kBM), (int)cdiv(H, kBN), 1, group_m);
+  if (!tc.active) return;
   const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
+  int Ce = cmax;
+  if (count != nullptr) {
+    const int64_t n = (int64_t)*count - c0;
+    Ce = n < 0 ? 0 : (n < cmax ? (int)n : cmax);
+  }
+  const int Kp = (int)round_up(Ce, kBK);
   Acc acc;
-  gemm_mainloop<true, false>(g, ldg, Kp, (int)ldg, m0, hT, ldh, H, 0, n0, 0, Kp / kBK, smem, acc);
+  gemm_mainloop<true, false>(g, ldg, max(Kp, 1), (int)ldg, m0, hT, ldh, H, 0, n0, 0, Kp / kBK, smem,
+                             acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN;

@@ -34,6 +34,67 @@ __global__ __launch_bounds__(1024) void k_divisor(const int64_t* __restrict__ ta
 }
 
 // ---------------------------------------------------------------------------
+// Row compaction.  Rows whose target is ignore_index contribute nothing (page
+// 1, cross_entropy_kernel step 2 zeroes them), so the bf16 path multiplies
+// only the others: rows[k] = index of the k-th row with target != ignore
+// (ascending), *count = their number.  One block; a wave ballot gives each
+// row its position, so the order (and everything after it) is deterministic.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void k_compact_rows(const int64_t* __restrict__ target, int64_t N,
+                                                       int64_t ignore, int* __restrict__ rows,
+                                                       int* __restrict__ count) {
+  __shared__ int wtot[16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int base = 0;
+  for (int64_t s0 = 0; s0 < N; s0 += 1024) {
+    const int64_t i = s0 + threadIdx.x;
+    const bool v = i < N && target[i] != ignore;
+    const uint64_t m = __ballot(v);
+    const int before = __popcll(m & ((uint64_t(1) << lane) - 1));
+    if (lane == 0) wtot[wave] = __popcll(m);
+    __syncthreads();
+    int off = base;
+    for (int w = 0; w < wave; ++w) off += wtot[w];
+    if (v) rows[off + before] = (int)i;
+    int tot = 0;
+    for (int w = 0; w < 16; ++w) tot += wtot[w];
+    base += tot;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *count = base;
+}
+
+// Outputs of ignored rows that no later kernel writes: a[i] = va, b[i] = vb,
+// c[i] = vc where target[i] == ignore (pointers may be null).
+__global__ __launch_bounds__(256) void k_ignored_rows_init(const int64_t* __restrict__ target,
+                                                           int64_t N, int64_t ignore, float* a,
+                                                           float va, float* b, float vb, float* c,
+                                                           float vc) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= N || target[i] != ignore) return;
+  if (a) a[i] = va;
+  if (b) b[i] = vb;
+  if (c) c[i] = vc;
+}
+
+// Rows of dH that belong to ignored targets are exactly +0 (one block per row).
+template <typename T>
+__global__ __launch_bounds__(256) void k_zero_ignored_rows(const int64_t* __restrict__ target,
+                                                           int64_t N, int64_t ignore,
+                                                           T* __restrict__ out, int64_t H) {
+  const int64_t i = blockIdx.x;
+  if (i >= N || target[i] != ignore) return;
+  for (int64_t e = threadIdx.x; e < H; e += 256) out[i * H + e] = from_f32<T>(0.f);
+}
+
+// Number of rows of a chunk: the compacted rows [c0, c0 + cmax) that exist.
+__device__ __forceinline__ int64_t chunk_rows(const int* count, int64_t c0, int64_t cmax) {
+  if (count == nullptr) return cmax;
+  const int64_t n = (int64_t)*count - c0;
+  return n < 0 ? 0 : (n < cmax ? n : cmax);
+}
+
+// ---------------------------------------------------------------------------
 // dst[c, r] = src[r, c] for r < R, c < Cn; dst[c, r] = 0 for R <= r < Rp.
 // 64 x 64 tiles through LDS.
 // ---------------------------------------------------------------------------
@@ -132,6 +193,40 @@ __global__ __launch_bounds__(256) void k_transpose_bf16(const bf16* __restrict__
   }
 }
 
+// h^T of a compacted chunk: dst[c, j] = src[rows[c0 + j], c] for j < the
+// chunk's row count (device-side), 0 for the rest of the Rp columns.  Same
+// tiling as k_transpose_bf16.
+__global__ __launch_bounds__(256) void k_transpose_gather_bf16(const bf16* __restrict__ src,
+                                                               const int* __restrict__ rows,
+                                                               const int* __restrict__ count,
+                                                               int64_t c0, int64_t cmax, int64_t Cn,
+                                                               bf16* __restrict__ dst, int64_t ldd,
+                                                               int64_t Rp) {
+  __shared__ bf16 tile[64][64 + 8];
+  const int tx = threadIdx.x & 7, ty = threadIdx.x >> 3;
+  const int64_t R = chunk_rows(count, c0, cmax);
+  const int64_t r0 = (int64_t)blockIdx.x * 64, c0c = (int64_t)blockIdx.y * 64;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int lr = ty + 32 * p;
+    const int64_t r = r0 + lr, c = c0c + tx * 8;
+    bf16x8 v = bf16x8{};
+    if (r < R && c + 8 <= Cn) v = *(const bf16x8*)(src + (int64_t)rows[c0 + r] * Cn + c);
+    *(bf16x8*)&tile[lr][tx * 8] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int lc = ty + 32 * p;
+    const int64_t c = c0c + lc, r = r0 + tx * 8;
+    if (c >= Cn || r + 8 > Rp) continue;
+    bf16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = tile[tx * 8 + e][lc];
+    *(bf16x8*)(dst + c * ldd + r) = v;
+  }
+}
+
 // out[c] = sum_b part[b, c], b ascending.
 __global__ __launch_bounds__(256) void k_colsum_finish(const float* __restrict__ part, int64_t nb,
                                                        int64_t Cn, float* __restrict__ out) {
@@ -212,32 +307,42 @@ __global__ __launch_bounds__(64) void k_row_partials_f32(const float* __restrict
 // mode 1 (shard): writes out_m[i] = M, out_s[i] = S (sum relative to M) and,
 // when out_r != nullptr, out_r[i] = R_i.
 // ---------------------------------------------------------------------------
+//
+// Rows: chunk row j (< the chunk's row count) is row i = rows[c0 + j] of the
+// batch when rows != nullptr (compacted chunk), else i = c0 + j.  Per-row
+// inputs and the lse / rloss / out_* outputs use i; coef_out, lsec and tcol
+// (when not null) use j: the chunk's coefficient, lse and target column
+// (target - v0, or -1 for an ignored row).
 __global__ __launch_bounds__(256) void k_combine_rows(
     const floatx2* __restrict__ part, const float* __restrict__ rpart, int64_t ldp, int64_t nT,
-    int64_t C, int mode, const int64_t* __restrict__ target, const float* __restrict__ p_mask,
+    int64_t cmax, const int* __restrict__ rows, const int* __restrict__ count, int64_t c0,
+    int mode, const int64_t* __restrict__ target, const float* __restrict__ p_mask,
     int64_t ignore, const float* __restrict__ zt, const float* __restrict__ R, float eps, float Vg,
     float s, const float* __restrict__ D, float* __restrict__ lse_out,
-    float* __restrict__ rloss_out, float* __restrict__ coef_out, float* __restrict__ out_m,
-    float* __restrict__ out_s, float* __restrict__ out_r) {
+    float* __restrict__ rloss_out, float* __restrict__ coef_out, float* __restrict__ lsec,
+    int* __restrict__ tcol, int64_t v0, float* __restrict__ out_m, float* __restrict__ out_s,
+    float* __restrict__ out_r) {
   __shared__ float sm[8][32], ss[8][32], sr[8][32];
   const int tx = threadIdx.x & 31, grp = threadIdx.x >> 5;
-  const int64_t i = (int64_t)blockIdx.x * 32 + tx;
+  const int64_t C = chunk_rows(count, c0, cmax);
+  const int64_t j = (int64_t)blockIdx.x * 32 + tx;
   float m = -INFINITY, sum = 0.f, rsum = 0.f;
-  if (i < C)
+  if (j < C)
     for (int64_t t = grp; t < nT; t += 8) {
-      const floatx2 p = part[t * ldp + i];
+      const floatx2 p = part[t * ldp + j];
       lse_merge(m, sum, p[0], p[1]);
-      if (rpart != nullptr) rsum += rpart[t * ldp + i];
+      if (rpart != nullptr) rsum += rpart[t * ldp + j];
     }
   sm[grp][tx] = m;
   ss[grp][tx] = sum;
   sr[grp][tx] = rsum;
   __syncthreads();
-  if (grp != 0 || i >= C) return;
+  if (grp != 0 || j >= C) return;
   for (int g = 1; g < 8; ++g) {
     lse_merge(m, sum, sm[g][tx], ss[g][tx]);
     rsum += sr[g][tx];
   }
+  const int64_t i = rows != nullptr ? (int64_t)rows[c0 + j] : c0 + j;
   if (mode == 1) {
     out_m[i] = m;
     out_s[i] = sum;
@@ -253,21 +358,34 @@ __global__ __launch_bounds__(256) void k_combine_rows(
     l = ((1.f - eps) * (lse - zt[i]) + eps * (lse - rs / Vg)) / p;
     cf = s / (p * D[0]);
   }
-  lse_out[i] = lse;
+  lse_out[i] = valid ? lse : 0.f;
   rloss_out[i] = l;
-  coef_out[i] = cf;
+  coef_out[j] = cf;
+  if (lsec != nullptr) lsec[j] = lse;
+  if (tcol != nullptr) tcol[j] = valid ? (int)(target[i] - v0) : -1;
 }
 
-// coef_i = s / (p_i D), 0 on ignored rows (shard backward, lse given).
+// coef_j = s / (p_i D), 0 on ignored rows (shard backward, lse given), for
+// chunk row j -> batch row i as in k_combine_rows; with lsec / tcol also the
+// chunk's lse (from the given lse) and target column.
 __global__ __launch_bounds__(256) void k_coef_rows(const int64_t* __restrict__ target,
                                                    const float* __restrict__ p_mask, int64_t ignore,
-                                                   int64_t C, float s, const float* __restrict__ D,
-                                                   float* __restrict__ coef) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= C) return;
+                                                   int64_t cmax, const int* __restrict__ rows,
+                                                   const int* __restrict__ count, int64_t c0,
+                                                   float s, const float* __restrict__ D,
+                                                   float* __restrict__ coef,
+                                                   const float* __restrict__ lse_in,
+                                                   float* __restrict__ lsec,
+                                                   int* __restrict__ tcol, int64_t v0) {
+  const int64_t C = chunk_rows(count, c0, cmax);
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j >= C) return;
+  const int64_t i = rows != nullptr ? (int64_t)rows[c0 + j] : c0 + j;
   const bool valid = target[i] != ignore;
   const float p = (p_mask != nullptr && valid) ? p_mask[i] : 1.f;
-  coef[i] = valid ? s / (p * D[0]) : 0.f;
+  coef[j] = valid ? s / (p * D[0]) : 0.f;
+  if (lsec != nullptr) lsec[j] = lse_in[i];
+  if (tcol != nullptr) tcol[j] = valid ? (int)(target[i] - v0) : -1;
 }
 
 // ---------------------------------------------------------------------------
@@ -358,8 +476,9 @@ __global__ __launch_bounds__(256) void k_gpass(T* __restrict__ z, int64_t ldz, i
 // dlogits for the bf16 path (same formula as k_gpass), reading z from the
 // blocked layout the logits GEMM writes: element (token t, column v) at
 // ((t / 16) * (ldz / 4) + v / 4) * 64 + (t % 16) * 4 + v % 4, and writing g
-// row-major [rows, ldz] for both backward GEMMs.  Rows C .. (grid rows) - 1
-// and columns >= V are written as zeros.
+// row-major [rows, ldz] for both backward GEMMs.  Chunk rows are given by the
+// device-side count (chunk_rows); rows C .. round_up(C, 64) - 1 and columns
+// >= V are written as zeros.  lse, coef and tcol are per chunk row.
 //
 // One block = 64 tokens x 256 columns, 256 threads.  Thread -> two fixed
 // tokens (their lse, coefficient and target stay in registers) and eight
@@ -368,14 +487,17 @@ __global__ __launch_bounds__(256) void k_gpass(T* __restrict__ z, int64_t ldz, i
 // ---------------------------------------------------------------------------
 constexpr int kGpassCols = 256;
 __global__ __launch_bounds__(256) void k_gpass_blk(const bf16* __restrict__ zblk, int64_t ldz,
-                                                   int64_t C, int64_t V,
+                                                   int64_t cmax, const int* __restrict__ count,
+                                                   int64_t c0, int64_t V,
                                                    const float* __restrict__ lse,
                                                    const float* __restrict__ coef,
-                                                   const int64_t* __restrict__ target, int64_t v0,
-                                                   float eps, float Vg, bf16* __restrict__ g) {
+                                                   const int* __restrict__ tcol, float eps,
+                                                   float Vg, bf16* __restrict__ g) {
   __shared__ bf16 tile[64][kGpassCols + 8];  // [token][column]
   const int tid = threadIdx.x;
+  const int64_t C = chunk_rows(count, c0, cmax);
   const int64_t i0 = (int64_t)blockIdx.y * 64, j0 = (int64_t)blockIdx.x * kGpassCols;
+  if (i0 >= round_up(C, 64)) return;  // rows past the chunk's padded count are never read
   const int64_t nvb = min((int64_t)kGpassCols / 4, (ldz - j0) / 4);  // column blocks in range
   const float epsV = eps / Vg;
   const int tb = tid >> 6, vbo = (tid >> 3) & 7, w = tid & 7;
@@ -388,7 +510,7 @@ __global__ __launch_bounds__(256) void k_gpass_blk(const bf16* __restrict__ zblk
     const int64_t i = i0 + tl0 + q;
     cf[q] = (i < C) ? coef[i] : 0.f;
     l2[q] = (cf[q] != 0.f) ? lse[i] * kLog2e : 0.f;
-    yc[q] = (cf[q] != 0.f) ? target[i] - v0 - j0 : -1;  // column within this tile
+    yc[q] = (cf[q] != 0.f && tcol[i] >= 0) ? (int64_t)tcol[i] - j0 : -1;  // column within this tile
     tg[q] = cf[q] * (1.f - eps);
     any |= cf[q] != 0.f;
   }
@@ -449,6 +571,36 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
       float a = part[k];
       for (int s = 1; s < S; ++s) a += part[(int64_t)s * MN + k];
       out[k] = from_f32<Tout>(a);
+    }
+  }
+}
+
+// dH rows of a compacted chunk: out[rows[c0 + j], :] = sum_s part[s][j][:]
+// (s ascending) for j < the chunk's row count.
+template <typename Tout>
+__global__ __launch_bounds__(256) void k_splitk_scatter(const float* __restrict__ part, int S,
+                                                        int64_t cmax, int64_t H,
+                                                        const int* __restrict__ rows,
+                                                        const int* __restrict__ count, int64_t c0,
+                                                        Tout* __restrict__ out) {
+  const int64_t C = chunk_rows(count, c0, cmax);
+  const int64_t j = blockIdx.x;  // one block per chunk row
+  if (j >= C) return;
+  const int64_t MN = cmax * H;
+  const int64_t dst = (int64_t)rows[c0 + j] * H;
+  for (int64_t e = (int64_t)threadIdx.x * 4; e < H; e += 256 * 4) {
+    const int64_t src = j * H + e;
+    if (e + 4 <= H) {
+      floatx4 acc = *(const floatx4*)(part + src);
+      for (int s = 1; s < S; ++s) acc += *(const floatx4*)(part + (int64_t)s * MN + src);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) out[dst + e + k] = from_f32<Tout>(acc[k]);
+    } else {
+      for (int64_t k = 0; e + k < H; ++k) {
+        float a = part[src + k];
+        for (int s = 1; s < S; ++s) a += part[(int64_t)s * MN + src + k];
+        out[dst + e + k] = from_f32<Tout>(a);
+      }
     }
   }
 }

@@ -38,7 +38,7 @@ def _sample_rows(target, n_valid=40, n_ign=6, seed=0):
     v = np.nonzero(target != -100)[0]
     ig = np.nonzero(target == -100)[0]
     rows = list(rng.choice(v, n_valid, replace=False)) + list(rng.choice(ig, n_ign, replace=False))
-    rows += [0, len(target) - 1]
+    rows += [int(v[0]), int(v[-1])] if n_ign == 0 else [0, len(target) - 1]
     return np.unique(np.array(rows, dtype=np.int64))
 
 
@@ -107,7 +107,11 @@ def test_full_size_vocab_shard():
     say(f"case full shard partials: N={w.N} H={w.H} V_local={Vl} shard {k}")
     r = fldce.fldce_shard_partials(hd, Wd, td, v0, logit_scale=w.logit_scale)
     torch.cuda.synchronize()
-    rows = _sample_rows(t)
+    rows = _sample_rows(t, n_ign=0)
+    ign = np.nonzero(t == -100)[0]
+    for x, want in (("row_max", -np.inf), ("row_sumexp", 0.0), ("target_logit", 0.0),
+                    ("row_sumlogit", 0.0)):
+        assert np.all(host(r[x])[ign] == want), x  # skipped rows
     m, S, tl, rs = (host(r[x])[rows] for x in ("row_max", "row_sumexp", "target_logit",
                                                "row_sumlogit"))
     om, oS, ot, orr = O.shard_partials(h.values[rows], Wk.values, t[rows], v0, w.logit_scale)

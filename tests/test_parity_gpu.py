@@ -100,6 +100,14 @@ def test_p_mask_none_is_ones():
     _compare(w, r, o, t)
 
 
+def test_no_ignored_rows():
+    w = synth.custom("all_valid_bf16", 2, 150, 128, 900, label_smoothing=0.1, logit_scale=0.5)
+    t = np.random.default_rng(7).integers(0, w.V, w.N).astype(np.int64)
+    _, p = synth.targets(w)
+    r, o, _ = _run(w, target=t, p_mask=p)
+    _compare(w, r, o, t)
+
+
 def test_all_ignored():
     w = synth.custom("all_ignored_bf16", 1, 200, 128, 500, total_is_N=False)
     t = np.full(w.N, -100, dtype=np.int64)
@@ -189,16 +197,21 @@ def test_vocab_shards_match_full_vocab(dtype):
         torch.cuda.synchronize()
         m, S, tl, rs = (host(r[x]) for x in ("row_max", "row_sumexp", "target_logit", "row_sumlogit"))
         om, oS, ot, orr = O.shard_partials(h.values, Wk.values, t, v0, 0.5)
-        np.testing.assert_allclose(m, om, atol=tol * 4, rtol=0)
-        np.testing.assert_allclose(np.log(S) + m, np.log(oS) + om, atol=tol * 4, rtol=0)
+        valid = t != -100
+        # rows whose target is ignore_index are skipped: (-inf, 0, 0, 0)
+        assert np.all(np.isneginf(m[~valid])) and np.all(S[~valid] == 0)
+        assert np.all(tl[~valid] == 0) and np.all(rs[~valid] == 0)
+        np.testing.assert_allclose(m[valid], om[valid], atol=tol * 4, rtol=0)
+        np.testing.assert_allclose((np.log(S) + m)[valid], (np.log(oS) + om)[valid], atol=tol * 4, rtol=0)
         np.testing.assert_allclose(tl, ot, atol=tol * 4, rtol=0)
-        np.testing.assert_allclose(rs, orr, atol=tol * 40, rtol=tol)
+        np.testing.assert_allclose(rs[valid], orr[valid], atol=tol * 40, rtol=tol)
         assert np.all(tl[(t < v0) | (t >= v0 + w.V_local)] == 0.0)
         parts.append((m, S, tl, rs))
-    lse, zt, zs = O.combine_shard_partials(parts)
-    np.testing.assert_allclose(lse, full["lse"], atol=tol * 4, rtol=0)
     valid = t != -100
-    rl = O.row_losses(lse, zt, zs, w.V, p, valid, 0.1)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        lse, zt, zs = O.combine_shard_partials(parts)
+    np.testing.assert_allclose(lse[valid], full["lse"][valid], atol=tol * 4, rtol=0)
+    rl = O.row_losses(np.where(valid, lse, 0.0), zt, zs, w.V, p, valid, 0.1)
     loss = O.loss_from_row_losses(rl, float(w.N))
     assert abs(loss - full["loss"]) <= LOSS_RTOL[dtype] * abs(full["loss"])
     # shard backward from the oracle's global lse
