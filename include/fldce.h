@@ -115,9 +115,15 @@ size_t fldce_workspace_size(int64_t N, int64_t H, int64_t V, int dtype,
  *   dW           [V,H] dtype       out: d loss / d W (overwritten; float32
  *                                  accumulation, rounded once to dtype)
  *   row_lse      [N]   float32     optional out (NULL ok): per-row lse
+ *                                  (0 on rows whose target is ignore_index)
  *   row_loss     [N]   float32     optional out (NULL ok): per-row l_i
  *   chunk_rows       rows per chunk, 0 = fldce_default_chunk_rows
  *   workspace        device scratch of at least fldce_workspace_size bytes
+ *
+ * Rows whose target is ignore_index contribute exactly nothing (page 1,
+ * cross_entropy_kernel step 2), so the bf16 path never multiplies them: the
+ * valid rows are compacted on the device and only they go through the three
+ * GEMMs; their dH rows are written as +0.
  *
  * bf16 requires H % 64 == 0 (FLDCE_ERR_UNSUPPORTED otherwise); all pointers
  * must be 16-byte aligned.
@@ -150,6 +156,9 @@ size_t fldce_shard_partials_workspace_size(int64_t N, int64_t H,
  *
  * Combining over shards: M = max_k m_k, lse = M + log sum_k S_k e^{m_k - M},
  * z_target = sum_k target_logit_k, sum_j z_ij = sum_k row_sumlogit_k.
+ *
+ * Rows whose target is ignore_index are skipped (they need no softmax): for
+ * them row_max = -INFINITY and row_sumexp = target_logit = row_sumlogit = 0.
  */
 int fldce_shard_partials(const void* h, const void* W_local,
                          const int64_t* target, int64_t N, int64_t H,
