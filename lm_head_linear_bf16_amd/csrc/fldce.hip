@@ -52,21 +52,6 @@ size_t take(size_t& cur, size_t bytes) {
   return o;
 }
 
-int choose_splits(int64_t tiles, int64_t k_tiles) {
-  int best = 1;
-  double bestc = 1e300;
-  for (int S = 1; S <= 8; ++S) {
-    if (k_tiles / S < 8) break;
-    const double waves = std::ceil((double)(tiles * S) / 256.0);
-    const double c = waves / S + 0.02 * S;  // small charge for the fp32 partials traffic
-    if (c < bestc - 1e-12) {
-      bestc = c;
-      best = S;
-    }
-  }
-  return best;
-}
-
 int64_t default_chunk(int64_t N, int64_t V, int64_t esz) {
   const int64_t Vp = round_up(V, 64);
   const int64_t per_row = 2 * esz * Vp;  // bf16: z and g; fp32: z/g and g^T
@@ -122,7 +107,7 @@ Plan make_plan(int mode, int64_t N, int64_t H, int64_t V, int dtype, int64_t chu
   p.oHT = take(cur, (size_t)H * p.Cp * p.esz);
   if (bf) {
     const int64_t tiles = cdiv(p.C, kBM) * cdiv(H, kBN);
-    p.splits = choose_splits(tiles, p.Vp / kBK);
+    p.splits = choose_splits(tiles, p.Vp / kBK, 8);
     p.oDHpart = take(cur, (size_t)p.splits * p.C * H * 4);
     if (p.nchunks > 1) p.oDW32 = take(cur, (size_t)V * H * 4);
   }
@@ -347,11 +332,11 @@ int run_core_bf16(const Core& c, const Plan& p, char* ws, hipStream_t st) {
       }
       StageTimer tm(kDHReduce, st);
       if (c.dH_f32)
-        k_splitk_scatter<float><<<(unsigned)cmax, 256, 0, st>>>(dHpart, S, cmax, H, c.rows,
-                                                                c.count, c0, (float*)c.dH);
+        k_splitk_scatter<float><<<(unsigned)cmax, 256, 0, st>>>(
+            dHpart, S, Vp / kBK, cmax, H, c.rows, c.count, c0, (float*)c.dH);
       else
-        k_splitk_scatter<bf16><<<(unsigned)cmax, 256, 0, st>>>(dHpart, S, cmax, H, c.rows,
-                                                               c.count, c0, (bf16*)c.dH);
+        k_splitk_scatter<bf16><<<(unsigned)cmax, 256, 0, st>>>(
+            dHpart, S, Vp / kBK, cmax, H, c.rows, c.count, c0, (bf16*)c.dH);
     }
     {  // 5. dW += g^T h
       StageTimer tm(kDWGemm, st);

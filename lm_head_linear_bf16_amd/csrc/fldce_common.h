@@ -55,4 +55,25 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
 __host__ __device__ constexpr int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 __host__ __device__ constexpr int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 
+// Split count for a split-K GEMM with `tiles` output tiles and k_tiles K
+// tiles, at most max_splits: minimises the waves of work over 256 CUs per
+// split (ceil(tiles * S / 256) / S, plus a small charge per split for the
+// fp32 partials), keeping >= 8 K tiles per split.  Used by the host to size
+// the grid and the partial buffer, and by the kernels on the device once the
+// number of active tiles is known.
+__host__ __device__ inline int choose_splits(int64_t tiles, int64_t k_tiles, int max_splits) {
+  int best = 1;
+  double bestc = 1e300;
+  for (int S = 1; S <= max_splits; ++S) {
+    if (k_tiles / S < 8) break;
+    const double waves = (double)((tiles * S + 255) / 256);
+    const double c = waves / S + 0.02 * S;
+    if (c < bestc - 1e-12) {
+      bestc = c;
+      best = S;
+    }
+  }
+  return best;
+}
+
 }  // namespace fldce

@@ -383,11 +383,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_logits_bf16(
 // K rows (vocabulary rows of W [V, H], transposed in LDS).  Rows of W past
 // V are clamped: g is zero in those columns.
 // ---------------------------------------------------------------------------
-// M = chunk tokens: the grid covers M (upper bound); the tokens that exist
-// are min(*count - c0, M) when count != nullptr.
+// M = chunk tokens: the grid covers M (upper bound) x max_splits; the tokens
+// that exist are min(*count - c0, M) when count != nullptr, and the split
+// count is chosen for them (choose_splits; k_splitk_scatter recomputes it).
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dh_bf16(
     const bf16* __restrict__ g, int64_t ldg, int M, const int* __restrict__ count, int64_t c0,
-    const bf16* __restrict__ W, int V, int H, int k_tiles, int splits, float* __restrict__ out,
+    const bf16* __restrict__ W, int V, int H, int k_tiles, int max_splits, float* __restrict__ out,
     int group_m) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   int Me = M;
@@ -395,6 +396,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dh_bf16(
     const int64_t n = (int64_t)*count - c0;
     Me = n < 0 ? 0 : (n < M ? (int)n : M);
   }
+  const int splits = choose_splits(cdiv(Me, kBM) * cdiv(H, kBN), k_tiles, max_splits);
   const TileCoord tc = tile_coord((int)cdiv(Me, kBM), (int)cdiv(H, kBN), splits, group_m);
   if (!tc.active) return;
   const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;

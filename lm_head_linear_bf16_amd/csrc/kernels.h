@@ -576,14 +576,17 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
 }
 
 // dH rows of a compacted chunk: out[rows[c0 + j], :] = sum_s part[s][j][:]
-// (s ascending) for j < the chunk's row count.
+// (s ascending) for j < the chunk's row count; S = choose_splits for that
+// count, exactly as the dH GEMM chose it.
 template <typename Tout>
-__global__ __launch_bounds__(256) void k_splitk_scatter(const float* __restrict__ part, int S,
+__global__ __launch_bounds__(256) void k_splitk_scatter(const float* __restrict__ part,
+                                                        int max_splits, int64_t k_tiles,
                                                         int64_t cmax, int64_t H,
                                                         const int* __restrict__ rows,
                                                         const int* __restrict__ count, int64_t c0,
                                                         Tout* __restrict__ out) {
   const int64_t C = chunk_rows(count, c0, cmax);
+  const int S = choose_splits(cdiv(C, 256) * cdiv(H, 256), k_tiles, max_splits);
   const int64_t j = blockIdx.x;  // one block per chunk row
   if (j >= C) return;
   const int64_t MN = cmax * H;
