@@ -35,6 +35,12 @@ Readings where the pages leave a step open (each listed in the design notes):
   number of non-ignored rows (page 1 counts them with ``target.ne``).  An
   all-ignored batch gives loss 0 and zero gradients.
 * p_mask of an ignored row is never used (page 1 returns before using it).
+* The optional bias enters the logits before the logit scale
+  (z = s (h W^T + b): ``F.linear(c_x, weight, bias)`` then the kernels'
+  scale), and db is the column sum of the same gradient g over the rows.
+* The end-of-block weight w of the module's forward divides p_mask by w on
+  the rows whose target is the EOB token (so their loss and gradient are
+  multiplied by w); the oracle applies it exactly that way.
 
 Rows are processed in blocks purely to bound memory; each row's arithmetic is
 the same as with a single block.
@@ -51,7 +57,8 @@ __all__ = [
     "scaled_logits", "row_logsumexp", "valid_rows", "divisor", "row_losses",
     "row_losses_literal", "dlogits", "forward_backward", "row_stats",
     "dH_rows", "dW_rows", "shard_partials", "combine_shard_partials",
-    "shard_backward", "loss_from_row_losses",
+    "shard_backward", "loss_from_row_losses", "eob_p_mask", "forward",
+    "scale_grads",
 ]
 
 _F = np.float64
@@ -62,10 +69,14 @@ def _f64(x) -> np.ndarray:
 
 
 # -- step 1: logits --------------------------------------------------------
-def scaled_logits(h, W, logit_scale: float) -> np.ndarray:
-    """z = s * (h W^T).  Page 1: ``F.linear(c_x, weight)`` in the chunk loop,
-    and the kernels multiply every loaded logit by ``logit_scale``."""
-    return float(logit_scale) * (_f64(h) @ _f64(W).T)
+def scaled_logits(h, W, logit_scale: float, bias=None) -> np.ndarray:
+    """z = s * (h W^T + b).  Page 1: ``F.linear(c_x, weight, bias)`` in the
+    chunk loop, and the kernels multiply every loaded logit by
+    ``logit_scale``.  ``bias`` is None (no bias) or [V]."""
+    a = _f64(h) @ _f64(W).T
+    if bias is not None:
+        a = a + _f64(bias)[None, :]
+    return float(logit_scale) * a
 
 
 # -- step 2: per-row logsumexp ---------------------------------------------
@@ -97,6 +108,20 @@ def divisor(valid, reduction: str, total: Optional[int] = None) -> float:
         return float(total)
     n = int(np.count_nonzero(valid))
     return float(n) if n > 0 else 1.0
+
+
+def eob_p_mask(target, p_mask, eob_token_id: Optional[int], eob_weight: float):
+    """Page 1, ``FusedLinearDiffusionCrossEntropyLoss.forward``: when an EOB
+    token id is given and its weight is not 1, p_mask is copied and divided
+    by the weight on the rows whose target is that token (the kernel divides
+    each row's loss by p_mask, so their loss is multiplied by the weight)."""
+    p = _f64(p_mask).copy()
+    if eob_token_id is None or eob_weight == 1.0:
+        return p
+    eob = np.asarray(target) == eob_token_id
+    with np.errstate(divide="ignore"):     # weight 0: p = inf, the rows add nothing
+        p[eob] = p[eob] / float(eob_weight)
+    return p
 
 
 # -- step 3: per-row loss --------------------------------------------------
@@ -165,16 +190,19 @@ def dlogits(z, lse, target_col, p_mask, valid, D: float,
 def forward_backward(h, W, target, p_mask=None, ignore_index: int = -100,
                      label_smoothing: float = 0.0, logit_scale: float = 1.0,
                      reduction: str = "mean", total: Optional[int] = None,
-                     row_block: int = 1024, need_grads: bool = True):
+                     row_block: int = 1024, need_grads: bool = True, bias=None,
+                     eob_token_id: Optional[int] = None, eob_weight: float = 1.0):
     """loss, dH = g W, dW = g^T h (page 1: the chunk loop's ``torch.mm`` and
-    ``c_logits.t() @ c_x``).  Returns a dict with loss, dH, dW, lse,
-    row_loss, D and the literal-reading loss (reference only)."""
+    ``c_logits.t() @ c_x``) and, with a bias, db = sum_i g_i (the loop's
+    ``c_logits.sum(0)``).  Returns a dict with loss, dH, dW, db (None without
+    a bias), lse, row_loss, D and the literal-reading loss (reference only)."""
     h, W = _f64(h), _f64(W)
     target = np.asarray(target, dtype=np.int64)
     N, H = h.shape
     V = W.shape[0]
     if p_mask is None:                      # page 1 module: None -> ones
         p_mask = np.ones(N)
+    p_mask = eob_p_mask(target, p_mask, eob_token_id, eob_weight)
     valid = valid_rows(target, ignore_index)
     if np.any(valid & ((target < 0) | (target >= V))):
         raise ValueError("target out of range")
@@ -184,10 +212,11 @@ def forward_backward(h, W, target, p_mask=None, ignore_index: int = -100,
     rl_lit = np.empty(N)
     dH = np.zeros((N, H)) if need_grads else None
     dW = np.zeros((V, H)) if need_grads else None
+    db = np.zeros(V) if (need_grads and bias is not None) else None
     tcol = np.where(valid, target, -1)
     for r0 in range(0, N, row_block):
         r1 = min(N, r0 + row_block)
-        z = scaled_logits(h[r0:r1], W, logit_scale)
+        z = scaled_logits(h[r0:r1], W, logit_scale, bias)
         lse[r0:r1] = row_logsumexp(z)
         zt = np.where(valid[r0:r1], z[np.arange(r1 - r0), np.maximum(tcol[r0:r1], 0)], 0.0)
         zs = z.sum(axis=1)
@@ -199,13 +228,33 @@ def forward_backward(h, W, target, p_mask=None, ignore_index: int = -100,
                         label_smoothing, logit_scale, V)
             dH[r0:r1] = g @ W
             dW += g.T @ h[r0:r1]
-    return dict(loss=loss_from_row_losses(rl, D), dH=dH, dW=dW, lse=lse,
+            if db is not None:
+                db += g.sum(axis=0)
+    return dict(loss=loss_from_row_losses(rl, D), dH=dH, dW=dW, db=db, lse=lse,
                 row_loss=rl, D=D, loss_literal=loss_from_row_losses(rl_lit, D))
+
+
+def forward(h, W, target, p_mask=None, **kw):
+    """Loss, per-row lse and per-row loss without gradients (the forward half
+    of page 1's chunk loop: ``F.linear``, ``logsumexp_fwd`` and the loss part
+    of ``cross_entropy_kernel``)."""
+    r = forward_backward(h, W, target, p_mask, need_grads=False, **kw)
+    return dict(loss=r["loss"], lse=r["lse"], row_loss=r["row_loss"], D=r["D"])
+
+
+def scale_grads(do: float, *grads):
+    """Page 1, ``fused_linear_cross_entropy_backward``: the gradients computed
+    in the forward pass are for d(loss) = 1; with an upstream gradient
+    ``do`` != 1 each is multiplied by it (skipped when do == 1).  None
+    entries stay None."""
+    if do == 1.0:
+        return tuple(grads)
+    return tuple(None if g is None else _f64(g) * float(do) for g in grads)
 
 
 # -- sampled pieces for large problems --------------------------------------
 def row_stats(h, W, target, rows: Sequence[int], logit_scale: float,
-              ignore_index: int = -100, row_block: int = 512):
+              ignore_index: int = -100, row_block: int = 512, bias=None):
     """(lse, z_target, z_sum) of the given rows over the full vocabulary."""
     h, W = _f64(h), _f64(W)
     rows = np.asarray(rows, dtype=np.int64)
@@ -215,7 +264,7 @@ def row_stats(h, W, target, rows: Sequence[int], logit_scale: float,
     zs = np.empty(len(rows))
     for b0 in range(0, len(rows), row_block):
         rr = rows[b0:b0 + row_block]
-        z = scaled_logits(h[rr], W, logit_scale)
+        z = scaled_logits(h[rr], W, logit_scale, bias)
         lse[b0:b0 + len(rr)] = row_logsumexp(z)
         zs[b0:b0 + len(rr)] = z.sum(axis=1)
         t = target[rr]
@@ -225,7 +274,7 @@ def row_stats(h, W, target, rows: Sequence[int], logit_scale: float,
 
 
 def dH_rows(h, W, target, p_mask, lse_rows, rows, D, label_smoothing,
-            logit_scale, ignore_index=-100, V_global=None, vocab_start=0):
+            logit_scale, ignore_index=-100, V_global=None, vocab_start=0, bias=None):
     """dH for the given rows: g_rows W (needs only those rows' lse).  ``W`` may
     be a vocabulary shard starting at ``vocab_start`` of a ``V_global`` vocab
     (then this is the shard's dH_partial)."""
@@ -235,29 +284,33 @@ def dH_rows(h, W, target, p_mask, lse_rows, rows, D, label_smoothing,
     V_global = W.shape[0] if V_global is None else V_global
     valid = t != ignore_index
     ins = valid & (t >= vocab_start) & (t < vocab_start + W.shape[0])
-    z = scaled_logits(h[rows], W, logit_scale)
+    z = scaled_logits(h[rows], W, logit_scale, bias)
     g = dlogits(z, lse_rows, np.where(ins, t - vocab_start, -1), np.asarray(p_mask)[rows],
                 valid, D, label_smoothing, logit_scale, V_global)
     return g @ W
 
 
 def dW_rows(h, W, target, p_mask, lse_all, vocab_rows, D, label_smoothing,
-            logit_scale, ignore_index=-100, V_global=None, vocab_start=0):
+            logit_scale, ignore_index=-100, V_global=None, vocab_start=0, bias=None,
+            with_db: bool = False):
     """dW for the given vocabulary rows (of ``W``, which may be a shard that
     starts at ``vocab_start`` in a vocabulary of ``V_global``): g[:, j]^T h
-    over all token rows (needs every row's lse)."""
+    over all token rows (needs every row's lse).  With ``with_db`` also returns
+    db of those vocabulary rows (the column sums of g)."""
     h = _f64(h)
     vr = np.asarray(vocab_rows, dtype=np.int64)
     Wr = _f64(W)[vr]
     target = np.asarray(target, dtype=np.int64)
     V_global = W.shape[0] if V_global is None else V_global
     valid = target != ignore_index
-    z = scaled_logits(h, Wr, logit_scale)                      # [N, |vr|]
+    z = scaled_logits(h, Wr, logit_scale, None if bias is None else _f64(bias)[vr])
     # column index of the target among the selected vocab rows (or -1)
     gcol = vocab_start + vr
     pos = {int(v): i for i, v in enumerate(gcol)}
     tc = np.array([pos.get(int(y), -1) if ok else -1 for y, ok in zip(target, valid)])
     g = dlogits(z, lse_all, tc, p_mask, valid, D, label_smoothing, logit_scale, V_global)
+    if with_db:
+        return g.T @ h, g.sum(axis=0)
     return g.T @ h
 
 

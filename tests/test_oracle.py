@@ -302,3 +302,148 @@ def test_out_of_range_target_rejected():
     y[1] = 5
     with pytest.raises(ValueError):
         O.forward_backward(h, W, y, p)
+
+
+# ------------------------- page 1's bias, EOB weight and upstream gradient
+def test_bias_is_an_extra_input_column():
+    """h W^T + b equals [h, 1] [W, b]^T, so the bias path must reproduce the
+    bias-free oracle on augmented inputs, and db must be the gradient of the
+    appended weight column (g^T 1 = column sums of g)."""
+    h, W, y, p = _problem(N=9, H=5, V=13, seed=21, n_ignored=3)
+    b = np.random.default_rng(22).standard_normal(13)
+    kw = dict(label_smoothing=0.2, logit_scale=0.7, reduction="mean")
+    r = O.forward_backward(h, W, y, p, bias=b, **kw)
+    ha = np.concatenate([h, np.ones((9, 1))], axis=1)
+    Wa = np.concatenate([W, b[:, None]], axis=1)
+    ra = O.forward_backward(ha, Wa, y, p, **kw)
+    assert r["loss"] == pytest.approx(ra["loss"], rel=1e-14)
+    np.testing.assert_allclose(r["dH"], ra["dH"][:, :5], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(r["dW"], ra["dW"][:, :5], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(r["db"], ra["dW"][:, 5], rtol=1e-12, atol=1e-15)
+    assert O.forward_backward(h, W, y, p, **kw)["db"] is None
+
+
+@pytest.mark.parametrize("eps,s,red", [(0.0, 1.0, "mean"), (0.1, 0.5, "sum")])
+def test_bias_finite_differences(eps, s, red):
+    h, W, y, p = _problem(N=5, H=3, V=7, seed=23, n_ignored=1)
+    b = np.random.default_rng(24).standard_normal(7) * 0.5
+    kw = dict(label_smoothing=eps, logit_scale=s, reduction=red)
+    r = O.forward_backward(h, W, y, p, bias=b, **kw)
+    d = 1e-6
+    num = np.zeros(7)
+    for j in range(7):
+        bp, bm = b.copy(), b.copy()
+        bp[j] += d
+        bm[j] -= d
+        num[j] = (_loss(h, W, y, p, bias=bp, **kw) - _loss(h, W, y, p, bias=bm, **kw)) / (2 * d)
+    np.testing.assert_allclose(r["db"], num, rtol=1e-6, atol=1e-8)
+
+
+def test_bias_matches_torch_linear_cross_entropy():
+    torch = pytest.importorskip("torch")
+    h, W, y, _ = _problem(N=12, H=6, V=40, seed=25, n_ignored=4)
+    b = np.random.default_rng(26).standard_normal(40)
+    r = O.forward_backward(h, W, y, np.ones(12), bias=b, label_smoothing=0.1,
+                           logit_scale=0.5, reduction="mean")
+    ht = torch.tensor(h, requires_grad=True)
+    Wt = torch.tensor(W, requires_grad=True)
+    bt = torch.tensor(b, requires_grad=True)
+    lt = torch.nn.functional.cross_entropy(0.5 * torch.nn.functional.linear(ht, Wt, bt),
+                                           torch.tensor(y), ignore_index=-100,
+                                           label_smoothing=0.1, reduction="mean")
+    lt.backward()
+    assert r["loss"] == pytest.approx(lt.item(), rel=1e-13)
+    np.testing.assert_allclose(r["dH"], ht.grad.numpy(), rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(r["dW"], Wt.grad.numpy(), rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(r["db"], bt.grad.numpy(), rtol=1e-11, atol=1e-14)
+
+
+@pytest.mark.parametrize("w", [2.5, 0.0])
+def test_eob_weight_scales_eob_rows(w):
+    """EOB rows' loss is multiplied by the weight: with p = 1 it is torch's
+    unreduced CE weighted per row, summed and divided by the non-ignored
+    count; the divisor still counts the EOB rows."""
+    torch = pytest.importorskip("torch")
+    h, W, y, _ = _problem(N=14, H=6, V=20, seed=27, n_ignored=3)
+    eob = 5
+    y[[1, 4, 9]] = np.where(y[[1, 4, 9]] == -100, -100, eob)
+    y[[2, 11]] = eob
+    kw = dict(label_smoothing=0.1, logit_scale=0.8, reduction="mean")
+    r = O.forward_backward(h, W, y, np.ones(14), eob_token_id=eob, eob_weight=w, **kw)
+    ht = torch.tensor(h, requires_grad=True)
+    Wt = torch.tensor(W, requires_grad=True)
+    ce = torch.nn.functional.cross_entropy(0.8 * (ht @ Wt.T), torch.tensor(y), ignore_index=-100,
+                                           label_smoothing=0.1, reduction="none")
+    wt = torch.tensor(np.where(y == eob, w, 1.0))
+    lt = (ce * wt).sum() / float(np.count_nonzero(y != -100))
+    lt.backward()
+    assert r["loss"] == pytest.approx(lt.item(), rel=1e-13)
+    np.testing.assert_allclose(r["dH"], ht.grad.numpy(), rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(r["dW"], Wt.grad.numpy(), rtol=1e-11, atol=1e-14)
+
+
+def test_eob_weight_one_or_absent_changes_nothing():
+    h, W, y, p = _problem(N=8, H=4, V=9, seed=28, n_ignored=2)
+    y[3] = 4
+    base = O.forward_backward(h, W, y, p)
+    for kw in (dict(eob_token_id=4, eob_weight=1.0), dict(eob_token_id=None, eob_weight=3.0)):
+        r = O.forward_backward(h, W, y, p, **kw)
+        assert r["loss"] == base["loss"]
+        assert np.array_equal(r["dH"], base["dH"]) and np.array_equal(r["dW"], base["dW"])
+
+
+def test_scale_grads_follows_the_chain_rule():
+    """Gradients of do * loss by central differences equal scale_grads(do, ...)
+    of the unit-upstream gradients; do = 1 returns them untouched."""
+    h, W, y, p = _problem(N=4, H=3, V=6, seed=29, n_ignored=1)
+    b = np.random.default_rng(30).standard_normal(6)
+    r = O.forward_backward(h, W, y, p, bias=b)
+    same = O.scale_grads(1.0, r["dH"], r["dW"], r["db"])
+    assert all(a is c for a, c in zip(same, (r["dH"], r["dW"], r["db"])))
+    do = -1.75
+    dH, dW, db = O.scale_grads(do, r["dH"], r["dW"], r["db"])
+    d = 1e-6
+    num = np.zeros_like(W)
+    for idx in np.ndindex(*W.shape):
+        Wp, Wm = W.copy(), W.copy()
+        Wp[idx] += d
+        Wm[idx] -= d
+        num[idx] = do * (_loss(h, Wp, y, p, bias=b) - _loss(h, Wm, y, p, bias=b)) / (2 * d)
+    np.testing.assert_allclose(dW, num, rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(dH, do * r["dH"], rtol=1e-15)
+    np.testing.assert_allclose(db, do * r["db"], rtol=1e-15)
+    assert O.scale_grads(2.0, None)[0] is None
+
+
+def test_forward_only_closed_form_and_library():
+    """The forward-only entry: W = 0 closed form (lse = log V, loss = log V
+    sum(1/p)/D) and torch's cross-entropy for p = 1."""
+    torch = pytest.importorskip("torch")
+    h, W, y, p = _problem(N=10, H=5, V=11, seed=31, n_ignored=3)
+    r0 = O.forward(h, np.zeros_like(W), y, p, reduction="sum")
+    np.testing.assert_allclose(r0["lse"], math.log(11), rtol=1e-15)
+    valid = y != -100
+    assert r0["loss"] == pytest.approx(math.log(11) * np.sum(1 / p[valid]), rel=1e-14)
+    r = O.forward(h, W, y, np.ones(10), label_smoothing=0.05, logit_scale=1.3, reduction="mean")
+    lt = torch.nn.functional.cross_entropy(1.3 * torch.tensor(h @ W.T), torch.tensor(y),
+                                           ignore_index=-100, label_smoothing=0.05)
+    assert r["loss"] == pytest.approx(lt.item(), rel=1e-13)
+    np.testing.assert_allclose(r["lse"], torch.logsumexp(1.3 * torch.tensor(h @ W.T), 1).numpy(),
+                               rtol=1e-14)
+
+
+def test_sampled_helpers_with_bias():
+    N, H, V = 20, 5, 30
+    h, W, y, p = _problem(N=N, H=H, V=V, seed=32, n_ignored=6)
+    b = np.random.default_rng(33).standard_normal(V)
+    full = O.forward_backward(h, W, y, p, bias=b, label_smoothing=0.1, logit_scale=0.5,
+                              reduction="sum")
+    rows = [1, 8, 19]
+    lse, _, _ = O.row_stats(h, W, y, rows, 0.5, bias=b)
+    np.testing.assert_allclose(lse, full["lse"][rows], rtol=1e-14)
+    np.testing.assert_allclose(O.dH_rows(h, W, y, p, lse, rows, 1.0, 0.1, 0.5, bias=b),
+                               full["dH"][rows], rtol=1e-12, atol=1e-15)
+    vr = [0, 13, 29]
+    dw, db = O.dW_rows(h, W, y, p, full["lse"], vr, 1.0, 0.1, 0.5, bias=b, with_db=True)
+    np.testing.assert_allclose(dw, full["dW"][vr], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(db, full["db"][vr], rtol=1e-12, atol=1e-15)
