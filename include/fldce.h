@@ -11,7 +11,7 @@
  * functions fused_linear_cross_entropy_forward, logsumexp_fwd and
  * cross_entropy_kernel, steps 4-6):
  *
- *   z      = s * (h W^T)                             logits, s = logit_scale
+ *   z      = s * (h W^T [+ b])                       logits, s = logit_scale
  *   lse_i  = log sum_j exp(z_ij)                     stable row logsumexp
  *   l_i    = [(1-eps)(lse_i - z_{i,y_i}) + eps(lse_i - mean_j z_ij)] / p_i
  *            (0 when y_i == ignore_index)            eps = label_smoothing
@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define FLDCE_VERSION 1
+#define FLDCE_VERSION 2
 
 enum fldce_dtype { FLDCE_DTYPE_F32 = 0, FLDCE_DTYPE_BF16 = 1 };
 
@@ -135,6 +135,74 @@ int fldce_fwd_bwd(const void* h, const void* W, const int64_t* target,
                   float* loss, void* dH, void* dW, float* row_lse,
                   float* row_loss, int64_t chunk_rows, void* workspace,
                   size_t workspace_bytes, void* stream);
+
+/*
+ * fldce_fwd_bwd with the rest of page 1's interface: the optional bias of
+ * fused_linear_cross_entropy_forward (F.linear(x, weight, bias)) and its
+ * gradient db, and the end-of-block weight of the module's forward
+ * (FusedLinearDiffusionCrossEntropyLoss.forward).
+ *
+ *   bias         [V]   dtype       optional (NULL = none): the logits become
+ *                                  z = s (h W^T + b)
+ *   db           [V]   dtype       optional out (NULL = not computed):
+ *                                  sum_i g_i, float32 accumulation over the
+ *                                  rows in a fixed order, rounded once;
+ *                                  allowed without a bias
+ *   eob_token_id     rows whose target equals it get their loss and
+ *                    gradient multiplied by eob_weight (the page divides
+ *                    their p_mask by the weight); < 0 = no such weighting
+ *   eob_weight       finite and >= 0 (checked only when eob_token_id >= 0)
+ *
+ * Every other argument is as in fldce_fwd_bwd, which equals this call with
+ * bias = db = NULL and eob_token_id = -1.  Workspace: fldce_workspace_size.
+ */
+int fldce_fwd_bwd_ex(const void* h, const void* W, const void* bias,
+                     const int64_t* target, const float* p_mask, int64_t N,
+                     int64_t H, int64_t V, int dtype, int64_t ignore_index,
+                     float label_smoothing, float logit_scale, int reduction,
+                     int64_t total, int64_t eob_token_id, float eob_weight,
+                     float* loss, void* dH, void* dW, void* db,
+                     float* row_lse, float* row_loss, int64_t chunk_rows,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace fldce_fwd needs. */
+size_t fldce_fwd_workspace_size(int64_t N, int64_t H, int64_t V, int dtype);
+
+/*
+ * Forward only (evaluation): the loss and optionally the per-row lse and
+ * loss, no gradient -- the forward half of page 1's chunk loop (F.linear,
+ * logsumexp_fwd and the loss part of cross_entropy_kernel).  The [N, V]
+ * logits are never written to memory on the bf16 path, which also skips
+ * rows whose target is ignore_index (their row_lse and row_loss are 0).
+ * Arguments as in fldce_fwd_bwd_ex.
+ */
+int fldce_fwd(const void* h, const void* W, const void* bias,
+              const int64_t* target, const float* p_mask, int64_t N, int64_t H,
+              int64_t V, int dtype, int64_t ignore_index,
+              float label_smoothing, float logit_scale, int reduction,
+              int64_t total, int64_t eob_token_id, float eob_weight,
+              float* loss, float* row_lse, float* row_loss, void* workspace,
+              size_t workspace_bytes, void* stream);
+
+/*
+ * Upstream-gradient scaling (page 1, fused_linear_cross_entropy_backward):
+ * the gradients above are for d(loss) = 1; a caller that receives the
+ * upstream gradient `do` later multiplies them by it, in place.  *grad_out
+ * is read on the device (no host sync): when it equals 1 the kernels return
+ * without touching the gradients (the page skips the multiply too),
+ * otherwise every element becomes dtype(float(x) * do), rounded to nearest
+ * even for bf16.
+ *
+ *   grad_out     [1]   float32     do, device memory
+ *   dH, dW, db         dtype       n_dH, n_dW, n_db elements each, scaled in
+ *                                  place; a NULL pointer (with n = 0) is
+ *                                  skipped
+ *
+ * Pointers must be 16-byte aligned; counts >= 0.
+ */
+int fldce_scale_grads(const float* grad_out, int dtype, void* dH, int64_t n_dH,
+                      void* dW, int64_t n_dW, void* db, int64_t n_db,
+                      void* stream);
 
 /* Bytes of workspace fldce_shard_partials needs. */
 size_t fldce_shard_partials_workspace_size(int64_t N, int64_t H,

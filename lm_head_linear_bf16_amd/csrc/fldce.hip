@@ -31,7 +31,7 @@ using namespace fldce;
 
 namespace {
 
-enum Mode { kFwdBwd = 0, kShardPartials = 1, kShardBwd = 2 };
+enum Mode { kFwdBwd = 0, kShardPartials = 1, kShardBwd = 2, kFwd = 3 };
 
 constexpr int64_t kZBudgetBytes = int64_t(16) << 30;  // chunk logits + g^T buffers
 constexpr int kGroupM = 4;
@@ -42,7 +42,8 @@ struct Plan {
   int splits = 1;
   size_t oD = 0, oWT = 0, oColpart = 0, oWsum = 0, oZt = 0, oR = 0, oLse = 0, oRloss = 0,
          oCoef = 0, oPart = 0, oRpart = 0, oZ = 0, oG = 0, oGT = 0, oHT = 0, oDHpart = 0,
-         oDW32 = 0, oRows = 0, oCount = 0, oLsec = 0, oTcol = 0;
+         oDW32 = 0, oRows = 0, oCount = 0, oLsec = 0, oTcol = 0, oBsum = 0, oDbpart = 0;
+  int64_t db_blocks = 0;  // row blocks of db partials (64 rows each, over all chunks)
   size_t total = 0;
 };
 
@@ -69,7 +70,7 @@ Plan make_plan(int mode, int64_t N, int64_t H, int64_t V, int dtype, int64_t chu
   p.Vp = round_up(V, 64);
   p.nT = cdiv(V, 128);
   const bool bf = dtype == FLDCE_DTYPE_BF16;
-  if (mode == kShardPartials && bf) {
+  if ((mode == kShardPartials || mode == kFwd) && bf) {
     p.C = std::max<int64_t>(N, 1);  // logits never stored: one pass over all rows
   } else {
     p.C = chunk_rows > 0 ? std::min<int64_t>(chunk_rows, std::max<int64_t>(N, 1))
@@ -83,9 +84,19 @@ Plan make_plan(int mode, int64_t N, int64_t H, int64_t V, int dtype, int64_t chu
   p.oRows = take(cur, (size_t)std::max<int64_t>(N, 1) * 4);  // compacted row indices
   p.oColpart = take(cur, (size_t)cdiv(V, kColSlab) * H * 4);
   p.oWsum = take(cur, (size_t)H * 4);
+  p.oBsum = take(cur, 256);
   p.oPart = take(cur, (size_t)p.nT * p.C * 8);
   p.oRpart = take(cur, (size_t)p.nT * p.C * 4);  // per-slab row sums of z (label smoothing)
   if (mode == kShardPartials) {
+    if (!bf) p.oZ = take(cur, (size_t)p.C * p.Vp * 4);
+    p.total = cur;
+    return p;
+  }
+  if (mode == kFwd) {
+    p.oZt = take(cur, (size_t)N * 4);
+    p.oR = take(cur, (size_t)N * 4);
+    p.oLse = take(cur, (size_t)N * 4);
+    p.oRloss = take(cur, (size_t)N * 4);
     if (!bf) p.oZ = take(cur, (size_t)p.C * p.Vp * 4);
     p.total = cur;
     return p;
@@ -105,6 +116,10 @@ Plan make_plan(int mode, int64_t N, int64_t H, int64_t V, int dtype, int64_t chu
     p.oGT = take(cur, (size_t)p.Vp * p.Cp * p.esz);
   }
   p.oHT = take(cur, (size_t)H * p.Cp * p.esz);
+  if (mode == kFwdBwd) {  // db partials: bf16 per 64 rows of a chunk, fp32 per kColSlab rows
+    p.db_blocks = cdiv(std::max<int64_t>(N, 1), 64) + p.nchunks;
+    p.oDbpart = take(cur, (size_t)p.db_blocks * p.Vp * 4);
+  }
   if (bf) {
     const int64_t tiles = cdiv(p.C, kBM) * cdiv(H, kBN);
     p.splits = choose_splits(tiles, p.Vp / kBK, 8);
@@ -215,19 +230,20 @@ void launch_colsum(const T* W, int64_t V, int64_t H, float* colpart, float* wsum
     if (H % 8 == 0) {
       dim3 g((unsigned)cdiv(V, kColSlab), (unsigned)cdiv(H, 256 * 8));
       k_colsum_slabs_bf16<<<g, 256, 0, st>>>(W, V, H, colpart);
-      k_colsum_finish<<<grid1(H, 256), 256, 0, st>>>(colpart, cdiv(V, kColSlab), H, wsum);
+      k_colsum_finish<float><<<grid1(H, 256), 256, 0, st>>>(colpart, cdiv(V, kColSlab), H, H, wsum);
       return;
     }
   }
   dim3 g((unsigned)cdiv(V, kColSlab), (unsigned)cdiv(H, 256));
   k_colsum_slabs<T><<<g, 256, 0, st>>>(W, V, H, colpart);
-  k_colsum_finish<<<grid1(H, 256), 256, 0, st>>>(colpart, cdiv(V, kColSlab), H, wsum);
+  k_colsum_finish<float><<<grid1(H, 256), 256, 0, st>>>(colpart, cdiv(V, kColSlab), H, H, wsum);
 }
 
 // Everything of the gradient path that fwd_bwd and shard_bwd share.
 struct Core {
   const void* h;
   const void* W;
+  const void* bias;      // [V] or nullptr
   const int64_t* target;
   const float* p_mask;
   int64_t N, H, V, v0, Vg;
@@ -246,6 +262,10 @@ struct Core {
   void* dH;              // [N, H]: h dtype (fwd_bwd) or fp32 (shard)
   bool dH_f32;
   void* dW;              // [V, H] W dtype
+  void* db;              // [V] W dtype or nullptr (fwd_bwd)
+  float* dbpart;         // db partials [db_blocks, Vp] when db != nullptr
+  int64_t eob;           // end-of-block token (< 0: none) and its weight
+  float eob_w;
 };
 
 // per-row stage of a chunk: lse/loss/coefficients (fwd_bwd) or coefficients
@@ -257,13 +277,13 @@ const float* run_rows(const Core& c, const Plan& p, const floatx2* part, float* 
   if (c.lse_in == nullptr) {
     k_combine_rows<<<grid1(cmax, 32), 256, 0, st>>>(
         part, c.rpart, p.C, p.nT, cmax, c.rows, c.count, c0, 0, c.target, c.p_mask, c.ignore,
-        c.zt, c.R, c.eps, (float)c.Vg, c.s, c.D, c.lse_out, c.rloss_out, coef, lsec, tcol, c.v0,
-        nullptr, nullptr, nullptr);
+        c.zt, c.R, c.eps, (float)c.Vg, c.s, c.D, c.eob, c.eob_w, c.lse_out, c.rloss_out, coef,
+        lsec, tcol, c.v0, nullptr, nullptr, nullptr);
     return c.lse_out + c0;
   }
   k_coef_rows<<<grid1(cmax, 256), 256, 0, st>>>(c.target, c.p_mask, c.ignore, cmax, c.rows,
-                                                 c.count, c0, c.s, c.D, coef, c.lse_in, lsec, tcol,
-                                                 c.v0);
+                                                 c.count, c0, c.s, c.D, c.eob, c.eob_w, coef,
+                                                 c.lse_in, lsec, tcol, c.v0);
   return c.lse_in + c0;
 }
 
@@ -282,7 +302,9 @@ int run_core_bf16(const Core& c, const Plan& p, char* ws, hipStream_t st) {
   float* dW32 = reinterpret_cast<float*>(ws + p.oDW32);
   const bf16* h = static_cast<const bf16*>(c.h);
   const bf16* W = static_cast<const bf16*>(c.W);
+  const bf16* bias = static_cast<const bf16*>(c.bias);
   const int64_t H = c.H, V = c.V, Vp = p.Vp;
+  int64_t db_off = 0;  // row blocks of db partials written so far
   {
     StageTimer tm(kPrep, st);
     if (c.dH_f32)
@@ -306,12 +328,12 @@ int run_core_bf16(const Core& c, const Plan& p, char* ws, hipStream_t st) {
       const int blocks = (int)(cdiv(V, kBM) * cdiv(cmax, kBN));
       if (c.lse_in == nullptr)
         k_logits_bf16<true, true><<<blocks, kGemmThreads, kGemmLds, st>>>(
-            W, h, (int)V, (int)cmax, (int)H, c.s, c.rows, c.count, c0, part, c.rpart, p.C, zb, Vp,
-            kGroupM);
+            W, bias, h, (int)V, (int)cmax, (int)H, c.s, c.rows, c.count, c0, part, c.rpart, p.C,
+            zb, Vp, kGroupM);
       else
         k_logits_bf16<true, false><<<blocks, kGemmThreads, kGemmLds, st>>>(
-            W, h, (int)V, (int)cmax, (int)H, c.s, c.rows, c.count, c0, part, nullptr, p.C, zb, Vp,
-            kGroupM);
+            W, bias, h, (int)V, (int)cmax, (int)H, c.s, c.rows, c.count, c0, part, nullptr, p.C,
+            zb, Vp, kGroupM);
     }
     // 2. per-row combine
     run_rows(c, p, part, coef, lsec, tcol, c0, cmax, st);
@@ -319,7 +341,9 @@ int run_core_bf16(const Core& c, const Plan& p, char* ws, hipStream_t st) {
       StageTimer tm(kDlogits, st);
       dim3 g((unsigned)cdiv(Vp, kGpassCols), (unsigned)(Cpc / 64));
       k_gpass_blk<<<g, 256, 0, st>>>(zb, Vp, cmax, c.count, c0, V, lsec, coef, tcol, c.eps,
-                                     (float)c.Vg, gb);
+                                     (float)c.Vg, gb,
+                                     c.db != nullptr ? c.dbpart + db_off * Vp : nullptr);
+      db_off += Cpc / 64;
     }
     {  // 4. dH = g W (split over the vocabulary, ordered reduction, scattered rows)
       const int S = p.splits;
@@ -349,6 +373,10 @@ int run_core_bf16(const Core& c, const Plan& p, char* ws, hipStream_t st) {
                                                    p.Cp, (int)H, (bf16*)c.dW, dW32, kGroupM);
     }
   }
+  if (c.db != nullptr) {
+    StageTimer tm(kDWGemm, st);
+    k_colsum_finish<bf16><<<grid1(V, 256), 256, 0, st>>>(c.dbpart, db_off, Vp, V, (bf16*)c.db);
+  }
   return launch_status();
 }
 
@@ -363,6 +391,7 @@ int run_core_f32(const Core& c, const Plan& p, char* ws, hipStream_t st) {
   const float* h = static_cast<const float*>(c.h);
   const float* W = static_cast<const float*>(c.W);
   const int64_t H = c.H, V = c.V, Vp = p.Vp;
+  int64_t db_off = 0;  // slabs of db partials written so far
   {
     StageTimer tm(kPrep, st);
     launch_transpose<float>(W, V, H, H, WT, Vp, Vp, st);
@@ -380,6 +409,9 @@ int run_core_f32(const Core& c, const Plan& p, char* ws, hipStream_t st) {
       StageTimer tm(kLogits, st);
       dim3 g((unsigned)cdiv(V, 64), (unsigned)cdiv(Cc, 64));
       k_gemm_f32_nt<<<g, 256, 0, st>>>(hc, H, Cc, W, H, V, H, c.s, zb, Vp, 0);
+      if (c.bias != nullptr)
+        k_add_bias_f32<<<dim3((unsigned)cdiv(V, 256), (unsigned)std::min<int64_t>(Cc, 256)), 256, 0,
+                         st>>>(zb, Vp, Cc, V, (const float*)c.bias, c.s);
       if (c.lse_in == nullptr) {
         dim3 g2((unsigned)cdiv(Cc, 64), (unsigned)p.nT);
         k_row_partials_f32<<<g2, 64, 0, st>>>(zb, Vp, Cc, V, part, p.C);
@@ -391,6 +423,11 @@ int run_core_f32(const Core& c, const Plan& p, char* ws, hipStream_t st) {
       dim3 g((unsigned)(Vp / 64), (unsigned)(Cpc / 64));
       k_gpass<float><<<g, 256, 0, st>>>(zb, Vp, Cc, V, lse_c, coef, c.target + c0, c.v0, c.eps,
                                         (float)c.Vg, gT, p.Cp);
+      if (c.db != nullptr) {  // column sums of g (now in zb), per kColSlab rows
+        dim3 g2((unsigned)cdiv(Cc, kColSlab), (unsigned)cdiv(Vp, 256));
+        k_colsum_slabs<float><<<g2, 256, 0, st>>>(zb, Cc, Vp, c.dbpart + db_off * Vp);
+        db_off += cdiv(Cc, kColSlab);
+      }
     }
     {
       StageTimer tm(kDHGemm, st);
@@ -403,6 +440,10 @@ int run_core_f32(const Core& c, const Plan& p, char* ws, hipStream_t st) {
       k_gemm_f32_nt<<<g, 256, 0, st>>>(gT, p.Cp, V, hT, p.Cp, H, Cpc, 1.f, (float*)c.dW, H,
                                        ic == 0 ? 0 : 1);
     }
+  }
+  if (c.db != nullptr) {
+    StageTimer tm(kDWGemm, st);
+    k_colsum_finish<float><<<grid1(V, 256), 256, 0, st>>>(c.dbpart, db_off, Vp, V, (float*)c.db);
   }
   return launch_status();
 }
@@ -418,6 +459,37 @@ void zero_fill(void* p, int64_t n_elems, int esz, hipStream_t st) {
     k_fill_u16<<<g, 256, 0, st>>>(static_cast<uint16_t*>(p), n_elems, 0);
   else
     k_fill_f32<<<g, 256, 0, st>>>(static_cast<float*>(p), n_elems, 0.f);
+}
+
+// Shared argument checks of the loss entry points.
+int check_loss_args(int reduction, float label_smoothing, int64_t eob, float eob_w) {
+  if (reduction != FLDCE_REDUCTION_SUM && reduction != FLDCE_REDUCTION_MEAN)
+    return FLDCE_ERR_BAD_ARGUMENT;
+  if (!(label_smoothing >= 0.f && label_smoothing <= 1.f)) return FLDCE_ERR_BAD_ARGUMENT;
+  if (eob >= 0 && !(eob_w >= 0.f && std::isfinite(eob_w))) return FLDCE_ERR_BAD_ARGUMENT;
+  return FLDCE_OK;
+}
+
+// Target logits and row sums of z for every row (prep of fwd_bwd and fwd):
+// bf16 takes the row sums from the logits epilogue (rpart), fp32 from
+// <h_i, sum_j W_j> (+ sum_j b_j).
+void launch_row_dots(const void* h, const void* W, const void* bias, const int64_t* target,
+                     int64_t N, int64_t H, int64_t V, bool bf, int64_t ignore, float s, bool smooth,
+                     float* colpart, float* wsum, float* bsum, float* zt, float* R, hipStream_t st) {
+  if (bf) {
+    k_rowdot<bf16><<<grid1(N, 4), 256, 0, st>>>((const bf16*)h, (const bf16*)W, (const bf16*)bias,
+                                                 H, target, 0, V, ignore, s, nullptr, nullptr, N,
+                                                 zt, nullptr);
+    return;
+  }
+  if (smooth) {
+    launch_colsum<float>((const float*)W, V, H, colpart, wsum, st);
+    if (bias != nullptr) launch_colsum<float>((const float*)bias, V, 1, colpart, bsum, st);
+  }
+  k_rowdot<float><<<grid1(N, 4), 256, 0, st>>>(
+      (const float*)h, (const float*)W, (const float*)bias, H, target, 0, V, ignore, s,
+      smooth ? wsum : nullptr, (smooth && bias != nullptr) ? bsum : nullptr, N, zt,
+      smooth ? R : nullptr);
 }
 
 }  // namespace
@@ -468,15 +540,27 @@ int fldce_fwd_bwd(const void* h, const void* W, const int64_t* target, const flo
                   float label_smoothing, float logit_scale, int reduction, int64_t total,
                   float* loss, void* dH, void* dW, float* row_lse, float* row_loss,
                   int64_t chunk_rows, void* workspace, size_t workspace_bytes, void* stream) {
+  return fldce_fwd_bwd_ex(h, W, nullptr, target, p_mask, N, H, V, dtype, ignore_index,
+                          label_smoothing, logit_scale, reduction, total, -1, 1.f, loss, dH, dW,
+                          nullptr, row_lse, row_loss, chunk_rows, workspace, workspace_bytes,
+                          stream);
+}
+
+int fldce_fwd_bwd_ex(const void* h, const void* W, const void* bias, const int64_t* target,
+                     const float* p_mask, int64_t N, int64_t H, int64_t V, int dtype,
+                     int64_t ignore_index, float label_smoothing, float logit_scale,
+                     int reduction, int64_t total, int64_t eob_token_id, float eob_weight,
+                     float* loss, void* dH, void* dW, void* db, float* row_lse, float* row_loss,
+                     int64_t chunk_rows, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_common(h, W, target, N, H, V, dtype, logit_scale);
   if (rc != FLDCE_OK) return rc;
   if (!loss || !dW || (N > 0 && !dH)) return FLDCE_ERR_NULL_POINTER;
-  if (reduction != FLDCE_REDUCTION_SUM && reduction != FLDCE_REDUCTION_MEAN)
-    return FLDCE_ERR_BAD_ARGUMENT;
-  if (!(label_smoothing >= 0.f && label_smoothing <= 1.f)) return FLDCE_ERR_BAD_ARGUMENT;
+  rc = check_loss_args(reduction, label_smoothing, eob_token_id, eob_weight);
+  if (rc != FLDCE_OK) return rc;
   if (chunk_rows < 0) return FLDCE_ERR_BAD_ARGUMENT;
-  if (!aligned16(h) || !aligned16(W) || !aligned16(target) || !aligned16(p_mask) || !aligned16(dH) ||
-      !aligned16(dW) || !aligned16(workspace))
+  if (!aligned16(h) || !aligned16(W) || !aligned16(bias) || !aligned16(target) ||
+      !aligned16(p_mask) || !aligned16(dH) || !aligned16(dW) || !aligned16(db) ||
+      !aligned16(workspace))
     return FLDCE_ERR_ALIGNMENT;
   const Plan p = make_plan(kFwdBwd, N, H, V, dtype, chunk_rows);
   if (!workspace || workspace_bytes < p.total) return FLDCE_ERR_WORKSPACE;
@@ -488,11 +572,13 @@ int fldce_fwd_bwd(const void* h, const void* W, const int64_t* target, const flo
   if (N == 0) {
     zero_fill(loss, 1, 4, st);
     zero_fill(dW, V * H, esz, st);
+    if (db != nullptr) zero_fill(db, V, esz, st);
     return launch_status();
   }
   const bool smooth = label_smoothing > 0.f;
   float* colpart = reinterpret_cast<float*>(ws + p.oColpart);
   float* wsum = reinterpret_cast<float*>(ws + p.oWsum);
+  float* bsum = reinterpret_cast<float*>(ws + p.oBsum);
   float* zt = reinterpret_cast<float*>(ws + p.oZt);
   float* R = reinterpret_cast<float*>(ws + p.oR);
   float* lse = row_lse ? row_lse : reinterpret_cast<float*>(ws + p.oLse);
@@ -502,9 +588,11 @@ int fldce_fwd_bwd(const void* h, const void* W, const int64_t* target, const flo
   // row sums of z: bf16 from the logits epilogue, fp32 from <h_i, sum_j W_j>
   int* rows = reinterpret_cast<int*>(ws + p.oRows);
   int* count = reinterpret_cast<int*>(ws + p.oCount);
-  Core c{h, W, target, p_mask, N, H, V, 0, V, dtype, ignore_index, label_smoothing, logit_scale,
-         nullptr, lse, rl, zt, (smooth && !bf) ? R : nullptr, (smooth && bf) ? rpart : nullptr, D,
-         bf ? rows : nullptr, bf ? count : nullptr, dH, false, dW};
+  float* dbpart = reinterpret_cast<float*>(ws + p.oDbpart);
+  Core c{h, W, bias, target, p_mask, N, H, V, 0, V, dtype, ignore_index, label_smoothing,
+         logit_scale, nullptr, lse, rl, zt, (smooth && !bf) ? R : nullptr,
+         (smooth && bf) ? rpart : nullptr, D, bf ? rows : nullptr, bf ? count : nullptr, dH,
+         false, dW, db, dbpart, eob_token_id, eob_weight};
   {
     StageTimer tm(kPrep, st);
     k_divisor<<<1, 1024, 0, st>>>(target, N, ignore_index, reduction, total, D);
@@ -512,22 +600,132 @@ int fldce_fwd_bwd(const void* h, const void* W, const int64_t* target, const flo
       k_compact_rows<<<1, 1024, 0, st>>>(target, N, ignore_index, rows, count);
       k_ignored_rows_init<<<grid1(N, 256), 256, 0, st>>>(target, N, ignore_index, lse, 0.f, rl, 0.f,
                                                          nullptr, 0.f);
-      k_rowdot<bf16><<<grid1(N, 4), 256, 0, st>>>((const bf16*)h, (const bf16*)W, H, target, 0,
-                                                   V, ignore_index, logit_scale, nullptr, N, zt,
-                                                   nullptr);
-    } else {
-      if (smooth) launch_colsum<float>((const float*)W, V, H, colpart, wsum, st);
-      k_rowdot<float><<<grid1(N, 4), 256, 0, st>>>((const float*)h, (const float*)W, H, target,
-                                                    0, V, ignore_index, logit_scale,
-                                                    smooth ? wsum : nullptr, N, zt,
-                                                    smooth ? R : nullptr);
     }
+    launch_row_dots(h, W, bias, target, N, H, V, bf, ignore_index, logit_scale, smooth, colpart,
+                    wsum, bsum, zt, R, st);
   }
   rc = run_core(c, p, ws, st);
   if (rc != FLDCE_OK) return rc;
   {
     StageTimer tm(kLoss, st);
     k_loss_reduce<<<1, 1024, 0, st>>>(rl, N, D, loss);
+  }
+  return launch_status();
+}
+
+size_t fldce_fwd_workspace_size(int64_t N, int64_t H, int64_t V, int dtype) {
+  if (N < 0 || H <= 0 || V <= 0 || (dtype != 0 && dtype != 1)) return 0;
+  return make_plan(kFwd, N, H, V, dtype, 0).total;
+}
+
+int fldce_fwd(const void* h, const void* W, const void* bias, const int64_t* target,
+              const float* p_mask, int64_t N, int64_t H, int64_t V, int dtype,
+              int64_t ignore_index, float label_smoothing, float logit_scale, int reduction,
+              int64_t total, int64_t eob_token_id, float eob_weight, float* loss, float* row_lse,
+              float* row_loss, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_common(h, W, target, N, H, V, dtype, logit_scale);
+  if (rc != FLDCE_OK) return rc;
+  if (!loss) return FLDCE_ERR_NULL_POINTER;
+  rc = check_loss_args(reduction, label_smoothing, eob_token_id, eob_weight);
+  if (rc != FLDCE_OK) return rc;
+  if (!aligned16(h) || !aligned16(W) || !aligned16(bias) || !aligned16(target) ||
+      !aligned16(p_mask) || !aligned16(workspace))
+    return FLDCE_ERR_ALIGNMENT;
+  const Plan p = make_plan(kFwd, N, H, V, dtype, 0);
+  if (!workspace || workspace_bytes < p.total) return FLDCE_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  set_gemm_attributes();
+  if (N == 0) {
+    zero_fill(loss, 1, 4, st);
+    return launch_status();
+  }
+  char* ws = static_cast<char*>(workspace);
+  float* D = reinterpret_cast<float*>(ws + p.oD);
+  const bool smooth = label_smoothing > 0.f;
+  const bool bf = dtype == FLDCE_DTYPE_BF16;
+  float* colpart = reinterpret_cast<float*>(ws + p.oColpart);
+  float* wsum = reinterpret_cast<float*>(ws + p.oWsum);
+  float* bsum = reinterpret_cast<float*>(ws + p.oBsum);
+  float* zt = reinterpret_cast<float*>(ws + p.oZt);
+  float* R = reinterpret_cast<float*>(ws + p.oR);
+  float* lse = row_lse ? row_lse : reinterpret_cast<float*>(ws + p.oLse);
+  float* rl = row_loss ? row_loss : reinterpret_cast<float*>(ws + p.oRloss);
+  floatx2* part = reinterpret_cast<floatx2*>(ws + p.oPart);
+  float* rpart = reinterpret_cast<float*>(ws + p.oRpart);
+  int* rows = reinterpret_cast<int*>(ws + p.oRows);
+  int* count = reinterpret_cast<int*>(ws + p.oCount);
+  {
+    StageTimer tm(kPrep, st);
+    k_divisor<<<1, 1024, 0, st>>>(target, N, ignore_index, reduction, total, D);
+    if (bf) {
+      k_compact_rows<<<1, 1024, 0, st>>>(target, N, ignore_index, rows, count);
+      k_ignored_rows_init<<<grid1(N, 256), 256, 0, st>>>(target, N, ignore_index, lse, 0.f, rl, 0.f,
+                                                         nullptr, 0.f);
+    }
+    launch_row_dots(h, W, bias, target, N, H, V, bf, ignore_index, logit_scale, smooth, colpart,
+                    wsum, bsum, zt, R, st);
+  }
+  const float Vf = (float)V;
+  if (bf) {  // logits never stored: partials from the GEMM epilogue, valid rows only
+    {
+      StageTimer tm(kLogits, st);
+      const int blocks = (int)(cdiv(V, kBM) * cdiv(N, kBN));
+      k_logits_bf16<false, true><<<blocks, kGemmThreads, kGemmLds, st>>>(
+          (const bf16*)W, (const bf16*)bias, (const bf16*)h, (int)V, (int)N, (int)H, logit_scale,
+          rows, count, 0, part, smooth ? rpart : nullptr, p.C, nullptr, 0, kGroupM);
+    }
+    StageTimer tm(kCombine, st);
+    k_combine_rows<<<grid1(N, 32), 256, 0, st>>>(
+        part, smooth ? rpart : nullptr, p.C, p.nT, N, rows, count, 0, 0, target, p_mask,
+        ignore_index, zt, nullptr, label_smoothing, Vf, logit_scale, D, eob_token_id, eob_weight,
+        lse, rl, nullptr, nullptr, nullptr, 0, nullptr, nullptr, nullptr);
+  } else {  // fp32: z per chunk, row partials, combine
+    float* zb = reinterpret_cast<float*>(ws + p.oZ);
+    for (int64_t c0 = 0; c0 < N; c0 += p.C) {
+      const int64_t Cc = std::min(p.C, N - c0);
+      {
+        StageTimer tm(kLogits, st);
+        dim3 g((unsigned)cdiv(V, 64), (unsigned)cdiv(Cc, 64));
+        k_gemm_f32_nt<<<g, 256, 0, st>>>((const float*)h + c0 * H, H, Cc, (const float*)W, H, V,
+                                         H, logit_scale, zb, p.Vp, 0);
+        if (bias != nullptr)
+          k_add_bias_f32<<<dim3((unsigned)cdiv(V, 256), (unsigned)std::min<int64_t>(Cc, 256)), 256,
+                           0, st>>>(zb, p.Vp, Cc, V, (const float*)bias, logit_scale);
+        dim3 g2((unsigned)cdiv(Cc, 64), (unsigned)p.nT);
+        k_row_partials_f32<<<g2, 64, 0, st>>>(zb, p.Vp, Cc, V, part, p.C);
+      }
+      StageTimer tm(kCombine, st);
+      k_combine_rows<<<grid1(Cc, 32), 256, 0, st>>>(
+          part, nullptr, p.C, p.nT, Cc, nullptr, nullptr, c0, 0, target, p_mask, ignore_index, zt,
+          smooth ? R : nullptr, label_smoothing, Vf, logit_scale, D, eob_token_id, eob_weight, lse,
+          rl, nullptr, nullptr, nullptr, 0, nullptr, nullptr, nullptr);
+    }
+  }
+  {
+    StageTimer tm(kLoss, st);
+    k_loss_reduce<<<1, 1024, 0, st>>>(rl, N, D, loss);
+  }
+  return launch_status();
+}
+
+int fldce_scale_grads(const float* grad_out, int dtype, void* dH, int64_t n_dH, void* dW,
+                      int64_t n_dW, void* db, int64_t n_db, void* stream) {
+  if (!grad_out) return FLDCE_ERR_NULL_POINTER;
+  if (dtype != FLDCE_DTYPE_F32 && dtype != FLDCE_DTYPE_BF16) return FLDCE_ERR_BAD_DTYPE;
+  if (n_dH < 0 || n_dW < 0 || n_db < 0) return FLDCE_ERR_BAD_SHAPE;
+  if ((n_dH > 0 && !dH) || (n_dW > 0 && !dW) || (n_db > 0 && !db)) return FLDCE_ERR_NULL_POINTER;
+  if (!aligned16(grad_out) || !aligned16(dH) || !aligned16(dW) || !aligned16(db))
+    return FLDCE_ERR_ALIGNMENT;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* xs[3] = {dH, dW, db};
+  const int64_t ns[3] = {n_dH, n_dW, n_db};
+  for (int k = 0; k < 3; ++k) {
+    if (ns[k] == 0) continue;
+    const unsigned g = (unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(ns[k], 256 * 8), 8192));
+    if (dtype == FLDCE_DTYPE_BF16)
+      k_scale_grad<bf16><<<g, 256, 0, st>>>(grad_out, static_cast<bf16*>(xs[k]), ns[k]);
+    else
+      k_scale_grad<float><<<g, 256, 0, st>>>(grad_out, static_cast<float*>(xs[k]), ns[k]);
   }
   return launch_status();
 }
@@ -569,20 +767,20 @@ int fldce_shard_partials(const void* h, const void* W_local, const int64_t* targ
     {
       StageTimer tm(kLogits, st);
       k_logits_bf16<false, true><<<blocks, kGemmThreads, kGemmLds, st>>>(
-          (const bf16*)W_local, (const bf16*)h, (int)V, (int)N, (int)H, logit_scale, rows, count,
-          0, part, row_sumlogit ? rpart : nullptr, p.C, nullptr, 0, kGroupM);
+          (const bf16*)W_local, nullptr, (const bf16*)h, (int)V, (int)N, (int)H, logit_scale,
+          rows, count, 0, part, row_sumlogit ? rpart : nullptr, p.C, nullptr, 0, kGroupM);
     }
     {
       StageTimer tm(kCombine, st);
       k_combine_rows<<<grid1(N, 32), 256, 0, st>>>(
           part, row_sumlogit ? rpart : nullptr, p.C, p.nT, N, rows, count, 0, 1, nullptr, nullptr,
-          0, nullptr, nullptr, 0.f, 1.f, 1.f, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
-          0, row_max, row_sumexp, row_sumlogit);
+          0, nullptr, nullptr, 0.f, 1.f, 1.f, nullptr, -1, 1.f, nullptr, nullptr, nullptr, nullptr,
+          nullptr, 0, row_max, row_sumexp, row_sumlogit);
     }
     StageTimer tm(kPrep, st);
-    k_rowdot<bf16><<<grid1(N, 4), 256, 0, st>>>((const bf16*)h, (const bf16*)W_local, H, target,
-                                                 vocab_start, V, ignore_index, logit_scale,
-                                                 nullptr, N, target_logit, nullptr);
+    k_rowdot<bf16><<<grid1(N, 4), 256, 0, st>>>((const bf16*)h, (const bf16*)W_local, nullptr, H,
+                                                 target, vocab_start, V, ignore_index, logit_scale,
+                                                 nullptr, nullptr, N, target_logit, nullptr);
   } else {
     float* zb = reinterpret_cast<float*>(ws + p.oZ);
     for (int64_t c0 = 0; c0 < N; c0 += p.C) {
@@ -594,14 +792,14 @@ int fldce_shard_partials(const void* h, const void* W_local, const int64_t* targ
       k_row_partials_f32<<<g2, 64, 0, st>>>(zb, p.Vp, Cc, V, part, p.C);
       k_combine_rows<<<grid1(Cc, 32), 256, 0, st>>>(
           part, nullptr, p.C, p.nT, Cc, nullptr, nullptr, c0, 1, nullptr, nullptr, 0, nullptr,
-          nullptr, 0.f, 1.f, 1.f, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, row_max,
-          row_sumexp, nullptr);
+          nullptr, 0.f, 1.f, 1.f, nullptr, -1, 1.f, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
+          row_max, row_sumexp, nullptr);
     }
     if (row_sumlogit) launch_colsum<float>((const float*)W_local, V, H, colpart, wsum, st);
-    k_rowdot<float><<<grid1(N, 4), 256, 0, st>>>((const float*)h, (const float*)W_local, H, target,
-                                                  vocab_start, V, ignore_index, logit_scale,
-                                                  row_sumlogit ? wsum : nullptr, N, target_logit,
-                                                  row_sumlogit);
+    k_rowdot<float><<<grid1(N, 4), 256, 0, st>>>((const float*)h, (const float*)W_local, nullptr, H,
+                                                  target, vocab_start, V, ignore_index, logit_scale,
+                                                  row_sumlogit ? wsum : nullptr, nullptr, N,
+                                                  target_logit, row_sumlogit);
     // same convention as the bf16 path for rows whose target is ignore_index
     k_ignored_rows_init<<<grid1(N, 256), 256, 0, st>>>(target, N, ignore_index, row_max, -INFINITY,
                                                        row_sumexp, 0.f, row_sumlogit, 0.f);
@@ -648,9 +846,10 @@ int fldce_shard_bwd(const void* h, const void* W_local, const int64_t* target, c
     StageTimer tm(kPrep, st);
     k_compact_rows<<<1, 1024, 0, st>>>(target, N, ignore_index, rows, count);
   }
-  Core c{h, W_local, target, p_mask, N, H, V_local, vocab_start, V_global, dtype, ignore_index,
-         label_smoothing, logit_scale, lse, nullptr, nullptr, nullptr, nullptr, nullptr, D,
-         bf ? rows : nullptr, bf ? count : nullptr, dH_partial, true, dW_local};
+  Core c{h, W_local, nullptr, target, p_mask, N, H, V_local, vocab_start, V_global, dtype,
+         ignore_index, label_smoothing, logit_scale, lse, nullptr, nullptr, nullptr, nullptr,
+         nullptr, D, bf ? rows : nullptr, bf ? count : nullptr, dH_partial, true, dW_local,
+         nullptr, nullptr, -1, 1.f};
   return run_core(c, p, ws, st);
 }
 

@@ -286,7 +286,7 @@ __device__ __forceinline__ int acc_col(int wn, int j, int lane) { return wn * kT
 //
 // For each token and each 128-wide vocabulary slab (one wave's M range) it
 // writes part[slab * ldp + token] = (max_j z, sum_j exp(z - max)) with
-// z = s * a, and rpart[slab * ldp + token] = sum_j z when rpart != nullptr
+// z = s * (a + b_j) (b = bias, or 0 when bias == nullptr), and rpart[slab * ldp + token] = sum_j z when rpart != nullptr
 // (kPart); with kStoreZ it stores z (bf16) into zbuf in the blocked layout
 // below (ldz = padded vocabulary, a multiple of 64).
 // ---------------------------------------------------------------------------
@@ -297,10 +297,10 @@ __device__ __forceinline__ int acc_col(int wn, int j, int lane) { return wn * kT
 // count exit at once.
 template <bool kStoreZ, bool kPart>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_logits_bf16(
-    const bf16* __restrict__ W, const bf16* __restrict__ h, int V, int cmax, int H, float s,
-    const int* __restrict__ rows, const int* __restrict__ count, int64_t c0,
-    floatx2* __restrict__ part, float* __restrict__ rpart, int64_t ldp, bf16* __restrict__ zbuf,
-    int64_t ldz, int group_m) {
+    const bf16* __restrict__ W, const bf16* __restrict__ bias, const bf16* __restrict__ h, int V,
+    int cmax, int H, float s, const int* __restrict__ rows, const int* __restrict__ count,
+    int64_t c0, floatx2* __restrict__ part, float* __restrict__ rpart, int64_t ldp,
+    bf16* __restrict__ zbuf, int64_t ldz, int group_m) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   int C = cmax;
   if (count != nullptr) {
@@ -319,6 +319,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_logits_bf16(
   if (vbase >= V) return;
   const bool full = vbase + kTM * 16 <= V;
   const float sl = s * kLog2e;
+  if (bias != nullptr) {  // F.linear's bias, before the logit scale
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = m0 + acc_row(wm, i, lane, r);
+        const float b = row < V ? (float)bias[row] : 0.f;
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) acc[i][j][r] += b;
+      }
+  }
 #pragma unroll
   for (int j = 0; j < kTN; ++j) {
     const int tok = n0 + acc_col(wn, j, lane);

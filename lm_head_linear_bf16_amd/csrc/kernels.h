@@ -227,28 +227,34 @@ __global__ __launch_bounds__(256) void k_transpose_gather_bf16(const bf16* __res
   }
 }
 
-// out[c] = sum_b part[b, c], b ascending.
+// out[c] = sum_b part[b * ld + c] for c < Cn, b ascending, cast to T.
+template <typename T>
 __global__ __launch_bounds__(256) void k_colsum_finish(const float* __restrict__ part, int64_t nb,
-                                                       int64_t Cn, float* __restrict__ out) {
+                                                       int64_t ld, int64_t Cn, T* __restrict__ out) {
   const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (c >= Cn) return;
   float s = 0.f;
-  for (int64_t b = 0; b < nb; ++b) s += part[b * Cn + c];
-  out[c] = s;
+  for (int64_t b = 0; b < nb; ++b) s += part[b * ld + c];
+  out[c] = from_f32<T>(s);
 }
 
 // ---------------------------------------------------------------------------
 // Per-row dot products (one wave per row):
-//   zt[i] = s * <h_i, W[y_i - v0]>  if y_i != ignore and v0 <= y_i < v0 + Vl, else 0
-//   R[i]  = s * <h_i, wsum>         (wsum = column sums of W: sum_j z_ij)
+//   zt[i] = s * (<h_i, W[y_i - v0]> + b[y_i - v0])
+//                                   if y_i != ignore and v0 <= y_i < v0 + Vl, else 0
+//   R[i]  = s * (<h_i, wsum> + bsum) (wsum = column sums of W, bsum = sum of
+//                                   the bias: sum_j z_ij)
 // The target logit is page 1's cross_entropy_kernel step 3 load of
-// logits[y]; the row sum feeds the label-smoothing term.
+// logits[y]; the row sum feeds the label-smoothing term.  bias and bsum may
+// be null (no bias).
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void k_rowdot(const T* __restrict__ h, const T* __restrict__ W,
-                                                int64_t H, const int64_t* __restrict__ target,
-                                                int64_t v0, int64_t Vl, int64_t ignore, float s,
-                                                const float* __restrict__ wsum, int64_t N,
+                                                const T* __restrict__ bias, int64_t H,
+                                                const int64_t* __restrict__ target, int64_t v0,
+                                                int64_t Vl, int64_t ignore, float s,
+                                                const float* __restrict__ wsum,
+                                                const float* __restrict__ bsum, int64_t N,
                                                 float* __restrict__ zt, float* __restrict__ R) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -267,6 +273,8 @@ __global__ __launch_bounds__(256) void k_rowdot(const T* __restrict__ h, const T
   a = wave_sum(a);
   b = wave_sum(b);
   if (lane == 0) {
+    if (bias != nullptr && in) a += to_f32(bias[col]);
+    if (bsum != nullptr) b += *bsum;
     if (zt != nullptr) zt[row] = in ? s * a : 0.f;
     if (R != nullptr) R[row] = s * b;
   }
@@ -299,11 +307,13 @@ __global__ __launch_bounds__(64) void k_row_partials_f32(const float* __restrict
 // R_i (the row sum of the logits) is R[i] when R != nullptr, else the sum of
 // rpart over the slabs when rpart != nullptr (fixed order), else 0.
 // mode 0 (loss):  lse_i = M + log S, and with p_i, D, eps:
-//     l_i   = [(1-eps)(lse_i - zt_i) + eps(lse_i - R_i / Vg)] / p_i   (0 if ignored)
-//     coef_i = s / (p_i D)                                            (0 if ignored)
+//     l_i   = w_i [(1-eps)(lse_i - zt_i) + eps(lse_i - R_i / Vg)] / p_i   (0 if ignored)
+//     coef_i = w_i s / (p_i D)                                            (0 if ignored)
 //   (page 1, cross_entropy_kernel steps 4 and the label-smoothing combine;
-//    the whole smoothed CE is divided by p_i).  Writes lse[i], rloss[i],
-//   coef[i] (chunk-local).
+//    the whole smoothed CE is divided by p_i).  w_i = eob_w on rows whose
+//   target is the end-of-block token eob >= 0 (the module's forward divides
+//   their p_mask by the weight), else 1.  Writes lse[i], rloss[i], coef[i]
+//   (chunk-local).
 // mode 1 (shard): writes out_m[i] = M, out_s[i] = S (sum relative to M) and,
 // when out_r != nullptr, out_r[i] = R_i.
 // ---------------------------------------------------------------------------
@@ -318,7 +328,7 @@ __global__ __launch_bounds__(256) void k_combine_rows(
     int64_t cmax, const int* __restrict__ rows, const int* __restrict__ count, int64_t c0,
     int mode, const int64_t* __restrict__ target, const float* __restrict__ p_mask,
     int64_t ignore, const float* __restrict__ zt, const float* __restrict__ R, float eps, float Vg,
-    float s, const float* __restrict__ D, float* __restrict__ lse_out,
+    float s, const float* __restrict__ D, int64_t eob, float eob_w, float* __restrict__ lse_out,
     float* __restrict__ rloss_out, float* __restrict__ coef_out, float* __restrict__ lsec,
     int* __restrict__ tcol, int64_t v0, float* __restrict__ out_m, float* __restrict__ out_s,
     float* __restrict__ out_r) {
@@ -355,17 +365,19 @@ __global__ __launch_bounds__(256) void k_combine_rows(
   float l = 0.f, cf = 0.f;
   if (valid) {
     const float rs = (R != nullptr) ? R[i] : rsum;
-    l = ((1.f - eps) * (lse - zt[i]) + eps * (lse - rs / Vg)) / p;
-    cf = s / (p * D[0]);
+    const float wt = (eob >= 0 && target[i] == eob) ? eob_w : 1.f;
+    l = wt * (((1.f - eps) * (lse - zt[i]) + eps * (lse - rs / Vg)) / p);
+    cf = wt * (s / (p * D[0]));
   }
   lse_out[i] = valid ? lse : 0.f;
   rloss_out[i] = l;
-  coef_out[j] = cf;
+  if (coef_out != nullptr) coef_out[j] = cf;
   if (lsec != nullptr) lsec[j] = lse;
   if (tcol != nullptr) tcol[j] = valid ? (int)(target[i] - v0) : -1;
 }
 
-// coef_j = s / (p_i D), 0 on ignored rows (shard backward, lse given), for
+// coef_j = w_i s / (p_i D), 0 on ignored rows (shard backward, lse given;
+// w_i the end-of-block weight as in k_combine_rows), for
 // chunk row j -> batch row i as in k_combine_rows; with lsec / tcol also the
 // chunk's lse (from the given lse) and target column.
 __global__ __launch_bounds__(256) void k_coef_rows(const int64_t* __restrict__ target,
@@ -373,6 +385,7 @@ __global__ __launch_bounds__(256) void k_coef_rows(const int64_t* __restrict__ t
                                                    int64_t cmax, const int* __restrict__ rows,
                                                    const int* __restrict__ count, int64_t c0,
                                                    float s, const float* __restrict__ D,
+                                                   int64_t eob, float eob_w,
                                                    float* __restrict__ coef,
                                                    const float* __restrict__ lse_in,
                                                    float* __restrict__ lsec,
@@ -383,7 +396,8 @@ __global__ __launch_bounds__(256) void k_coef_rows(const int64_t* __restrict__ t
   const int64_t i = rows != nullptr ? (int64_t)rows[c0 + j] : c0 + j;
   const bool valid = target[i] != ignore;
   const float p = (p_mask != nullptr && valid) ? p_mask[i] : 1.f;
-  coef[j] = valid ? s / (p * D[0]) : 0.f;
+  const float wt = (valid && eob >= 0 && target[i] == eob) ? eob_w : 1.f;
+  coef[j] = valid ? wt * (s / (p * D[0])) : 0.f;
   if (lsec != nullptr) lsec[j] = lse_in[i];
   if (tcol != nullptr) tcol[j] = valid ? (int)(target[i] - v0) : -1;
 }
@@ -478,7 +492,9 @@ __global__ __launch_bounds__(256) void k_gpass(T* __restrict__ z, int64_t ldz, i
 // ((t / 16) * (ldz / 4) + v / 4) * 64 + (t % 16) * 4 + v % 4, and writing g
 // row-major [rows, ldz] for both backward GEMMs.  Chunk rows are given by the
 // device-side count (chunk_rows); rows C .. round_up(C, 64) - 1 and columns
-// >= V are written as zeros.  lse, coef and tcol are per chunk row.
+// >= V are written as zeros.  lse, coef and tcol are per chunk row.  With
+// dbpart, block (x, y) also writes the column sums of its 64 rows of g (as
+// stored, bf16) to dbpart[y * ldz + column], zeros for blocks past the rows.
 //
 // One block = 64 tokens x 256 columns, 256 threads.  Thread -> two fixed
 // tokens (their lse, coefficient and target stay in registers) and eight
@@ -492,13 +508,19 @@ __global__ __launch_bounds__(256) void k_gpass_blk(const bf16* __restrict__ zblk
                                                    const float* __restrict__ lse,
                                                    const float* __restrict__ coef,
                                                    const int* __restrict__ tcol, float eps,
-                                                   float Vg, bf16* __restrict__ g) {
+                                                   float Vg, bf16* __restrict__ g,
+                                                   float* __restrict__ dbpart) {
   __shared__ bf16 tile[64][kGpassCols + 8];  // [token][column]
   const int tid = threadIdx.x;
   const int64_t C = chunk_rows(count, c0, cmax);
   const int64_t i0 = (int64_t)blockIdx.y * 64, j0 = (int64_t)blockIdx.x * kGpassCols;
-  if (i0 >= round_up(C, 64)) return;  // rows past the chunk's padded count are never read
   const int64_t nvb = min((int64_t)kGpassCols / 4, (ldz - j0) / 4);  // column blocks in range
+  // dbpart (when not null): this block's column sums of g, row block y
+  float* dbrow = dbpart != nullptr ? dbpart + (int64_t)blockIdx.y * ldz + j0 : nullptr;
+  if (i0 >= round_up(C, 64)) {  // rows past the chunk's padded count are never read
+    if (dbrow != nullptr && tid < nvb * 4) dbrow[tid] = 0.f;
+    return;
+  }
   const float epsV = eps / Vg;
   const int tb = tid >> 6, vbo = (tid >> 3) & 7, w = tid & 7;
   const int tl0 = tb * 16 + w * 2;  // tokens tl0, tl0 + 1 of the tile
@@ -546,12 +568,51 @@ __global__ __launch_bounds__(256) void k_gpass_blk(const bf16* __restrict__ zblk
     }
   }
   __syncthreads();
+  if (dbrow != nullptr && tid < nvb * 4) {  // page 1: db += c_logits.sum(0)
+    float acc = 0.f;
+#pragma unroll 8
+    for (int r = 0; r < 64; ++r) acc += (float)tile[r][tid];
+    dbrow[tid] = acc;
+  }
   const int units = (int)nvb / 2;  // 16-byte units per token row in range
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
     const int unit = tid + 256 * p;
     const int r = unit >> 5, c = unit & 31;
     if (c < units) *(bf16x8*)(g + (i0 + r) * ldz + j0 + c * 8) = *(const bf16x8*)&tile[r][c * 8];
+  }
+}
+
+// fp32 path: z[i, j] += s * b[j] for i < C, j < V (the bias of F.linear,
+// before the logit scale).
+__global__ __launch_bounds__(256) void k_add_bias_f32(float* __restrict__ z, int64_t ldz, int64_t C,
+                                                      int64_t V, const float* __restrict__ b,
+                                                      float s) {
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j >= V) return;
+  const float sb = s * b[j];
+  for (int64_t i = blockIdx.y; i < C; i += gridDim.y) z[i * ldz + j] += sb;
+}
+
+// Upstream-gradient scaling (page 1, fused_linear_cross_entropy_backward):
+// x[e] = T(float(x[e]) * do) unless do == 1.  Grid-stride over 8-element
+// groups (x 16-byte aligned); the tail past a multiple of 8 element by element.
+template <typename T>
+__global__ __launch_bounds__(256) void k_scale_grad(const float* __restrict__ grad_out,
+                                                    T* __restrict__ x, int64_t n) {
+  const float d = *grad_out;
+  if (d == 1.f) return;
+  const int64_t n8 = n / 8;
+  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < n8; q += (int64_t)gridDim.x * 256) {
+    float v[8];
+    load8(x + q * 8, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] *= d;
+    store8(x + q * 8, v);
+  }
+  if (blockIdx.x == 0 && threadIdx.x < n - n8 * 8) {
+    const int64_t e = n8 * 8 + threadIdx.x;
+    x[e] = from_f32<T>(to_f32(x[e]) * d);
   }
 }
 

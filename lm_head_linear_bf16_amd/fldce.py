@@ -32,6 +32,14 @@ _SIGNATURES = {
     "fldce_fwd_bwd": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_int, _c_i64,
                                _c_f, _c_f, _c_int, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64,
                                _c_p, _c_sz, _c_p]),
+    "fldce_fwd_bwd_ex": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_int,
+                                  _c_i64, _c_f, _c_f, _c_int, _c_i64, _c_i64, _c_f, _c_p, _c_p,
+                                  _c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_sz, _c_p]),
+    "fldce_fwd_workspace_size": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_int]),
+    "fldce_fwd": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_int, _c_i64,
+                           _c_f, _c_f, _c_int, _c_i64, _c_i64, _c_f, _c_p, _c_p, _c_p, _c_p, _c_sz,
+                           _c_p]),
+    "fldce_scale_grads": (_c_int, [_c_p, _c_int, _c_p, _c_i64, _c_p, _c_i64, _c_p, _c_i64, _c_p]),
     "fldce_shard_partials_workspace_size": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_int]),
     "fldce_shard_partials": (_c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_int,
                                       _c_i64, _c_f, _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
@@ -202,6 +210,122 @@ def fldce_fwd_bwd(h: torch.Tensor, W: torch.Tensor, target: torch.Tensor,
     if row_stats:
         r.update(row_lse=lse, row_loss=rl)
     return r
+
+
+def _eob_code(eob_token_id: Optional[int]) -> int:
+    return -1 if eob_token_id is None else int(eob_token_id)
+
+
+def fldce_fwd_bwd_ex(h: torch.Tensor, W: torch.Tensor, target: torch.Tensor,
+                     p_mask: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
+                     ignore_index: int = -100, label_smoothing: float = 0.0,
+                     logit_scale: float = 1.0, reduction="mean", total: int = 0,
+                     eob_token_id: Optional[int] = None, eob_weight: float = 1.0,
+                     want_db: Optional[bool] = None, chunk_rows: int = 0,
+                     row_stats: bool = False, workspace: Optional[torch.Tensor] = None) -> dict:
+    """fldce_fwd_bwd plus page 1's optional bias [V] (and its gradient db,
+    returned when ``want_db`` or, by default, when a bias is given) and the
+    end-of-block weight (rows whose target is ``eob_token_id``)."""
+    N, H = h.shape
+    V = W.shape[0]
+    _check(h, "h")
+    _check(W, "W", h.dtype)
+    _check(target, "target", torch.int64)
+    if p_mask is not None:
+        _check(p_mask, "p_mask", torch.float32)
+    if bias is not None:
+        _check(bias, "bias", h.dtype)
+        if bias.shape != (V,):
+            raise ValueError(f"bias must have shape ({V},)")
+    dev = h.device
+    code = _dtype_code(h.dtype)
+    want_db = (bias is not None) if want_db is None else want_db
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    dH = torch.empty_like(h)
+    dW = torch.empty_like(W)
+    db = torch.empty(V, dtype=h.dtype, device=dev) if want_db else None
+    lse = rl = None
+    if row_stats:
+        lse = torch.empty(N, dtype=torch.float32, device=dev)
+        rl = torch.empty(N, dtype=torch.float32, device=dev)
+    nbytes = lib().fldce_workspace_size(N, H, V, code, chunk_rows)
+    ws = _workspace(nbytes, dev, workspace)
+    rc = lib().fldce_fwd_bwd_ex(_ptr(h), _ptr(W), _ptr(bias), _ptr(target), _ptr(p_mask), N, H, V,
+                                code, ignore_index, label_smoothing, logit_scale,
+                                _reduction_code(reduction), total, _eob_code(eob_token_id),
+                                eob_weight, _ptr(loss), _ptr(dH), _ptr(dW), _ptr(db), _ptr(lse),
+                                _ptr(rl), chunk_rows, _ptr(ws), nbytes, _stream(dev))
+    if rc != 0:
+        raise FldceError(rc, "fldce_fwd_bwd_ex")
+    r = dict(loss=loss, dH=dH, dW=dW, db=db)
+    if row_stats:
+        r.update(row_lse=lse, row_loss=rl)
+    return r
+
+
+def fldce_fwd_workspace_size(N: int, H: int, V: int, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    return lib().fldce_fwd_workspace_size(N, H, V, code)
+
+
+def fldce_fwd(h: torch.Tensor, W: torch.Tensor, target: torch.Tensor,
+              p_mask: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
+              ignore_index: int = -100, label_smoothing: float = 0.0, logit_scale: float = 1.0,
+              reduction="mean", total: int = 0, eob_token_id: Optional[int] = None,
+              eob_weight: float = 1.0, row_stats: bool = False,
+              workspace: Optional[torch.Tensor] = None) -> dict:
+    """Forward only: loss (and per-row lse / loss with row_stats), no gradients."""
+    N, H = h.shape
+    V = W.shape[0]
+    _check(h, "h")
+    _check(W, "W", h.dtype)
+    _check(target, "target", torch.int64)
+    if p_mask is not None:
+        _check(p_mask, "p_mask", torch.float32)
+    if bias is not None:
+        _check(bias, "bias", h.dtype)
+        if bias.shape != (V,):
+            raise ValueError(f"bias must have shape ({V},)")
+    dev = h.device
+    code = _dtype_code(h.dtype)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    lse = rl = None
+    if row_stats:
+        lse = torch.empty(N, dtype=torch.float32, device=dev)
+        rl = torch.empty(N, dtype=torch.float32, device=dev)
+    nbytes = lib().fldce_fwd_workspace_size(N, H, V, code)
+    ws = _workspace(nbytes, dev, workspace)
+    rc = lib().fldce_fwd(_ptr(h), _ptr(W), _ptr(bias), _ptr(target), _ptr(p_mask), N, H, V, code,
+                         ignore_index, label_smoothing, logit_scale, _reduction_code(reduction),
+                         total, _eob_code(eob_token_id), eob_weight, _ptr(loss), _ptr(lse),
+                         _ptr(rl), _ptr(ws), nbytes, _stream(dev))
+    if rc != 0:
+        raise FldceError(rc, "fldce_fwd")
+    r = dict(loss=loss)
+    if row_stats:
+        r.update(row_lse=lse, row_loss=rl)
+    return r
+
+
+def fldce_scale_grads(grad_out: torch.Tensor, dH: Optional[torch.Tensor] = None,
+                      dW: Optional[torch.Tensor] = None, db: Optional[torch.Tensor] = None) -> None:
+    """In place: each given gradient *= grad_out (a float32 device scalar),
+    skipped on the device when grad_out == 1."""
+    _check(grad_out, "grad_out", torch.float32)
+    if grad_out.numel() != 1:
+        raise ValueError("grad_out must hold one element")
+    ts = [t for t in (dH, dW, db) if t is not None]
+    if not ts:
+        return
+    dtype = ts[0].dtype
+    for name, t in (("dH", dH), ("dW", dW), ("db", db)):
+        if t is not None:
+            _check(t, name, dtype)
+    n = lambda t: 0 if t is None else t.numel()  # noqa: E731
+    rc = lib().fldce_scale_grads(_ptr(grad_out), _dtype_code(dtype), _ptr(dH), n(dH), _ptr(dW),
+                                 n(dW), _ptr(db), n(db), _stream(grad_out.device))
+    if rc != 0:
+        raise FldceError(rc, "fldce_scale_grads")
 
 
 def fldce_shard_partials(h: torch.Tensor, W_local: torch.Tensor, target: torch.Tensor,

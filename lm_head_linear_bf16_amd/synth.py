@@ -15,6 +15,8 @@ head of the model page "fused_linear_diffusion_cross_entropy.py"):
 * ``shard``     B=16, L=2048, H=5120, vocab shard k=3 of 8 (18992 rows of a
                  151936 vocab), targets uniform over the full vocab
 
+An optional bias b [V] ~ N(0, 1) can be drawn for any workload (``bias``).
+
 Masking recipe (the masked-diffusion forward process): per sequence (or per
 block) a masking probability t ~ U(0.05, 1) is drawn; each token is masked
 when its own uniform draw u < t.  Masked tokens keep their token id as target,
@@ -37,7 +39,7 @@ import numpy as np
 
 IGNORE_INDEX = -100
 
-_T_ID, _TT_ID, _U_ID, _H_ID, _W_ID = 0, 1, 2, 3, 4
+_T_ID, _TT_ID, _U_ID, _H_ID, _W_ID, _B_ID = 0, 1, 2, 3, 4, 5
 
 
 @dataclasses.dataclass(frozen=True)
@@ -169,6 +171,13 @@ def weight(w: Workload, shard: Optional[int] = None) -> Tensor:
         x *= np.float32(w.w_std)
         parts.append(x)
     x = parts[0] if len(parts) == 1 else np.concatenate(parts, axis=0)
+    return _as_dtype(x, w.dtype)
+
+
+def bias(w: Workload) -> Tensor:
+    """b [V] ~ N(0, 1): an input for the optional bias of the LM head (the
+    model page's functions accept one; its workloads use none)."""
+    x = _rng(w.index, _B_ID).standard_normal(w.V, dtype=np.float32)
     return _as_dtype(x, w.dtype)
 
 

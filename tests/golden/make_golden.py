@@ -1,8 +1,9 @@
 """Write the stored expected row statistics for the large workloads.
 
 For every token row of the ``4b``, ``headline``, ``block`` and ``shard``
-workloads this stores the oracle's float64 logsumexp over the FULL vocabulary,
-the target logit and the row sum of the logits (``oracle.row_stats``).  The
+workloads (and ``4b_bias``: the ``4b`` inputs with the seeded bias) this
+stores the oracle's float64 logsumexp over the FULL vocabulary, the target
+logit and the row sum of the logits (``oracle.row_stats``).  The
 parity tests then finish the loss, sampled dH rows and sampled dW rows with
 the oracle at test time; only this O(N*H*V) float64 GEMM is too slow to redo
 there.  Inputs come from ``lm_head_linear_bf16_amd.synth``; nothing here
@@ -31,18 +32,21 @@ def path_for(name: str) -> str:
 
 
 def make(name: str) -> None:
-    w = synth.WORKLOADS[name]
+    with_bias = name.endswith("_bias")
+    w = synth.WORKLOADS[name[:-5] if with_bias else name]
     t0 = time.time()
     target, _ = synth.targets(w)
     h = synth.hidden(w).values
     W = synth.weight(w).values               # full vocabulary (all shards)
-    lse, zt, zs = O.row_stats(h, W, target, np.arange(w.N), w.logit_scale, row_block=1024)
+    b = synth.bias(w).values if with_bias else None
+    lse, zt, zs = O.row_stats(h, W, target, np.arange(w.N), w.logit_scale, row_block=1024,
+                              bias=b)
     np.savez(path_for(name), lse=lse, z_target=zt, z_sum=zs,
              fingerprint=np.array(synth.fingerprint(w)))
     print(f"{name}: N={w.N} H={w.H} V={w.V} in {time.time() - t0:.1f}s", flush=True)
 
 
 if __name__ == "__main__":
-    names = sys.argv[1:] or ["4b", "headline", "block", "shard"]
+    names = sys.argv[1:] or ["4b", "headline", "block", "shard", "4b_bias"]
     for n in names:
         make(n)

@@ -41,7 +41,7 @@ def test_status_strings(L):
     for s in range(-8, 0):
         assert fldce.status_string(s) != "unknown status"
     assert fldce.status_string(-99) == "unknown status"
-    assert fldce.fldce_version() == 1
+    assert fldce.fldce_version() == 2
 
 
 def test_workspace_queries(L):
@@ -120,6 +120,59 @@ def test_shard_argument_checks(L):
     assert call(lse=None) == -1
     assert call(dHp=BAD) == -6
     assert call(ws_bytes=1) == -5
+
+
+def _ex(L, **kw):
+    a = dict(h=P, W=P, bias=None, target=P, p_mask=None, N=16, H=64, V=100, dtype=1, ignore=-100,
+             eps=0.0, s=1.0, red=1, total=0, eob=-1, eob_w=1.0, loss=P, dH=P, dW=P, db=None,
+             lse=None, rl=None, chunk=0, ws=P, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return L.fldce_fwd_bwd_ex(*a.values())
+
+
+def _fwd_only(L, **kw):
+    a = dict(h=P, W=P, bias=None, target=P, p_mask=None, N=16, H=64, V=100, dtype=1, ignore=-100,
+             eps=0.0, s=1.0, red=1, total=0, eob=-1, eob_w=1.0, loss=P, lse=None, rl=None, ws=P,
+             wsb=1 << 40, stream=None)
+    a.update(kw)
+    return L.fldce_fwd(*a.values())
+
+
+@pytest.mark.parametrize("f", [_ex, _fwd_only])
+def test_extended_argument_checks(L, f):
+    assert f(L, W=None) == -1
+    assert f(L, loss=None) == -1
+    assert f(L, dtype=2) == -3
+    assert f(L, red=3) == -4
+    assert f(L, eps=2.0) == -4
+    assert f(L, eob=5, eob_w=-1.0) == -4          # weight must be >= 0
+    assert f(L, eob=5, eob_w=float("nan")) == -4
+    assert f(L, eob=5, eob_w=float("inf")) == -4
+    assert f(L, eob=-1, eob_w=-1.0, wsb=8) == -5  # no EOB: the weight is not checked
+    assert f(L, bias=BAD) == -6
+    assert f(L, H=96) == -8
+    assert f(L, wsb=8) == -5
+    if f is _ex:
+        assert f(L, db=BAD) == -6
+        assert f(L, dH=None) == -1
+        assert f(L, chunk=-1) == -4
+
+
+def test_fwd_workspace_query(L):
+    a = fldce.fldce_fwd_workspace_size(8192, 2560, 151936, 1)
+    assert 0 < a < fldce.fldce_workspace_size(8192, 2560, 151936, 1)
+    assert fldce.fldce_fwd_workspace_size(-1, 64, 10, 1) == 0
+    assert fldce.fldce_fwd_workspace_size(4, 64, 10, 5) == 0
+
+
+def test_scale_grads_argument_checks(L):
+    f = L.fldce_scale_grads
+    assert f(None, 1, P, 16, None, 0, None, 0, None) == -1
+    assert f(P, 4, P, 16, None, 0, None, 0, None) == -3
+    assert f(P, 1, P, -1, None, 0, None, 0, None) == -2
+    assert f(P, 1, None, 16, None, 0, None, 0, None) == -1
+    assert f(P, 1, P, 16, BAD, 8, None, 0, None) == -6
+    assert f(BAD, 1, P, 16, None, 0, None, 0, None) == -6
 
 
 def test_binding_rejects_host_tensors():
