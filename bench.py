@@ -159,6 +159,66 @@ def cpu_baseline(w, rows: int) -> dict:
             "seconds": dt}
 
 
+def _timed(fn, steps: int, warmup: int):
+    """(ms per call, {stage: ms per call}) with the library's stage events."""
+    import torch
+    from lm_head_linear_bf16_amd import fldce
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    fldce.fldce_profile_begin()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    fldce.fldce_profile_end()
+    stages = {}
+    for st in range(fldce.fldce_profile_num_stages()):
+        tot, n = fldce.fldce_profile_read(st)
+        if n:
+            stages[fldce.fldce_profile_stage_name(st)] = round(tot / steps, 4)
+    return (t1 - t0) * 1e3 / steps, stages
+
+
+def extra_legs(args, w, h, W, tgt, pm, dt, rows_mult: int, ms_plain: float, peak: float) -> dict:
+    """The rest of page 1's interface on the same inputs: forward only
+    (fldce_fwd: 2 * rows * H * V flops) and fwd+bwd with the seeded bias and
+    its gradient db (fldce_fwd_bwd_ex)."""
+    import numpy as np
+    import torch
+    from lm_head_linear_bf16_amd import fldce, synth
+    N, H, V = w.N, w.H, w.V
+    dev = h.device
+    steps, warm = max(3, args.steps // 2), 1
+    out = {}
+    ws = torch.empty(fldce.fldce_fwd_workspace_size(N, H, V, dt), dtype=torch.uint8, device=dev)
+    kw = dict(label_smoothing=w.label_smoothing, logit_scale=w.logit_scale,
+              reduction=w.reduction, total=w.total)
+    log(f"forward only: {steps} steps")
+    m, st = _timed(lambda: fldce.fldce_fwd(h, W, tgt, pm, workspace=ws, **kw), steps, warm)
+    tf = 2.0 * rows_mult * H * V / (m * 1e-3) / 1e12
+    out["forward_only"] = {"ms_per_step": round(m, 4), "tokens_per_s": round(N / (m * 1e-3), 1),
+                           "tflops": round(tf, 2), "pct_peak": round(100.0 * tf / peak, 2),
+                           "stage_ms_per_step": st}
+    del ws
+    bt = synth.bias(w)
+    b = (torch.from_numpy(bt.bits.view(np.int16)).view(torch.bfloat16) if bt.bits is not None
+         else torch.from_numpy(bt.values)).to(dev)
+    ws = torch.empty(fldce.fldce_workspace_size(N, H, V, dt), dtype=torch.uint8, device=dev)
+    log(f"fwd+bwd with bias and db: {steps} steps")
+    m, st = _timed(lambda: fldce.fldce_fwd_bwd_ex(h, W, tgt, pm, b, want_db=True, workspace=ws,
+                                                  **kw), steps, warm)
+    tf = 6.0 * rows_mult * H * V / (m * 1e-3) / 1e12
+    out["with_bias_db"] = {"ms_per_step": round(m, 4), "tokens_per_s": round(N / (m * 1e-3), 1),
+                           "tflops": round(tf, 2), "pct_peak": round(100.0 * tf / peak, 2),
+                           "overhead_vs_plain": round(m / ms_plain - 1.0, 4),
+                           "stage_ms_per_step": st}
+    del ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -175,6 +235,8 @@ def main() -> int:
                     help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a "
                          "run with --calib-copy-mib into profiles/traffic.json and exit")
     ap.add_argument("--calib-mib", type=int, default=1024, help="size of that calibration copy")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the forward-only and bias + db legs")
     args = ap.parse_args()
     if args.traffic_summary:
         return traffic_summary(args.traffic_summary[0], args.traffic_summary[1], args.workload,
@@ -291,6 +353,8 @@ def main() -> int:
         "stage_ms_per_step": stage_ms,
         "roofline": roofline,
     }
+    if not args.no_extras:
+        result.update(extra_legs(args, w, h, W, tgt, pm, dt, rows_mult, ms, peak))
     if args.sweep:
         sw = {}
         for c in [int(x) for x in args.sweep.split(",") if x]:

@@ -72,7 +72,9 @@ def lib() -> ctypes.CDLL:
             raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
         L = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in _SIGNATURES.items():
-            f = getattr(L, name)
+            f = getattr(L, name, None)
+            if f is None:  # an older build (FLDCE_LIB): calling it raises AttributeError
+                continue
             f.restype = res
             f.argtypes = args
         _lib = L
