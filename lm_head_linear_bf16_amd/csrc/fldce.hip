@@ -34,7 +34,10 @@ namespace {
 enum Mode { kFwdBwd = 0, kShardPartials = 1, kShardBwd = 2, kFwd = 3 };
 
 constexpr int64_t kZBudgetBytes = int64_t(16) << 30;  // chunk logits + g^T buffers
+// Tile rows per group in the XCD-aware block order (measured best per GEMM at
+// the 4B-scale shapes: 4 for logits, 2 for the two backward products).
 constexpr int kGroupM = 4;
+constexpr int kGroupMBwd = 2;
 
 struct Plan {
   int64_t N = 0, H = 0, V = 0, C = 0, Cp = 0, Vp = 0, nT = 0, nchunks = 0;
@@ -342,7 +345,7 @@ int run_core_bf16(const Core& c, const Plan& p, char* ws, hipStream_t st) {
       dim3 g((unsigned)cdiv(Vp, kGpassCols), (unsigned)(Cpc / 64));
       k_gpass_blk<<<g, 256, 0, st>>>(zb, Vp, cmax, c.count, c0, V, lsec, coef, tcol, c.eps,
                                      (float)c.Vg, gb,
-                                     c.db != nullptr ? c.dbpart + db_off * Vp : nullptr);
+                                     c.db != nullptr ? c.dbpart + db_off * Vp : nullptr, c.s);
       db_off += Cpc / 64;
     }
     {  // 4. dH = g W (split over the vocabulary, ordered reduction, scattered rows)
@@ -352,7 +355,7 @@ int run_core_bf16(const Core& c, const Plan& p, char* ws, hipStream_t st) {
         StageTimer tm(kDHGemm, st);
         k_gemm_dh_bf16<<<blocks, kGemmThreads, kGemmLds, st>>>(gb, Vp, (int)cmax, c.count, c0, W,
                                                                (int)V, (int)H, (int)(Vp / kBK), S,
-                                                               dHpart, kGroupM);
+                                                               dHpart, kGroupMBwd);
       }
       StageTimer tm(kDHReduce, st);
       if (c.dH_f32)
@@ -370,7 +373,7 @@ int run_core_bf16(const Core& c, const Plan& p, char* ws, hipStream_t st) {
       auto kern = mode == 0 ? k_gemm_dw_bf16<0>
                             : (mode == 1 ? k_gemm_dw_bf16<1> : (mode == 2 ? k_gemm_dw_bf16<2> : k_gemm_dw_bf16<3>));
       kern<<<blocks, kGemmThreads, kGemmLds, st>>>(gb, Vp, (int)cmax, c.count, c0, (int)V, hT,
-                                                   p.Cp, (int)H, (bf16*)c.dW, dW32, kGroupM);
+                                                   p.Cp, (int)H, (bf16*)c.dW, dW32, kGroupMBwd);
     }
   }
   if (c.db != nullptr) {

@@ -287,8 +287,9 @@ __device__ __forceinline__ int acc_col(int wn, int j, int lane) { return wn * kT
 // For each token and each 128-wide vocabulary slab (one wave's M range) it
 // writes part[slab * ldp + token] = (max_j z, sum_j exp(z - max)) with
 // z = s * (a + b_j) (b = bias, or 0 when bias == nullptr), and rpart[slab * ldp + token] = sum_j z when rpart != nullptr
-// (kPart); with kStoreZ it stores z (bf16) into zbuf in the blocked layout
-// below (ldz = padded vocabulary, a multiple of 64).
+// (kPart); with kStoreZ it stores the unscaled logits a + b_j (bf16; the
+// dlogits pass applies s) into zbuf in the blocked layout below (ldz =
+// padded vocabulary, a multiple of 64).
 // ---------------------------------------------------------------------------
 //
 // Token rows: chunk token j (< the chunk's row count, read from `count` when
@@ -374,7 +375,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_logits_bf16(
         const int row0 = m0 + acc_row(wm, i, lane, 0);
         bf16x4 v;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = (bf16)(acc[i][j][r] * s);
+        for (int r = 0; r < 4; ++r) v[r] = (bf16)acc[i][j][r];
         bf16* dst = zt + (int64_t)(row0 >> 2) * 64;
         if (full || row0 + 3 < V) {
           *(bf16x4*)dst = v;

@@ -487,8 +487,9 @@ __global__ __launch_bounds__(256) void k_gpass(T* __restrict__ z, int64_t ldz, i
 }
 
 // ---------------------------------------------------------------------------
-// dlogits for the bf16 path (same formula as k_gpass), reading z from the
-// blocked layout the logits GEMM writes: element (token t, column v) at
+// dlogits for the bf16 path (same formula as k_gpass), reading the unscaled
+// logits (z = zscale * stored value) from the blocked layout the logits GEMM
+// writes: element (token t, column v) at
 // ((t / 16) * (ldz / 4) + v / 4) * 64 + (t % 16) * 4 + v % 4, and writing g
 // row-major [rows, ldz] for both backward GEMMs.  Chunk rows are given by the
 // device-side count (chunk_rows); rows C .. round_up(C, 64) - 1 and columns
@@ -499,7 +500,9 @@ __global__ __launch_bounds__(256) void k_gpass(T* __restrict__ z, int64_t ldz, i
 // One block = 64 tokens x 256 columns, 256 threads.  Thread -> two fixed
 // tokens (their lse, coefficient and target stay in registers) and eight
 // 16-byte units of z (a wave reads 1 KB contiguous per step); g goes out
-// through LDS as 512-byte row segments.
+// through LDS as 512-byte row segments.  z is read once and g is read by the
+// next kernels from HBM anyway (1.4 GB each at the 4B-scale sizes, far past
+// the caches), so both use non-temporal accesses.
 // ---------------------------------------------------------------------------
 constexpr int kGpassCols = 256;
 __global__ __launch_bounds__(256) void k_gpass_blk(const bf16* __restrict__ zblk, int64_t ldz,
@@ -509,7 +512,7 @@ __global__ __launch_bounds__(256) void k_gpass_blk(const bf16* __restrict__ zblk
                                                    const float* __restrict__ coef,
                                                    const int* __restrict__ tcol, float eps,
                                                    float Vg, bf16* __restrict__ g,
-                                                   float* __restrict__ dbpart) {
+                                                   float* __restrict__ dbpart, float zscale) {
   __shared__ bf16 tile[64][kGpassCols + 8];  // [token][column]
   const int tid = threadIdx.x;
   const int64_t C = chunk_rows(count, c0, cmax);
@@ -522,6 +525,7 @@ __global__ __launch_bounds__(256) void k_gpass_blk(const bf16* __restrict__ zblk
     return;
   }
   const float epsV = eps / Vg;
+  const float zl2 = zscale * kLog2e;
   const int tb = tid >> 6, vbo = (tid >> 3) & 7, w = tid & 7;
   const int tl0 = tb * 16 + w * 2;  // tokens tl0, tl0 + 1 of the tile
   float cf[2], l2[2], tg[2];
@@ -542,7 +546,7 @@ __global__ __launch_bounds__(256) void k_gpass_blk(const bf16* __restrict__ zblk
 #pragma unroll
   for (int p = 0; p < kSteps; ++p) {  // all loads in flight before any math
     const int vb = vbo + 8 * p;
-    zin[p] = (any && vb < nvb) ? *(const bf16x8*)(zsrc + (int64_t)vb * 64) : bf16x8{};
+    zin[p] = (any && vb < nvb) ? __builtin_nontemporal_load((const bf16x8*)(zsrc + (int64_t)vb * 64)) : bf16x8{};
   }
 #pragma unroll
   for (int p = 0; p < kSteps; ++p) {
@@ -556,7 +560,7 @@ __global__ __launch_bounds__(256) void k_gpass_blk(const bf16* __restrict__ zblk
         const int jl = vb * 4 + (e & 3);
         float v = 0.f;
         if (cf[q] != 0.f && j0 + jl < V) {
-          v = cf[q] * (fast_exp2(__builtin_fmaf((float)zv[e], kLog2e, -l2[q])) - epsV);
+          v = cf[q] * (fast_exp2(__builtin_fmaf((float)zv[e], zl2, -l2[q])) - epsV);
           if (jl == yc[q]) v -= tg[q];
         }
         out[q][e & 3] = (bf16)v;
@@ -579,7 +583,7 @@ __global__ __launch_bounds__(256) void k_gpass_blk(const bf16* __restrict__ zblk
   for (int p = 0; p < 8; ++p) {
     const int unit = tid + 256 * p;
     const int r = unit >> 5, c = unit & 31;
-    if (c < units) *(bf16x8*)(g + (i0 + r) * ldz + j0 + c * 8) = *(const bf16x8*)&tile[r][c * 8];
+    if (c < units) __builtin_nontemporal_store(*(const bf16x8*)&tile[r][c * 8], (bf16x8*)(g + (i0 + r) * ldz + j0 + c * 8));
   }
 }
 
