@@ -45,7 +45,8 @@ struct Plan {
   int splits = 1;
   size_t oD = 0, oWT = 0, oColpart = 0, oWsum = 0, oZt = 0, oR = 0, oLse = 0, oRloss = 0,
          oCoef = 0, oPart = 0, oRpart = 0, oZ = 0, oG = 0, oGT = 0, oHT = 0, oDHpart = 0,
-         oDW32 = 0, oRows = 0, oCount = 0, oLsec = 0, oTcol = 0, oBsum = 0, oDbpart = 0;
+         oDW32 = 0, oRows = 0, oCount = 0, oLsec = 0, oTcol = 0, oBsum = 0, oDbpart = 0,
+         oHC = 0;
   int64_t db_blocks = 0;  // row blocks of db partials (64 rows each, over all chunks)
   size_t total = 0;
 };
@@ -88,6 +89,7 @@ Plan make_plan(int mode, int64_t N, int64_t H, int64_t V, int dtype, int64_t chu
   p.oColpart = take(cur, (size_t)cdiv(V, kColSlab) * H * 4);
   p.oWsum = take(cur, (size_t)H * 4);
   p.oBsum = take(cur, 256);
+  if (bf) p.oHC = take(cur, (size_t)p.Cp * H * 2);  // gathered rows of h, the logits B operand
   p.oPart = take(cur, (size_t)p.nT * p.C * 8);
   p.oRpart = take(cur, (size_t)p.nT * p.C * 4);  // per-slab row sums of z (label smoothing)
   if (mode == kShardPartials) {
@@ -297,6 +299,7 @@ int run_core_bf16(const Core& c, const Plan& p, char* ws, hipStream_t st) {
   bf16* zb = reinterpret_cast<bf16*>(ws + p.oZ);
   bf16* gb = reinterpret_cast<bf16*>(ws + p.oG);
   bf16* hT = reinterpret_cast<bf16*>(ws + p.oHT);
+  bf16* hc = reinterpret_cast<bf16*>(ws + p.oHC);
   float* coef = reinterpret_cast<float*>(ws + p.oCoef);
   float* lsec = reinterpret_cast<float*>(ws + p.oLsec);
   int* tcol = reinterpret_cast<int*>(ws + p.oTcol);
@@ -324,18 +327,19 @@ int run_core_bf16(const Core& c, const Plan& p, char* ws, hipStream_t st) {
     {
       StageTimer tm(kHT, st);
       dim3 g((unsigned)(Cpc / 64), (unsigned)cdiv(H, 64));
-      k_transpose_gather_bf16<<<g, 256, 0, st>>>(h, c.rows, c.count, c0, cmax, H, hT, p.Cp, Cpc);
+      k_transpose_gather_bf16<<<g, 256, 0, st>>>(h, c.rows, c.count, c0, cmax, H, hT, p.Cp, Cpc,
+                                                 hc);
     }
     {  // 1. logits (+ softmax partials)
       StageTimer tm(kLogits, st);
       const int blocks = (int)(cdiv(V, kBM) * cdiv(cmax, kBN));
       if (c.lse_in == nullptr)
         k_logits_bf16<true, true><<<blocks, kGemmThreads, kGemmLds, st>>>(
-            W, bias, h, (int)V, (int)cmax, (int)H, c.s, c.rows, c.count, c0, part, c.rpart, p.C,
+            W, bias, hc, (int)V, (int)cmax, (int)H, c.s, nullptr, c.count, c0, part, c.rpart, p.C,
             zb, Vp, kGroupM);
       else
         k_logits_bf16<true, false><<<blocks, kGemmThreads, kGemmLds, st>>>(
-            W, bias, h, (int)V, (int)cmax, (int)H, c.s, c.rows, c.count, c0, part, nullptr, p.C,
+            W, bias, hc, (int)V, (int)cmax, (int)H, c.s, nullptr, c.count, c0, part, nullptr, p.C,
             zb, Vp, kGroupM);
     }
     // 2. per-row combine
@@ -670,12 +674,19 @@ int fldce_fwd(const void* h, const void* W, const void* bias, const int64_t* tar
   }
   const float Vf = (float)V;
   if (bf) {  // logits never stored: partials from the GEMM epilogue, valid rows only
+    bf16* hc = reinterpret_cast<bf16*>(ws + p.oHC);
+    {
+      StageTimer tm(kHT, st);
+      dim3 g((unsigned)(p.Cp / 64), (unsigned)cdiv(H, 64));
+      k_transpose_gather_bf16<<<g, 256, 0, st>>>((const bf16*)h, rows, count, 0, N, H, nullptr, 0,
+                                                 p.Cp, hc);
+    }
     {
       StageTimer tm(kLogits, st);
       const int blocks = (int)(cdiv(V, kBM) * cdiv(N, kBN));
       k_logits_bf16<false, true><<<blocks, kGemmThreads, kGemmLds, st>>>(
-          (const bf16*)W, (const bf16*)bias, (const bf16*)h, (int)V, (int)N, (int)H, logit_scale,
-          rows, count, 0, part, smooth ? rpart : nullptr, p.C, nullptr, 0, kGroupM);
+          (const bf16*)W, (const bf16*)bias, hc, (int)V, (int)N, (int)H, logit_scale, nullptr,
+          count, 0, part, smooth ? rpart : nullptr, p.C, nullptr, 0, kGroupM);
     }
     StageTimer tm(kCombine, st);
     k_combine_rows<<<grid1(N, 32), 256, 0, st>>>(
@@ -767,11 +778,18 @@ int fldce_shard_partials(const void* h, const void* W_local, const int64_t* targ
                                                          0.f);
     }
     const int blocks = (int)(cdiv(V, kBM) * cdiv(N, kBN));
+    bf16* hc = reinterpret_cast<bf16*>(ws + p.oHC);
+    {
+      StageTimer tm(kHT, st);
+      dim3 g((unsigned)(p.Cp / 64), (unsigned)cdiv(H, 64));
+      k_transpose_gather_bf16<<<g, 256, 0, st>>>((const bf16*)h, rows, count, 0, N, H, nullptr, 0,
+                                                 p.Cp, hc);
+    }
     {
       StageTimer tm(kLogits, st);
       k_logits_bf16<false, true><<<blocks, kGemmThreads, kGemmLds, st>>>(
-          (const bf16*)W_local, nullptr, (const bf16*)h, (int)V, (int)N, (int)H, logit_scale,
-          rows, count, 0, part, row_sumlogit ? rpart : nullptr, p.C, nullptr, 0, kGroupM);
+          (const bf16*)W_local, nullptr, hc, (int)V, (int)N, (int)H, logit_scale, nullptr, count,
+          0, part, row_sumlogit ? rpart : nullptr, p.C, nullptr, 0, kGroupM);
     }
     {
       StageTimer tm(kCombine, st);

@@ -293,8 +293,8 @@ __device__ __forceinline__ int acc_col(int wn, int j, int lane) { return wn * kT
 // ---------------------------------------------------------------------------
 //
 // Token rows: chunk token j (< the chunk's row count, read from `count` when
-// it is not null) is row rows[c0 + j] of h when rows != nullptr (compacted
-// chunk), else row c0 + j.  The grid covers cmax tokens; tiles past the
+// it is not null) is row rows[c0 + j] of h when rows != nullptr (gathered
+// here), else row j of h (h = the chunk's rows, already gathered).  The grid covers cmax tokens; tiles past the
 // count exit at once.
 template <bool kStoreZ, bool kPart>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_logits_bf16(
@@ -312,7 +312,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_logits_bf16(
   if (!tc.active) return;
   const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
   Acc acc;
-  gemm_mainloop<false, false>(W, H, V, 0, m0, h, H, C, 0, n0, 0, H / kBK, smem, acc, rows, c0);
+  gemm_mainloop<false, false>(W, H, V, 0, m0, h, H, C, 0, n0, 0, H / kBK, smem, acc, rows,
+                              rows != nullptr ? c0 : 0);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN;

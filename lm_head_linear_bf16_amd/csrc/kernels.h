@@ -193,15 +193,18 @@ __global__ __launch_bounds__(256) void k_transpose_bf16(const bf16* __restrict__
   }
 }
 
-// h^T of a compacted chunk: dst[c, j] = src[rows[c0 + j], c] for j < the
-// chunk's row count (device-side), 0 for the rest of the Rp columns.  Same
-// tiling as k_transpose_bf16.
+// Gathered chunk rows of h (row r of the chunk = source row rows[c0 + r],
+// r < the chunk's count; rows up to Rp are zero): hT [Cn, Rp] (ldd, when
+// dst != nullptr, the B operand of dW) and the row-major copy hc [Rp, Cn]
+// (when hc != nullptr, the B operand of the logits GEMM, so the GEMM reads
+// contiguous rows instead of chasing indices in every tile's prologue).
+// 64 x 64 tiles through LDS, 16-byte accesses (Cn % 8 == 0).
 __global__ __launch_bounds__(256) void k_transpose_gather_bf16(const bf16* __restrict__ src,
                                                                const int* __restrict__ rows,
                                                                const int* __restrict__ count,
                                                                int64_t c0, int64_t cmax, int64_t Cn,
                                                                bf16* __restrict__ dst, int64_t ldd,
-                                                               int64_t Rp) {
+                                                               int64_t Rp, bf16* __restrict__ hc) {
   __shared__ bf16 tile[64][64 + 8];
   const int tx = threadIdx.x & 7, ty = threadIdx.x >> 3;
   const int64_t R = chunk_rows(count, c0, cmax);
@@ -213,7 +216,9 @@ __global__ __launch_bounds__(256) void k_transpose_gather_bf16(const bf16* __res
     bf16x8 v = bf16x8{};
     if (r < R && c + 8 <= Cn) v = *(const bf16x8*)(src + (int64_t)rows[c0 + r] * Cn + c);
     *(bf16x8*)&tile[lr][tx * 8] = v;
+    if (hc != nullptr && r < Rp && c + 8 <= Cn) *(bf16x8*)(hc + r * Cn + c) = v;
   }
+  if (dst == nullptr) return;
   __syncthreads();
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
