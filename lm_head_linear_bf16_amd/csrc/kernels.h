@@ -268,13 +268,32 @@ __global__ __launch_bounds__(256) void k_rowdot(const T* __restrict__ h, const T
   const int64_t col = y - v0;
   const bool in = (y != ignore) && col >= 0 && col < Vl;
   float a = 0.f, b = 0.f;
+  if (!in && wsum == nullptr) {  // nothing to multiply on this row
+    if (lane == 0) {
+      if (zt != nullptr) zt[row] = 0.f;
+      if (R != nullptr) R[row] = bsum != nullptr ? s * *bsum : 0.f;
+    }
+    return;
+  }
   const T* hr = h + row * H;
   const T* wr = W + (in ? col : 0) * H;
-  for (int64_t k = lane; k < H; k += 64) {
-    const float x = to_f32(hr[k]);
-    if (in) a += x * to_f32(wr[k]);
-    if (wsum != nullptr) b += x * wsum[k];
+  bool done = false;
+  if constexpr (sizeof(T) == 2) {
+    if (wsum == nullptr && (H & 7) == 0) {  // 16-byte loads: a wave reads 1 KB per step
+      for (int64_t k = (int64_t)lane * 8; k < H; k += 512) {
+        const bf16x8 xv = *(const bf16x8*)(hr + k), wv = *(const bf16x8*)(wr + k);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a += (float)xv[e] * (float)wv[e];
+      }
+      done = true;
+    }
   }
+  if (!done)
+    for (int64_t k = lane; k < H; k += 64) {
+      const float x = to_f32(hr[k]);
+      if (in) a += x * to_f32(wr[k]);
+      if (wsum != nullptr) b += x * wsum[k];
+    }
   a = wave_sum(a);
   b = wave_sum(b);
   if (lane == 0) {
@@ -342,12 +361,29 @@ __global__ __launch_bounds__(256) void k_combine_rows(
   const int64_t C = chunk_rows(count, c0, cmax);
   const int64_t j = (int64_t)blockIdx.x * 32 + tx;
   float m = -INFINITY, sum = 0.f, rsum = 0.f;
-  if (j < C)
-    for (int64_t t = grp; t < nT; t += 8) {
-      const floatx2 p = part[t * ldp + j];
-      lse_merge(m, sum, p[0], p[1]);
+  if (j < C) {
+    // slabs grp, grp + 8, ... in order; eight loads in flight per batch
+    int64_t t = grp;
+    for (; t + 56 < nT; t += 64) {
+      floatx2 pv[8];
+      float rv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        pv[u] = part[(t + 8 * u) * ldp + j];
+        rv[u] = rpart != nullptr ? rpart[(t + 8 * u) * ldp + j] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        lse_merge(m, sum, pv[u][0], pv[u][1]);
+        rsum += rv[u];
+      }
+    }
+    for (; t < nT; t += 8) {
+      const floatx2 pv = part[t * ldp + j];
+      lse_merge(m, sum, pv[0], pv[1]);
       if (rpart != nullptr) rsum += rpart[t * ldp + j];
     }
+  }
   sm[grp][tx] = m;
   ss[grp][tx] = sum;
   sr[grp][tx] = rsum;
@@ -499,17 +535,23 @@ __global__ __launch_bounds__(256) void k_gpass(T* __restrict__ z, int64_t ldz, i
 // row-major [rows, ldz] for both backward GEMMs.  Chunk rows are given by the
 // device-side count (chunk_rows); rows C .. round_up(C, 64) - 1 and columns
 // >= V are written as zeros.  lse, coef and tcol are per chunk row.  With
-// dbpart, block (x, y) also writes the column sums of its 64 rows of g (as
-// stored, bf16) to dbpart[y * ldz + column], zeros for blocks past the rows.
+// dbpart, block (x, y) also writes the column sums of its kGpassTok rows of g
+// (as stored, bf16) to dbpart[y * ldz + column], zeros for blocks past the
+// rows.
 //
-// One block = 64 tokens x 256 columns, 256 threads.  Thread -> two fixed
-// tokens (their lse, coefficient and target stay in registers) and eight
-// 16-byte units of z (a wave reads 1 KB contiguous per step); g goes out
-// through LDS as 512-byte row segments.  z is read once and g is read by the
+// One block = kGpassTok tokens x kGpassCols columns, 256 threads.  Thread ->
+// two fixed tokens (their lse, coefficient and target stay in registers) and
+// eight 16-byte units of z (a wave reads 1 KB contiguous per step); g goes
+// out through LDS as row segments of 2 * kGpassCols bytes.  z is read once and g is read by the
 // next kernels from HBM anyway (1.4 GB each at the 4B-scale sizes, far past
 // the caches), so both use non-temporal accesses.
 // ---------------------------------------------------------------------------
-constexpr int kGpassCols = 256;
+#ifndef GPASS_TOK
+#define GPASS_TOK 16
+#define GPASS_COLS 1024
+#endif
+constexpr int kGpassTok = GPASS_TOK;    // tokens per block (a multiple of 16 dividing 64)
+constexpr int kGpassCols = GPASS_COLS;  // vocabulary columns per block
 __global__ __launch_bounds__(256) void k_gpass_blk(const bf16* __restrict__ zblk, int64_t ldz,
                                                    int64_t cmax, const int* __restrict__ count,
                                                    int64_t c0, int64_t V,
@@ -518,20 +560,26 @@ __global__ __launch_bounds__(256) void k_gpass_blk(const bf16* __restrict__ zblk
                                                    const int* __restrict__ tcol, float eps,
                                                    float Vg, bf16* __restrict__ g,
                                                    float* __restrict__ dbpart, float zscale) {
-  __shared__ bf16 tile[64][kGpassCols + 8];  // [token][column]
+  constexpr int kTG = kGpassTok / 16;      // 16-token groups of the blocked layout
+  constexpr int kVBO = 32 / kTG;           // column blocks a thread row covers per step
+  constexpr int kSteps = kGpassCols / 4 / kVBO;
+  constexpr int kUnits = kGpassCols / 8;   // 16-byte units per token row
+  static_assert(kGpassTok * kUnits == 256 * 8, "eight 16-byte output units per thread");
+  __shared__ bf16 tile[kGpassTok][kGpassCols + 8];  // [token][column]
   const int tid = threadIdx.x;
   const int64_t C = chunk_rows(count, c0, cmax);
-  const int64_t i0 = (int64_t)blockIdx.y * 64, j0 = (int64_t)blockIdx.x * kGpassCols;
+  const int64_t i0 = (int64_t)blockIdx.y * kGpassTok, j0 = (int64_t)blockIdx.x * kGpassCols;
   const int64_t nvb = min((int64_t)kGpassCols / 4, (ldz - j0) / 4);  // column blocks in range
   // dbpart (when not null): this block's column sums of g, row block y
   float* dbrow = dbpart != nullptr ? dbpart + (int64_t)blockIdx.y * ldz + j0 : nullptr;
   if (i0 >= round_up(C, 64)) {  // rows past the chunk's padded count are never read
-    if (dbrow != nullptr && tid < nvb * 4) dbrow[tid] = 0.f;
+    if (dbrow != nullptr)
+      for (int col = tid; col < nvb * 4; col += 256) dbrow[col] = 0.f;
     return;
   }
   const float epsV = eps / Vg;
   const float zl2 = zscale * kLog2e;
-  const int tb = tid >> 6, vbo = (tid >> 3) & 7, w = tid & 7;
+  const int tb = tid / (256 / kTG), vbo = (tid >> 3) % kVBO, w = tid & 7;
   const int tl0 = tb * 16 + w * 2;  // tokens tl0, tl0 + 1 of the tile
   float cf[2], l2[2], tg[2];
   int64_t yc[2];
@@ -546,16 +594,15 @@ __global__ __launch_bounds__(256) void k_gpass_blk(const bf16* __restrict__ zblk
     any |= cf[q] != 0.f;
   }
   const bf16* zsrc = zblk + ((i0 / 16 + tb) * (ldz >> 2) + j0 / 4) * 64 + w * 8;
-  constexpr int kSteps = kGpassCols / 32;
   bf16x8 zin[kSteps];
 #pragma unroll
   for (int p = 0; p < kSteps; ++p) {  // all loads in flight before any math
-    const int vb = vbo + 8 * p;
+    const int vb = vbo + kVBO * p;
     zin[p] = (any && vb < nvb) ? __builtin_nontemporal_load((const bf16x8*)(zsrc + (int64_t)vb * 64)) : bf16x8{};
   }
 #pragma unroll
   for (int p = 0; p < kSteps; ++p) {
-    const int vb = vbo + 8 * p;  // column block (4 columns) within the tile
+    const int vb = vbo + kVBO * p;  // column block (4 columns) within the tile
     bf16x4 out[2] = {bf16x4{}, bf16x4{}};
     if (any) {
       const bf16x8 zv = zin[p];
@@ -577,17 +624,18 @@ __global__ __launch_bounds__(256) void k_gpass_blk(const bf16* __restrict__ zblk
     }
   }
   __syncthreads();
-  if (dbrow != nullptr && tid < nvb * 4) {  // page 1: db += c_logits.sum(0)
-    float acc = 0.f;
+  if (dbrow != nullptr)  // page 1: db += c_logits.sum(0)
+    for (int col = tid; col < nvb * 4; col += 256) {
+      float acc = 0.f;
 #pragma unroll 8
-    for (int r = 0; r < 64; ++r) acc += (float)tile[r][tid];
-    dbrow[tid] = acc;
-  }
+      for (int r = 0; r < kGpassTok; ++r) acc += (float)tile[r][col];
+      dbrow[col] = acc;
+    }
   const int units = (int)nvb / 2;  // 16-byte units per token row in range
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
     const int unit = tid + 256 * p;
-    const int r = unit >> 5, c = unit & 31;
+    const int r = unit / kUnits, c = unit % kUnits;
     if (c < units) __builtin_nontemporal_store(*(const bf16x8*)&tile[r][c * 8], (bf16x8*)(g + (i0 + r) * ldz + j0 + c * 8));
   }
 }
