@@ -468,6 +468,36 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dw_bf16(
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN;
+  if constexpr (kMode == 0) {
+    // Stage the bf16 tile in LDS (free after the main loop) and write it out
+    // as 512-byte rows: the accumulator layout alone only gives 32-byte row
+    // pieces per store.  16-byte chunk ch of tile row r sits at ch ^ sw(r),
+    // which keeps both the 2-byte writes and the 16-byte reads conflict-free.
+    bf16* stg = reinterpret_cast<bf16*>(smem);  // [256][256]
+    auto sw = [](int r) { return ((r >> 2) & 3) << 1; };
+    __syncthreads();  // every wave is done reading the operand stages
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+      for (int j = 0; j < kTN; ++j) {
+        const int cl = acc_col(wn, j, lane);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int rl = acc_row(wm, i, lane, r);
+          stg[rl * kBN + (((cl >> 3) ^ sw(rl)) << 3) + (cl & 7)] = (bf16)acc[i][j][r];
+        }
+      }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < kBM * kBN / 8 / kGemmThreads; ++p) {
+      const int u = threadIdx.x + kGemmThreads * p;
+      const int rl = u / (kBN / 8), ch = u % (kBN / 8);
+      const int row = m0 + rl, col = n0 + ch * 8;
+      if (row < V && col < H)  // H % 64 == 0: a chunk is wholly in or out
+        *(bf16x8*)(out + (int64_t)row * H + col) = *(const bf16x8*)&stg[rl * kBN + ((ch ^ sw(rl)) << 3)];
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < kTM; ++i)
 #pragma unroll
@@ -479,8 +509,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dw_bf16(
         if (row < V && col < H) {
           const int64_t e = (int64_t)row * H + col;
           const float v = acc[i][j][r];
-          if (kMode == 0) out[e] = (bf16)v;
-          else if (kMode == 1) acc32[e] = v;
+          if (kMode == 1) acc32[e] = v;
           else if (kMode == 2) acc32[e] += v;
           else out[e] = (bf16)(acc32[e] + v);
         }
