@@ -83,8 +83,9 @@ def _counter_per_kernel(path: str, counter: str) -> dict:
     return out
 
 
-STAGE_KERNELS = {"logits_gemm": "k_logits_bf16", "dH_gemm": "k_gemm_dh_bf16",
-                 "dW_gemm": "k_gemm_dw_bf16", "dlogits": "k_gpass_blk"}
+# the kernel instance each stage of the plain fwd+bwd call launches
+STAGE_KERNELS = {"logits_gemm": "k_logits_bf16<true, true>", "dH_gemm": "k_gemm_dh_bf16",
+                 "dW_gemm": "k_gemm_dw_bf16<0>", "dlogits": "k_gpass_blk<16, 1024>"}
 
 
 def traffic_summary(fetch_csv: str, write_csv: str, workload: str, calib_mib: int) -> int:
@@ -104,7 +105,7 @@ def traffic_summary(fetch_csv: str, write_csv: str, workload: str, calib_mib: in
     lines = [f"# HBM traffic per launch, {workload} workload",
              "",
              "FETCH_SIZE and WRITE_SIZE (KiB per dispatch) from two rocprofv3 --pmc runs of",
-             f"`bench.py --workload {workload} --steps 2 --warmup 1 --no-cpu-baseline --calib-copy-mib {calib_mib}`,",
+             f"`bench.py --workload {workload} --steps 2 --warmup 1 --no-cpu-baseline --no-extras --calib-copy-mib {calib_mib}`,",
              f"scaled by the calibration copy of {calib_mib} MiB (read scale {cf:.4f}, write scale {cw:.4f}).",
              "",
              "| stage | kernel | fetch GB/launch | write GB/launch | launches |",

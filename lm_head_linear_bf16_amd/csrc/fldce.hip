@@ -121,9 +121,8 @@ Plan make_plan(int mode, int64_t N, int64_t H, int64_t V, int dtype, int64_t chu
     p.oGT = take(cur, (size_t)p.Vp * p.Cp * p.esz);
   }
   p.oHT = take(cur, (size_t)H * p.Cp * p.esz);
-  if (mode == kFwdBwd) {  // db partials: bf16 per kGpassTok rows of a chunk (the chunk's
-                          // rows padded to 64), fp32 per kColSlab rows
-    p.db_blocks = (cdiv(std::max<int64_t>(N, 1), 64) + p.nchunks) * (64 / kGpassTok);
+  if (mode == kFwdBwd) {  // db partials: bf16 per 64 rows of a chunk, fp32 per kColSlab rows
+    p.db_blocks = cdiv(std::max<int64_t>(N, 1), 64) + p.nchunks;
     p.oDbpart = take(cur, (size_t)p.db_blocks * p.Vp * 4);
   }
   if (bf) {
@@ -347,11 +346,17 @@ int run_core_bf16(const Core& c, const Plan& p, char* ws, hipStream_t st) {
     run_rows(c, p, part, coef, lsec, tcol, c0, cmax, st);
     {  // 3. dlogits: blocked z -> row-major g, zero rows up to the padded count
       StageTimer tm(kDlogits, st);
-      dim3 g((unsigned)cdiv(Vp, kGpassCols), (unsigned)(Cpc / kGpassTok));
-      k_gpass_blk<<<g, 256, 0, st>>>(zb, Vp, cmax, c.count, c0, V, lsec, coef, tcol, c.eps,
-                                     (float)c.Vg, gb,
-                                     c.db != nullptr ? c.dbpart + db_off * Vp : nullptr, c.s);
-      db_off += Cpc / kGpassTok;
+      if (c.db == nullptr) {
+        dim3 g((unsigned)cdiv(Vp, 1024), (unsigned)(Cpc / 16));
+        k_gpass_blk<16, 1024><<<g, 256, 0, st>>>(zb, Vp, cmax, c.count, c0, V, lsec, coef, tcol,
+                                                 c.eps, (float)c.Vg, gb, nullptr, c.s);
+      } else {  // db partials per 64 rows
+        dim3 g((unsigned)cdiv(Vp, 256), (unsigned)(Cpc / 64));
+        k_gpass_blk<64, 256><<<g, 256, 0, st>>>(zb, Vp, cmax, c.count, c0, V, lsec, coef, tcol,
+                                                c.eps, (float)c.Vg, gb, c.dbpart + db_off * Vp,
+                                                c.s);
+        db_off += Cpc / 64;
+      }
     }
     {  // 4. dH = g W (split over the vocabulary, ordered reduction, scattered rows)
       const int S = p.splits;

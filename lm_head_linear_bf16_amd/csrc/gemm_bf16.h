@@ -322,12 +322,22 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_logits_bf16(
   const bool full = vbase + kTM * 16 <= V;
   const float sl = s * kLog2e;
   if (bias != nullptr) {  // F.linear's bias, before the logit scale
+    bf16x4 bv[kTM];  // rows row0 .. row0 + 3 of sub-tile i (row0 % 4 == 0): one 8-byte load
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) {
+      const int row0 = m0 + acc_row(wm, i, lane, 0);
+      if (row0 + 3 < V) {
+        bv[i] = *(const bf16x4*)(bias + row0);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) bv[i][r] = row0 + r < V ? bias[row0 + r] : (bf16)0.f;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < kTM; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = m0 + acc_row(wm, i, lane, r);
-        const float b = row < V ? (float)bias[row] : 0.f;
+        const float b = (float)bv[i][r];
 #pragma unroll
         for (int j = 0; j < kTN; ++j) acc[i][j][r] += b;
       }

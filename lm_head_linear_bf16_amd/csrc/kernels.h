@@ -239,7 +239,15 @@ __global__ __launch_bounds__(256) void k_colsum_finish(const float* __restrict__
   const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (c >= Cn) return;
   float s = 0.f;
-  for (int64_t b = 0; b < nb; ++b) s += part[b * ld + c];
+  int64_t b = 0;
+  for (; b + 8 <= nb; b += 8) {  // eight loads in flight, added in order
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = part[(b + u) * ld + c];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; b < nb; ++b) s += part[b * ld + c];
   out[c] = from_f32<T>(s);
 }
 
@@ -539,19 +547,16 @@ __global__ __launch_bounds__(256) void k_gpass(T* __restrict__ z, int64_t ldz, i
 // (as stored, bf16) to dbpart[y * ldz + column], zeros for blocks past the
 // rows.
 //
-// One block = kGpassTok tokens x kGpassCols columns, 256 threads.  Thread ->
-// two fixed tokens (their lse, coefficient and target stay in registers) and
-// eight 16-byte units of z (a wave reads 1 KB contiguous per step); g goes
-// out through LDS as row segments of 2 * kGpassCols bytes.  z is read once and g is read by the
-// next kernels from HBM anyway (1.4 GB each at the 4B-scale sizes, far past
-// the caches), so both use non-temporal accesses.
+// One block = kGpassTok tokens (a multiple of 16 dividing 64) x kGpassCols
+// columns, 256 threads (16 x 1024 streams best; 64 x 256 when db is wanted,
+// so the column-sum partials cover 64 rows each).  Thread -> two fixed
+// tokens (their lse, coefficient and target stay in registers) and eight
+// 16-byte units of z (a wave reads 1 KB contiguous per step); g goes out
+// through LDS as row segments of 2 * kGpassCols bytes.  z is read once and g
+// is read by the next kernels from HBM anyway (1.4 GB each at the 4B-scale
+// sizes, far past the caches), so both use non-temporal accesses.
 // ---------------------------------------------------------------------------
-#ifndef GPASS_TOK
-#define GPASS_TOK 16
-#define GPASS_COLS 1024
-#endif
-constexpr int kGpassTok = GPASS_TOK;    // tokens per block (a multiple of 16 dividing 64)
-constexpr int kGpassCols = GPASS_COLS;  // vocabulary columns per block
+template <int kGpassTok, int kGpassCols>
 __global__ __launch_bounds__(256) void k_gpass_blk(const bf16* __restrict__ zblk, int64_t ldz,
                                                    int64_t cmax, const int* __restrict__ count,
                                                    int64_t c0, int64_t V,
