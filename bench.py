@@ -61,8 +61,8 @@ def traffic_entry(kernel: str, workload: str):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    e = t.get(kernel)
-    if not e or e.get("src_hash") != src_hash() or e.get("workload") != workload:
+    e = t.get(workload, {}).get(kernel)
+    if not e or e.get("src_hash") != src_hash():
         return None
     return e.get("bytes_per_launch")
 
@@ -83,9 +83,16 @@ def _counter_per_kernel(path: str, counter: str) -> dict:
     return out
 
 
-# the kernel instance each stage of the plain fwd+bwd call launches
+# the kernel instance each stage launches: plain fwd+bwd, and for the vocab
+# shard workload the shard partials and the shard backward
 STAGE_KERNELS = {"logits_gemm": "k_logits_bf16<true, true>", "dH_gemm": "k_gemm_dh_bf16",
                  "dW_gemm": "k_gemm_dw_bf16<0>", "dlogits": "k_gpass_blk<16, 1024>"}
+SHARD_STAGE_KERNELS = {"partials_logits": "k_logits_bf16<false, true>",
+                       "bwd_logits": "k_logits_bf16<true, false>", "dH_gemm": "k_gemm_dh_bf16",
+                       "dW_gemm": "k_gemm_dw_bf16<0>", "dlogits": "k_gpass_blk<16, 1024>"}
+
+
+WORKLOAD_NAMES = ("tiny", "4b", "headline", "block", "shard")
 
 
 def traffic_summary(fetch_csv: str, write_csv: str, workload: str, calib_mib: int) -> int:
@@ -101,16 +108,25 @@ def traffic_summary(fetch_csv: str, write_csv: str, workload: str, calib_mib: in
     known_kib = calib_mib * 1024.0
     cf = known_kib / max(fetch[calib[0]])
     cw = known_kib / max(write[calib[0]])
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            everything = json.load(f)
+    except (OSError, ValueError):
+        everything = {}
+    everything = {k: v for k, v in everything.items() if k in WORKLOAD_NAMES}
     out = {}
     lines = [f"# HBM traffic per launch, {workload} workload",
              "",
              "FETCH_SIZE and WRITE_SIZE (KiB per dispatch) from two rocprofv3 --pmc runs of",
-             f"`bench.py --workload {workload} --steps 2 --warmup 1 --no-cpu-baseline --no-extras --calib-copy-mib {calib_mib}`,",
+             f"`bench.py --workload {workload} --steps 2 --warmup 1 --no-cpu-baseline --no-extras --calib-copy-mib {calib_mib}`",
+             "(`rocprofv3 --pmc FETCH_SIZE` and `--pmc WRITE_SIZE`, each `-- python3 bench.py ...`),",
              f"scaled by the calibration copy of {calib_mib} MiB (read scale {cf:.4f}, write scale {cw:.4f}).",
              "",
              "| stage | kernel | fetch GB/launch | write GB/launch | launches |",
              "|---|---|---|---|---|"]
-    for stage, kname in STAGE_KERNELS.items():
+    kernels = SHARD_STAGE_KERNELS if workload == "shard" else STAGE_KERNELS
+    for stage, kname in kernels.items():
         fk = [k for k in fetch if kname in k]
         wk = [k for k in write if kname in k]
         if not fk or not wk:
@@ -119,13 +135,14 @@ def traffic_summary(fetch_csv: str, write_csv: str, workload: str, calib_mib: in
         wv = [v for k in wk for v in write[k]]
         fb = sum(fv) / len(fv) * 1024 * cf
         wb = sum(wv) / len(wv) * 1024 * cw
-        out[stage] = {"workload": workload, "src_hash": src_hash(), "fetch_bytes": fb,
+        out[stage] = {"kernel": kname, "src_hash": src_hash(), "fetch_bytes": fb,
                       "write_bytes": wb, "bytes_per_launch": fb + wb, "launches": len(fv),
                       "read_scale": cf, "write_scale": cw}
         lines.append(f"| {stage} | {kname} | {fb / 1e9:.3f} | {wb / 1e9:.3f} | {len(fv)} |")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
-        json.dump(out, f, indent=1)
+    everything[workload] = out
+    with open(path, "w") as f:
+        json.dump(everything, f, indent=1)
     with open(os.path.join(ROOT, "profiles", f"{workload}_traffic.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -220,6 +237,90 @@ def extra_legs(args, w, h, W, tgt, pm, dt, rows_mult: int, ms_plain: float, peak
     return out
 
 
+def shard_bench(args, w) -> int:
+    """One GPU's share of the vocabulary-split LM head (the shard workload:
+    N=32768, H=5120, shard k=3 of 8, 18992 vocabulary rows): one step =
+    fldce_shard_partials (softmax partials of the shard, logits never stored)
+    + fldce_shard_bwd (dH_partial, dW_local given the rows' lse).  The
+    exchange of partials between GPUs is not part of a one-GPU step; the lse
+    passed to the backward is the shard's own (timing does not depend on its
+    values)."""
+    import numpy as np
+    import torch
+    from lm_head_linear_bf16_amd import fldce, synth
+    N, H, Vl, v0 = w.N, w.H, w.V_local, w.vocab_start
+    dev = torch.device("cuda:0")
+    log(f"workload {w.name}: N={N} H={H} V_local={Vl} (shard {w.shard_k} of {w.shards}); inputs")
+    target, p_mask = synth.targets(w)
+
+    def dev_t(t):
+        return torch.from_numpy(t.bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    if args.calib_copy_mib:
+        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
+        del src
+    h, W = dev_t(synth.hidden(w)), dev_t(synth.weight(w, shard=w.shard_k))
+    tgt, pm = torch.from_numpy(target).to(dev), torch.from_numpy(p_mask).to(dev)
+    dt = torch.bfloat16
+    ws_p = torch.empty(fldce.fldce_shard_partials_workspace_size(N, H, Vl, dt), dtype=torch.uint8,
+                       device=dev)
+    ws_b = torch.empty(fldce.fldce_shard_bwd_workspace_size(N, H, Vl, dt), dtype=torch.uint8,
+                       device=dev)
+    r = fldce.fldce_shard_partials(h, W, tgt, v0, logit_scale=w.logit_scale, workspace=ws_p)
+    lse = (r["row_max"] + torch.log(r["row_sumexp"])).nan_to_num(0.0, 0.0, 0.0).contiguous()
+    kw = dict(label_smoothing=w.label_smoothing, logit_scale=w.logit_scale,
+              reduction=w.reduction, total=w.total)
+
+    def partials():
+        return fldce.fldce_shard_partials(h, W, tgt, v0, logit_scale=w.logit_scale,
+                                          sumlogit=w.label_smoothing > 0, workspace=ws_p)
+
+    def bwd():
+        return fldce.fldce_shard_bwd(h, W, tgt, pm, lse, v0, w.V, workspace=ws_b, **kw)
+
+    log(f"timing {args.steps} steps after {args.warmup} warmup")
+    mp, sp = _timed(partials, args.steps, args.warmup)
+    mb, sb = _timed(bwd, args.steps, args.warmup)
+    ms = mp + mb
+    n_valid = int(np.count_nonzero(target != synth.IGNORE_INDEX))
+    peak = PEAK_BF16_TFLOPS
+    gemm = 2.0 * n_valid * H * Vl              # one GEMM over the shard, valid rows
+    # dominant kernel: the slowest GEMM stage of either call
+    cands = {"partials_logits": sp.get("logits_gemm", 0.0), "bwd_logits": sb.get("logits_gemm", 0.0),
+             "dH_gemm": sb.get("dH_gemm", 0.0), "dW_gemm": sb.get("dW_gemm", 0.0)}
+    dom = max(cands, key=cands.get)
+    achieved = gemm / (cands[dom] * 1e-3) / 1e12
+    result = {
+        "metric": "fused LM-head CE fwd+bwd tokens/s and TFLOP/s (% bf16 MFMA peak), 1 GPU",
+        "value": round(N / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": (f"shard: B={w.B} L={w.L} (N={N}) H={H} V_local={Vl} "
+                                f"(shard {w.shard_k} of {w.shards} of V={w.V}) eps={w.label_smoothing} "
+                                f"s={w.logit_scale}, shard partials + shard backward"),
+                   "global_batch": w.B, "seq_len": w.L, "parallelism": "one vocabulary shard"},
+        "tflops": round(4 * gemm / (ms * 1e-3) / 1e12, 2),
+        "pct_peak": round(100.0 * 4 * gemm / (ms * 1e-3) / 1e12 / peak, 2),
+        "rows_multiplied": n_valid,
+        "partials": {"ms": round(mp, 4), "tflops": round(gemm / (mp * 1e-3) / 1e12, 2),
+                     "stage_ms": sp,
+                     "traffic_bytes": traffic_entry("partials_logits", "shard"),
+                     "algorithmic_bytes": 2 * (N * H + Vl * H) + 16 * N},
+        "backward": {"ms": round(mb, 4), "tflops": round(3 * gemm / (mb * 1e-3) / 1e12, 2),
+                     "stage_ms": sb},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic_entry(dom, "shard"), "avg_launch_ms": cands[dom],
+                     "flops_per_launch": gemm},
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -254,6 +355,8 @@ def main() -> int:
     from lm_head_linear_bf16_amd import fldce, synth
 
     w = synth.WORKLOADS[args.workload]
+    if w.shards > 1:
+        return shard_bench(args, w)
     N, H, V = w.N, w.H, w.V
     dev = torch.device("cuda:0")
     log(f"workload {w.name}: N={N} H={H} V={V} {w.dtype}; generating inputs")
