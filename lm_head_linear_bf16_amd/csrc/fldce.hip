@@ -365,10 +365,13 @@ int run_core_bf16(const Core& c, const Plan& p, char* ws, hipStream_t st) {
         StageTimer tm(kDHGemm, st);
         k_gemm_dh_bf16<<<blocks, kGemmThreads, kGemmLds, st>>>(gb, Vp, (int)cmax, c.count, c0, W,
                                                                (int)V, (int)H, (int)(Vp / kBK), S,
-                                                               dHpart, kGroupMBwd);
+                                                               dHpart, kGroupMBwd, c.dH,
+                                                               c.dH_f32 ? 1 : 0, c.rows);
       }
       StageTimer tm(kDHReduce, st);
-      if (c.dH_f32)
+      if (S == 1) {
+        // at most one split: the GEMM wrote dH itself
+      } else if (c.dH_f32)
         k_splitk_scatter<float><<<(unsigned)cmax, 256, 0, st>>>(
             dHpart, S, Vp / kBK, cmax, H, c.rows, c.count, c0, (float*)c.dH);
       else

@@ -409,10 +409,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_logits_bf16(
 // M = chunk tokens: the grid covers M (upper bound) x max_splits; the tokens
 // that exist are min(*count - c0, M) when count != nullptr, and the split
 // count is chosen for them (choose_splits; k_splitk_scatter recomputes it).
+// With a single split there is nothing to reduce: the epilogue writes row m
+// straight to row rows[c0 + m] of dst (fp32 when dst_f32, else bf16) and the
+// reduction kernel returns at once.
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dh_bf16(
     const bf16* __restrict__ g, int64_t ldg, int M, const int* __restrict__ count, int64_t c0,
     const bf16* __restrict__ W, int V, int H, int k_tiles, int max_splits, float* __restrict__ out,
-    int group_m) {
+    int group_m, void* __restrict__ dst, int dst_f32, const int* __restrict__ rows) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   int Me = M;
   if (count != nullptr) {
@@ -430,6 +433,24 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dh_bf16(
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN;
+  if (splits == 1) {  // nothing to reduce: rows go straight to their place in dH
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = m0 + acc_row(wm, i, lane, r);
+        if (row >= Me) continue;
+        const int64_t drow = (int64_t)rows[c0 + row] * H;
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) {
+          const int col = n0 + acc_col(wn, j, lane);
+          if (col >= H) continue;
+          if (dst_f32) static_cast<float*>(dst)[drow + col] = acc[i][j][r];
+          else static_cast<bf16*>(dst)[drow + col] = (bf16)acc[i][j][r];
+        }
+      }
+    return;
+  }
   float* o = out + (int64_t)tc.split * M * H;
 #pragma unroll
   for (int i = 0; i < kTM; ++i)
