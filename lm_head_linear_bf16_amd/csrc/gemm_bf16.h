@@ -389,7 +389,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_logits_bf16(
         for (int r = 0; r < 4; ++r) v[r] = (bf16)acc[i][j][r];
         bf16* dst = zt + (int64_t)(row0 >> 2) * 64;
         if (full || row0 + 3 < V) {
-          *(bf16x4*)dst = v;
+          __builtin_nontemporal_store(v, (bf16x4*)dst);  // read once, by dlogits
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
@@ -460,7 +460,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dh_bf16(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = m0 + acc_row(wm, i, lane, r);
-        if (row < Me && col < H) o[(int64_t)row * H + col] = acc[i][j][r];
+        if (row < Me && col < H) o[(int64_t)row * H + col] = acc[i][j][r];  // re-read from the MALL
       }
     }
 }
@@ -525,7 +525,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dw_bf16(
       const int rl = u / (kBN / 8), ch = u % (kBN / 8);
       const int row = m0 + rl, col = n0 + ch * 8;
       if (row < V && col < H)  // H % 64 == 0: a chunk is wholly in or out
-        *(bf16x8*)(out + (int64_t)row * H + col) = *(const bf16x8*)&stg[rl * kBN + ((ch ^ sw(rl)) << 3)];
+        __builtin_nontemporal_store(*(const bf16x8*)&stg[rl * kBN + ((ch ^ sw(rl)) << 3)],
+                                    (bf16x8*)(out + (int64_t)row * H + col));
     }
     return;
   }
