@@ -605,23 +605,36 @@ __global__ __launch_bounds__(256) void k_gpass_blk(const bf16* __restrict__ zblk
     const int vb = vbo + kVBO * p;
     zin[p] = (any && vb < nvb) ? __builtin_nontemporal_load((const bf16x8*)(zsrc + (int64_t)vb * 64)) : bf16x8{};
   }
+  const bool inside = j0 + kGpassCols <= V;  // no column of this tile is past V
+  float ce[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) ce[q] = cf[q] * epsV;
 #pragma unroll
   for (int p = 0; p < kSteps; ++p) {
     const int vb = vbo + kVBO * p;  // column block (4 columns) within the tile
     bf16x4 out[2] = {bf16x4{}, bf16x4{}};
-    if (any) {
-      const bf16x8 zv = zin[p];
+    const bf16x8 zv = zin[p];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int q = e >> 2;
-        const int jl = vb * 4 + (e & 3);
-        float v = 0.f;
-        if (cf[q] != 0.f && j0 + jl < V) {
-          v = cf[q] * (fast_exp2(__builtin_fmaf((float)zv[e], zl2, -l2[q])) - epsV);
-          if (jl == yc[q]) v -= tg[q];
-        }
-        out[q][e & 3] = (bf16)v;
+    for (int q = 0; q < 2; ++q) {
+      if (cf[q] == 0.f) continue;  // ignored or padding row: stays +0
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        v[e] = __builtin_fmaf(cf[q], fast_exp2(__builtin_fmaf((float)zv[q * 4 + e], zl2, -l2[q])),
+                              -ce[q]);
+      const int64_t d = yc[q] - vb * 4;  // the target column, when it is in this block
+      if (d >= 0 && d < 4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (e == d) v[e] -= tg[q];
       }
+      if (!inside) {  // after the target: a shard's out-of-range target column may fall here
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (j0 + vb * 4 + e >= V) v[e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[q][e] = (bf16)v[e];
     }
     if (vb < nvb) {
 #pragma unroll
