@@ -611,12 +611,11 @@ int fldce_fwd_bwd_ex(const void* h, const void* W, const void* bias, const int64
          false, dW, db, dbpart, eob_token_id, eob_weight};
   {
     StageTimer tm(kPrep, st);
-    k_divisor<<<1, 1024, 0, st>>>(target, N, ignore_index, reduction, total, D);
-    if (bf) {
-      k_compact_rows<<<1, 1024, 0, st>>>(target, N, ignore_index, rows, count);
-      k_ignored_rows_init<<<grid1(N, 256), 256, 0, st>>>(target, N, ignore_index, lse, 0.f, rl, 0.f,
-                                                         nullptr, 0.f);
-    }
+    if (bf)
+      k_prep_rows<<<1, 1024, 0, st>>>(target, N, ignore_index, rows, count, reduction, total, D,
+                                      lse, 0.f, rl, 0.f, nullptr, 0.f);
+    else
+      k_divisor<<<1, 1024, 0, st>>>(target, N, ignore_index, reduction, total, D);
     launch_row_dots(h, W, bias, target, N, H, V, bf, ignore_index, logit_scale, smooth, colpart,
                     wsum, bsum, zt, R, st);
   }
@@ -672,12 +671,11 @@ int fldce_fwd(const void* h, const void* W, const void* bias, const int64_t* tar
   int* count = reinterpret_cast<int*>(ws + p.oCount);
   {
     StageTimer tm(kPrep, st);
-    k_divisor<<<1, 1024, 0, st>>>(target, N, ignore_index, reduction, total, D);
-    if (bf) {
-      k_compact_rows<<<1, 1024, 0, st>>>(target, N, ignore_index, rows, count);
-      k_ignored_rows_init<<<grid1(N, 256), 256, 0, st>>>(target, N, ignore_index, lse, 0.f, rl, 0.f,
-                                                         nullptr, 0.f);
-    }
+    if (bf)
+      k_prep_rows<<<1, 1024, 0, st>>>(target, N, ignore_index, rows, count, reduction, total, D,
+                                      lse, 0.f, rl, 0.f, nullptr, 0.f);
+    else
+      k_divisor<<<1, 1024, 0, st>>>(target, N, ignore_index, reduction, total, D);
     launch_row_dots(h, W, bias, target, N, H, V, bf, ignore_index, logit_scale, smooth, colpart,
                     wsum, bsum, zt, R, st);
   }
@@ -781,10 +779,8 @@ int fldce_shard_partials(const void* h, const void* W_local, const int64_t* targ
     // rows with target == ignore_index are skipped: (-inf, 0, 0, 0)
     {
       StageTimer tm(kPrep, st);
-      k_compact_rows<<<1, 1024, 0, st>>>(target, N, ignore_index, rows, count);
-      k_ignored_rows_init<<<grid1(N, 256), 256, 0, st>>>(target, N, ignore_index, row_max,
-                                                         -INFINITY, row_sumexp, 0.f, row_sumlogit,
-                                                         0.f);
+      k_prep_rows<<<1, 1024, 0, st>>>(target, N, ignore_index, rows, count, 0, 0, nullptr,
+                                      row_max, -INFINITY, row_sumexp, 0.f, row_sumlogit, 0.f);
     }
     const int blocks = (int)(cdiv(V, kBM) * cdiv(N, kBN));
     bf16* hc = reinterpret_cast<bf16*>(ws + p.oHC);
@@ -865,16 +861,16 @@ int fldce_shard_bwd(const void* h, const void* W_local, const int64_t* target, c
   }
   char* ws = static_cast<char*>(workspace);
   float* D = reinterpret_cast<float*>(ws + p.oD);
-  {
-    StageTimer tm(kPrep, st);
-    k_divisor<<<1, 1024, 0, st>>>(target, N, ignore_index, reduction, total, D);
-  }
   const bool bf = dtype == FLDCE_DTYPE_BF16;
   int* rows = reinterpret_cast<int*>(ws + p.oRows);
   int* count = reinterpret_cast<int*>(ws + p.oCount);
-  if (bf) {
+  {
     StageTimer tm(kPrep, st);
-    k_compact_rows<<<1, 1024, 0, st>>>(target, N, ignore_index, rows, count);
+    if (bf)
+      k_prep_rows<<<1, 1024, 0, st>>>(target, N, ignore_index, rows, count, reduction, total, D,
+                                      nullptr, 0.f, nullptr, 0.f, nullptr, 0.f);
+    else
+      k_divisor<<<1, 1024, 0, st>>>(target, N, ignore_index, reduction, total, D);
   }
   Core c{h, W_local, nullptr, target, p_mask, N, H, V_local, vocab_start, V_global, dtype,
          ignore_index, label_smoothing, logit_scale, lse, nullptr, nullptr, nullptr, nullptr,

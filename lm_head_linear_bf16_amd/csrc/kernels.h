@@ -37,31 +37,66 @@ __global__ __launch_bounds__(1024) void k_divisor(const int64_t* __restrict__ ta
 // Row compaction.  Rows whose target is ignore_index contribute nothing (page
 // 1, cross_entropy_kernel step 2 zeroes them), so the bf16 path multiplies
 // only the others: rows[k] = index of the k-th row with target != ignore
-// (ascending), *count = their number.  One block; a wave ballot gives each
-// row its position, so the order (and everything after it) is deterministic.
+// (ascending), *count = their number.  One block; each thread takes four
+// consecutive rows per pass and a block-wide prefix sum gives their
+// positions, so the order (and everything after it) is deterministic.
+// In the same pass, when the pointers are not null: the divisor D as
+// k_divisor computes it (the count is the number of non-ignored rows), and
+// a[i] = va, b[i] = vb, c[i] = vc on ignored rows (outputs no later kernel
+// writes for them).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void k_compact_rows(const int64_t* __restrict__ target, int64_t N,
-                                                       int64_t ignore, int* __restrict__ rows,
-                                                       int* __restrict__ count) {
+__global__ __launch_bounds__(1024) void k_prep_rows(const int64_t* __restrict__ target, int64_t N,
+                                                    int64_t ignore, int* __restrict__ rows,
+                                                    int* __restrict__ count, int reduction,
+                                                    int64_t total, float* __restrict__ D, float* a,
+                                                    float va, float* b, float vb, float* c,
+                                                    float vc) {
   __shared__ int wtot[16];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int base = 0;
-  for (int64_t s0 = 0; s0 < N; s0 += 1024) {
-    const int64_t i = s0 + threadIdx.x;
-    const bool v = i < N && target[i] != ignore;
-    const uint64_t m = __ballot(v);
-    const int before = __popcll(m & ((uint64_t(1) << lane) - 1));
-    if (lane == 0) wtot[wave] = __popcll(m);
+  for (int64_t s0 = 0; s0 < N; s0 += 4096) {
+    const int64_t i0 = s0 + (int64_t)threadIdx.x * 4;
+    bool v[4];
+    int cnt = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t i = i0 + k;
+      const bool in = i < N;
+      const bool ign = in && target[i] == ignore;
+      v[k] = in && !ign;
+      cnt += v[k] ? 1 : 0;
+      if (ign) {
+        if (a) a[i] = va;
+        if (b) b[i] = vb;
+        if (c) c[i] = vc;
+      }
+    }
+    int x = cnt;  // inclusive prefix sum over the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wtot[wave] = x;
     __syncthreads();
-    int off = base;
-    for (int w = 0; w < wave; ++w) off += wtot[w];
-    if (v) rows[off + before] = (int)i;
+    int pos = base + x - cnt;
+    for (int w = 0; w < wave; ++w) pos += wtot[w];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (v[k]) rows[pos++] = (int)(i0 + k);
     int tot = 0;
     for (int w = 0; w < 16; ++w) tot += wtot[w];
     base += tot;
     __syncthreads();
   }
-  if (threadIdx.x == 0) *count = base;
+  if (threadIdx.x == 0) {
+    *count = base;
+    if (D != nullptr) {
+      float d = 1.f;
+      if (reduction == 1) d = total > 0 ? (float)total : (float)(base > 0 ? base : 1);
+      *D = d;
+    }
+  }
 }
 
 // Outputs of ignored rows that no later kernel writes: a[i] = va, b[i] = vb,
