@@ -151,3 +151,38 @@ def test_full_size_vocab_shard():
     ew = grad_err(host(b["dW_local"][torch.from_numpy(vr).to(dev)]), dw_want)
     say(f"  dH_partial rows err {eh:.2e}  dW_local rows err {ew:.2e}")
     assert eh <= GRAD_RTOL["bf16"] and ew <= GRAD_RTOL["bf16"]
+
+
+def test_full_size_headline_chunked():
+    """The headline workload in chunks of 2048 compacted rows: the fp32 dW
+    accumulator carries over chunks (first, middle and last chunk modes) at
+    the full vocabulary."""
+    torch = torch_cuda()
+    from lm_head_linear_bf16_amd import fldce
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS["headline"]
+    g = _golden(w)
+    t, p = synth.targets(w)
+    h, W = synth.hidden(w), synth.weight(w)
+    say(f"case full headline, chunk_rows=2048: N={w.N} H={w.H} V={w.V}")
+    r = fldce.fldce_fwd_bwd(to_dev(h, dev), to_dev(W, dev), torch.from_numpy(t).to(dev),
+                            torch.from_numpy(p).to(dev), label_smoothing=w.label_smoothing,
+                            logit_scale=w.logit_scale, reduction=w.reduction, total=w.total,
+                            chunk_rows=2048)
+    torch.cuda.synchronize()
+    valid = t != -100
+    D = O.divisor(valid, w.reduction, w.total or None)
+    rl = O.row_losses(g["lse"], g["z_target"], g["z_sum"], w.V, p, valid, w.label_smoothing)
+    want = O.loss_from_row_losses(rl, D)
+    got = float(r["loss"].item())
+    say(f"  loss {got:.7g} oracle {want:.7g}")
+    assert abs(got - want) <= LOSS_RTOL["bf16"] * abs(want)
+    rows = _sample_rows(t, seed=3)
+    dH_want = O.dH_rows(h.values, W.values, t, p, g["lse"][rows], rows, D, w.label_smoothing,
+                        w.logit_scale)
+    eh = grad_err(host(r["dH"][torch.from_numpy(rows).to(dev)]), dH_want)
+    vr = _sample_vocab(t, w.V, seed=4)
+    dW_want = O.dW_rows(h.values, W.values, t, p, g["lse"], vr, D, w.label_smoothing, w.logit_scale)
+    ew = grad_err(host(r["dW"][torch.from_numpy(vr).to(dev)]), dW_want)
+    say(f"  dH rows err {eh:.2e}  dW rows err {ew:.2e}")
+    assert eh <= GRAD_RTOL["bf16"] and ew <= GRAD_RTOL["bf16"]
