@@ -201,8 +201,8 @@ def _timed(fn, steps: int, warmup: int):
 
 def extra_legs(args, w, h, W, tgt, pm, dt, rows_mult: int, ms_plain: float, peak: float) -> dict:
     """The rest of page 1's interface on the same inputs: forward only
-    (fldce_fwd: 2 * rows * H * V flops) and fwd+bwd with the seeded bias and
-    its gradient db (fldce_fwd_bwd_ex)."""
+    (fldce_fwd: 2 * rows * H * V flops) and, with --bias-leg, fwd+bwd with
+    the seeded bias and its gradient db (fldce_fwd_bwd_ex)."""
     import numpy as np
     import torch
     from lm_head_linear_bf16_amd import fldce, synth
@@ -220,6 +220,8 @@ def extra_legs(args, w, h, W, tgt, pm, dt, rows_mult: int, ms_plain: float, peak
                            "tflops": round(tf, 2), "pct_peak": round(100.0 * tf / peak, 2),
                            "stage_ms_per_step": st}
     del ws
+    if not args.bias_leg:
+        return out
     bt = synth.bias(w)
     b = (torch.from_numpy(bt.bits.view(np.int16)).view(torch.bfloat16) if bt.bits is not None
          else torch.from_numpy(bt.values)).to(dev)
@@ -338,7 +340,10 @@ def main() -> int:
                          "run with --calib-copy-mib into profiles/traffic.json and exit")
     ap.add_argument("--calib-mib", type=int, default=1024, help="size of that calibration copy")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the forward-only and bias + db legs")
+                    help="skip the forward-only leg (and the bias + db leg)")
+    ap.add_argument("--bias-leg", action="store_true",
+                    help="also time fwd+bwd with the seeded bias and db (fldce_fwd_bwd_ex); off by "
+                         "default so that the plain step is the only user of its logits kernel")
     args = ap.parse_args()
     if args.traffic_summary:
         return traffic_summary(args.traffic_summary[0], args.traffic_summary[1], args.workload,
