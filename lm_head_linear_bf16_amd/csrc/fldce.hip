@@ -126,9 +126,17 @@ Plan make_plan(int mode, int64_t N, int64_t H, int64_t V, int dtype, int64_t chu
     p.oDbpart = take(cur, (size_t)p.db_blocks * p.Vp * 4);
   }
   if (bf) {
-    const int64_t tiles = cdiv(p.C, kBM) * cdiv(H, kBN);
-    p.splits = choose_splits(tiles, p.Vp / kBK, 8);
-    p.oDHpart = take(cur, (size_t)p.splits * p.C * H * 4);
+    // the device picks the split count S for the rows that exist (fewer than
+    // C when rows are ignored) and stores S x rows x H partials; reserve the
+    // largest such product over every possible number of row tiles
+    p.splits = 1;
+    size_t part_elems = 0;
+    for (int64_t tm = 1; tm <= cdiv(p.C, kBM); ++tm) {
+      const int S = choose_splits(tm * cdiv(H, kBN), p.Vp / kBK, 8);
+      p.splits = std::max(p.splits, S);
+      if (S > 1) part_elems = std::max(part_elems, (size_t)S * std::min(tm * kBM, p.C) * H);
+    }
+    p.oDHpart = take(cur, std::max<size_t>(part_elems, 1) * 4);
     if (p.nchunks > 1) p.oDW32 = take(cur, (size_t)V * H * 4);
   }
   p.total = cur;
@@ -372,10 +380,10 @@ int run_core_bf16(const Core& c, const Plan& p, char* ws, hipStream_t st) {
       if (S == 1) {
         // at most one split: the GEMM wrote dH itself
       } else if (c.dH_f32)
-        k_splitk_scatter<float><<<(unsigned)cmax, 256, 0, st>>>(
+        k_splitk_scatter<float><<<(unsigned)std::min<int64_t>(cmax, 2048), 256, 0, st>>>(
             dHpart, S, Vp / kBK, cmax, H, c.rows, c.count, c0, (float*)c.dH);
       else
-        k_splitk_scatter<bf16><<<(unsigned)cmax, 256, 0, st>>>(
+        k_splitk_scatter<bf16><<<(unsigned)std::min<int64_t>(cmax, 2048), 256, 0, st>>>(
             dHpart, S, Vp / kBK, cmax, H, c.rows, c.count, c0, (bf16*)c.dH);
     }
     {  // 5. dW += g^T h

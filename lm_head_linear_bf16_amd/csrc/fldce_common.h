@@ -56,12 +56,17 @@ __host__ __device__ constexpr int64_t cdiv(int64_t a, int64_t b) { return (a + b
 __host__ __device__ constexpr int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 
 // Split count for a split-K GEMM with `tiles` output tiles and k_tiles K
-// tiles, at most max_splits: minimises the waves of work over 256 CUs per
-// split (ceil(tiles * S / 256) / S, plus a small charge per split for the
-// fp32 partials), keeping >= 8 K tiles per split.  Used by the host to size
+// tiles, at most max_splits: 1 when the tiles fill the 256 CUs at least
+// once; else minimises the waves of work per split (ceil(tiles * S / 256) /
+// S, plus a small charge per split for the fp32 partials), keeping >= 8 K
+// tiles per split.  Used by the host to size
 // the grid and the partial buffer, and by the kernels on the device once the
 // number of active tiles is known.
 __host__ __device__ inline int choose_splits(int64_t tiles, int64_t k_tiles, int max_splits) {
+  // With a full wave of tiles already, a partly filled last wave costs little
+  // (measured: its CUs run at a higher clock and with less memory contention),
+  // so more splits would only add partial-sum traffic.
+  if (tiles >= 256) return 1;
   int best = 1;
   double bestc = 1e300;
   for (int S = 1; S <= max_splits; ++S) {

@@ -401,8 +401,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_logits_bf16(
 }
 
 // ---------------------------------------------------------------------------
-// dH = g W, split over K = vocabulary: out[split][m][n] (fp32) for this
-// split's K tiles.  A = g [M = C tokens, ldg] (K contiguous); B = W read as
+// dH = g W, split over K = vocabulary: out[split][m][n] (fp32, m < the rows
+// that exist) for this split's K tiles.  A = g [M = C tokens, ldg] (K contiguous); B = W read as
 // K rows (vocabulary rows of W [V, H], transposed in LDS).  Rows of W past
 // V are clamped: g is zero in those columns.
 // ---------------------------------------------------------------------------
@@ -451,7 +451,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dh_bf16(
       }
     return;
   }
-  float* o = out + (int64_t)tc.split * M * H;
+  float* o = out + (int64_t)tc.split * Me * H;  // partials [split][Me][H]
 #pragma unroll
   for (int i = 0; i < kTM; ++i)
 #pragma unroll

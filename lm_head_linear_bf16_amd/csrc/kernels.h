@@ -758,11 +758,11 @@ __global__ __launch_bounds__(256) void k_splitk_scatter(const float* __restrict_
                                                         Tout* __restrict__ out) {
   const int64_t C = chunk_rows(count, c0, cmax);
   const int S = choose_splits(cdiv(C, 256) * cdiv(H, 256), k_tiles, max_splits);
-  const int64_t j = blockIdx.x;  // one block per chunk row
-  if (j >= C || S == 1) return;  // one split: the GEMM wrote the rows itself
-  const int64_t MN = cmax * H;
-  const int64_t dst = (int64_t)rows[c0 + j] * H;
+  if (S == 1) return;  // one split: the GEMM wrote the rows itself
+  const int64_t MN = C * H;  // partials [split][C][H]
+  for (int64_t j = blockIdx.x; j < C; j += gridDim.x)  // chunk rows, grid-strided
   for (int64_t e = (int64_t)threadIdx.x * 4; e < H; e += 256 * 4) {
+    const int64_t dst = (int64_t)rows[c0 + j] * H;
     const int64_t src = j * H + e;
     if (e + 4 <= H) {
       floatx4 acc = *(const floatx4*)(part + src);
