@@ -10,11 +10,14 @@
 //   3. dlogits pass: z -> g
 //   4. dH = g W     (split-K GEMM over the vocabulary + ordered reduction)
 //   5. dW += g^T h  (fp32 across chunks, rounded once at the end)
-// Before the loop: divisor D, column sums of W (label smoothing), target
-// logits and row sums of z by per-row dot products.  After it: the loss.
-// bf16 GEMMs read W and g in their own layouts (one via the LDS transpose
-// read); only the chunk's h is copied transposed.  The fp32 path (float32
-// inputs) uses plain fp32 GEMMs over transposed copies.
+// Before the loop: divisor D and, on the bf16 path, the compacted list of
+// rows whose target is not ignore_index (only they are multiplied; chunks
+// are taken over that list); target logits by per-row dot products (and,
+// for fp32, the row sums of z from the column sums of W).  After it: the
+// loss.  bf16 GEMMs read W and g in their own layouts (one via the LDS
+// transpose read); the chunk's rows of h are gathered once, row-major and
+// transposed.  The fp32 path (float32 inputs) uses plain fp32 GEMMs over
+// transposed copies.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
