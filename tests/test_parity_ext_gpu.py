@@ -301,3 +301,26 @@ def test_full_size_4b_with_bias_and_eob():
     eb = grad_err(host(r["db"][vt]), db_want)
     say(f"  dH rows err {eh:.2e}  dW rows err {ew:.2e}  db err {eb:.2e}")
     assert max(eh, ew, eb) <= GRAD_RTOL["bf16"]
+
+
+def test_deterministic_repeat_ex_and_forward():
+    """Bias, db, EOB and the forward-only entry repeat bit for bit (fixed-order
+    reductions everywhere, including the db column sums and the split-K dH)."""
+    torch = torch_cuda()
+    from lm_head_linear_bf16_amd import fldce
+    dev = torch.device("cuda:0")
+    w = synth.custom("repeat_ex", 4, 200, 256, 3000, label_smoothing=0.1, logit_scale=0.5)
+    target, p_mask, _, _, _, hd, Wd, bd = _inputs(w, True, dev)
+    t, p = torch.from_numpy(_eob_targets(target, 7)).to(dev), torch.from_numpy(p_mask).to(dev)
+    say("case repeat ex / forward")
+    kw = dict(label_smoothing=0.1, logit_scale=0.5, total=w.N, eob_token_id=7, eob_weight=1.5)
+    a = fldce.fldce_fwd_bwd_ex(hd, Wd, t, p, bd, row_stats=True, **kw)
+    b = fldce.fldce_fwd_bwd_ex(hd, Wd, t, p, bd, row_stats=True, **kw)
+    f1 = fldce.fldce_fwd(hd, Wd, t, p, bd, row_stats=True, **kw)
+    f2 = fldce.fldce_fwd(hd, Wd, t, p, bd, row_stats=True, **kw)
+    torch.cuda.synchronize()
+    for k in ("loss", "dH", "dW", "db", "row_lse", "row_loss"):
+        assert torch.equal(a[k], b[k]), k
+    for k in ("loss", "row_lse", "row_loss"):
+        assert torch.equal(f1[k], f2[k]), k
+        assert torch.equal(f1[k], a[k]), k  # the forward half of fwd_bwd_ex, bit for bit
