@@ -229,7 +229,8 @@ __global__ __launch_bounds__(256) void k_transpose_bf16(const bf16* __restrict__
 }
 
 // Gathered chunk rows of h (row r of the chunk = source row rows[c0 + r],
-// r < the chunk's count; rows up to Rp are zero): hT [Cn, Rp] (ldd, when
+// r < the chunk's count R; rows R .. round_up(R, 64) - 1 are zero, later
+// rows up to Rp are not written: no GEMM reads them): hT [Cn, Rp] (ldd, when
 // dst != nullptr, the B operand of dW) and the row-major copy hc [Rp, Cn]
 // (when hc != nullptr, the B operand of the logits GEMM, so the GEMM reads
 // contiguous rows instead of chasing indices in every tile's prologue).
@@ -244,6 +245,7 @@ __global__ __launch_bounds__(256) void k_transpose_gather_bf16(const bf16* __res
   const int tx = threadIdx.x & 7, ty = threadIdx.x >> 3;
   const int64_t R = chunk_rows(count, c0, cmax);
   const int64_t r0 = (int64_t)blockIdx.x * 64, c0c = (int64_t)blockIdx.y * 64;
+  if (r0 >= round_up(R, 64)) return;  // rows past the padded count are never read
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     const int lr = ty + 32 * p;
