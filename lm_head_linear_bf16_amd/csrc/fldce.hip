@@ -229,29 +229,17 @@ int launch_status() { return hipGetLastError() == hipSuccess ? FLDCE_OK : FLDCE_
 
 inline unsigned grid1(int64_t n, int64_t per) { return (unsigned)cdiv(n, per); }
 
-template <typename T>
-void launch_transpose(const T* src, int64_t R, int64_t Cn, int64_t lds, T* dst, int64_t ldd,
-                      int64_t Rp, hipStream_t st) {
+void launch_transpose(const float* src, int64_t R, int64_t Cn, int64_t lds, float* dst,
+                      int64_t ldd, int64_t Rp, hipStream_t st) {
   dim3 g((unsigned)cdiv(Rp, 64), (unsigned)cdiv(Cn, 64));
-  if constexpr (sizeof(T) == 2)
-    k_transpose_bf16<<<g, 256, 0, st>>>(src, R, Cn, lds, dst, ldd, Rp);
-  else
-    k_transpose<T><<<g, 256, 0, st>>>(src, R, Cn, lds, dst, ldd, Rp);
+  k_transpose<float><<<g, 256, 0, st>>>(src, R, Cn, lds, dst, ldd, Rp);
 }
 
-// wsum[c] = sum_j W[j, c] (two ordered passes).
-template <typename T>
-void launch_colsum(const T* W, int64_t V, int64_t H, float* colpart, float* wsum, hipStream_t st) {
-  if constexpr (sizeof(T) == 2) {
-    if (H % 8 == 0) {
-      dim3 g((unsigned)cdiv(V, kColSlab), (unsigned)cdiv(H, 256 * 8));
-      k_colsum_slabs_bf16<<<g, 256, 0, st>>>(W, V, H, colpart);
-      k_colsum_finish<float><<<grid1(H, 256), 256, 0, st>>>(colpart, cdiv(V, kColSlab), H, H, wsum);
-      return;
-    }
-  }
+// wsum[c] = sum_j W[j, c] (two ordered passes; fp32 inputs).
+void launch_colsum(const float* W, int64_t V, int64_t H, float* colpart, float* wsum,
+                   hipStream_t st) {
   dim3 g((unsigned)cdiv(V, kColSlab), (unsigned)cdiv(H, 256));
-  k_colsum_slabs<T><<<g, 256, 0, st>>>(W, V, H, colpart);
+  k_colsum_slabs<float><<<g, 256, 0, st>>>(W, V, H, colpart);
   k_colsum_finish<float><<<grid1(H, 256), 256, 0, st>>>(colpart, cdiv(V, kColSlab), H, H, wsum);
 }
 
@@ -421,7 +409,7 @@ int run_core_f32(const Core& c, const Plan& p, char* ws, hipStream_t st) {
   int64_t db_off = 0;  // slabs of db partials written so far
   {
     StageTimer tm(kPrep, st);
-    launch_transpose<float>(W, V, H, H, WT, Vp, Vp, st);
+    launch_transpose(W, V, H, H, WT, Vp, Vp, st);
   }
   for (int64_t ic = 0; ic < p.nchunks; ++ic) {
     const int64_t c0 = ic * p.C;
@@ -430,7 +418,7 @@ int run_core_f32(const Core& c, const Plan& p, char* ws, hipStream_t st) {
     const float* hc = h + c0 * H;
     {
       StageTimer tm(kHT, st);
-      launch_transpose<float>(hc, Cc, H, H, hT, p.Cp, Cpc, st);
+      launch_transpose(hc, Cc, H, H, hT, p.Cp, Cpc, st);
     }
     {
       StageTimer tm(kLogits, st);
@@ -510,8 +498,8 @@ void launch_row_dots(const void* h, const void* W, const void* bias, const int64
     return;
   }
   if (smooth) {
-    launch_colsum<float>((const float*)W, V, H, colpart, wsum, st);
-    if (bias != nullptr) launch_colsum<float>((const float*)bias, V, 1, colpart, bsum, st);
+    launch_colsum((const float*)W, V, H, colpart, wsum, st);
+    if (bias != nullptr) launch_colsum((const float*)bias, V, 1, colpart, bsum, st);
   }
   k_rowdot<float><<<grid1(N, 4), 256, 0, st>>>(
       (const float*)h, (const float*)W, (const float*)bias, H, target, 0, V, ignore, s,
@@ -832,7 +820,7 @@ int fldce_shard_partials(const void* h, const void* W_local, const int64_t* targ
           nullptr, 0.f, 1.f, 1.f, nullptr, -1, 1.f, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
           row_max, row_sumexp, nullptr);
     }
-    if (row_sumlogit) launch_colsum<float>((const float*)W_local, V, H, colpart, wsum, st);
+    if (row_sumlogit) launch_colsum((const float*)W_local, V, H, colpart, wsum, st);
     k_rowdot<float><<<grid1(N, 4), 256, 0, st>>>((const float*)h, (const float*)W_local, nullptr, H,
                                                   target, vocab_start, V, ignore_index, logit_scale,
                                                   row_sumlogit ? wsum : nullptr, nullptr, N,

@@ -168,66 +168,6 @@ __global__ __launch_bounds__(256) void k_colsum_slabs(const T* __restrict__ src,
   colpart[(int64_t)blockIdx.x * Cn + c] = s;
 }
 
-// bf16 variant with 16-byte loads: each thread sums 8 adjacent columns
-// (Cn % 8 == 0); a wave reads 1 KB of a row per step.
-__global__ __launch_bounds__(256) void k_colsum_slabs_bf16(const bf16* __restrict__ src, int64_t R,
-                                                           int64_t Cn, float* __restrict__ colpart) {
-  const int64_t c = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 8;
-  if (c >= Cn) return;
-  const int64_t r0 = (int64_t)blockIdx.x * kColSlab, r1 = min(R, r0 + kColSlab);
-  float s[8] = {};
-  for (int64_t r = r0; r < r1; ++r) {
-    const bf16x8 v = *(const bf16x8*)(src + r * Cn + c);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) s[e] += (float)v[e];
-  }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) colpart[(int64_t)blockIdx.x * Cn + c + e] = s[e];
-}
-
-// bf16 transpose with 16-byte accesses: 64 x 64 tile, each thread moves
-// 8 consecutive elements in and 8 out.  Same contract as k_transpose.
-__global__ __launch_bounds__(256) void k_transpose_bf16(const bf16* __restrict__ src, int64_t R,
-                                                        int64_t Cn, int64_t lds,
-                                                        bf16* __restrict__ dst, int64_t ldd,
-                                                        int64_t Rp) {
-  __shared__ bf16 tile[64][64 + 8];
-  const int tx = threadIdx.x & 7, ty = threadIdx.x >> 3;  // 8 chunks x 32 rows
-  const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
-  const bool vec_in = (Cn % 8 == 0) && (lds % 8 == 0);
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int lr = ty + 32 * p;
-    const int64_t r = r0 + lr, c = c0 + tx * 8;
-    bf16x8 v;
-    if (r < R && vec_in && c + 8 <= Cn) {
-      v = *(const bf16x8*)(src + r * lds + c);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = (r < R && c + e < Cn) ? src[r * lds + c + e] : (bf16)0.f;
-    }
-    *(bf16x8*)&tile[lr][tx * 8] = v;  // rows are 144 B: 16-byte aligned
-  }
-  __syncthreads();
-  const bool vec_out = (ldd % 8 == 0) && (Rp % 8 == 0);
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int lc = ty + 32 * p;
-    const int64_t c = c0 + lc, r = r0 + tx * 8;
-    if (c >= Cn) continue;
-    bf16x8 v;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = tile[tx * 8 + e][lc];
-    if (vec_out && r + 8 <= Rp) {
-      *(bf16x8*)(dst + c * ldd + r) = v;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (r + e < Rp) dst[c * ldd + r + e] = v[e];
-    }
-  }
-}
-
 // Gathered chunk rows of h (row r of the chunk = source row rows[c0 + r],
 // r < the chunk's count R; rows R .. round_up(R, 64) - 1 are zero, later
 // rows up to Rp are not written: no GEMM reads them): hT [Cn, Rp] (ldd, when
@@ -725,26 +665,6 @@ __global__ __launch_bounds__(256) void k_scale_grad(const float* __restrict__ gr
   if (blockIdx.x == 0 && threadIdx.x < n - n8 * 8) {
     const int64_t e = n8 * 8 + threadIdx.x;
     x[e] = from_f32<T>(to_f32(x[e]) * d);
-  }
-}
-
-// out[e] = sum_{s < S} part[s * MN + e], s ascending; cast to Tout.
-template <typename Tout>
-__global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ part, int S,
-                                                       int64_t MN, Tout* __restrict__ out) {
-  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (e >= MN) return;
-  if (e + 4 <= MN) {
-    floatx4 acc = *(const floatx4*)(part + e);
-    for (int s = 1; s < S; ++s) acc += *(const floatx4*)(part + (int64_t)s * MN + e);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) out[e + k] = from_f32<Tout>(acc[k]);
-  } else {
-    for (int64_t k = e; k < MN; ++k) {
-      float a = part[k];
-      for (int s = 1; s < S; ++s) a += part[(int64_t)s * MN + k];
-      out[k] = from_f32<Tout>(a);
-    }
   }
 }
 
