@@ -75,7 +75,9 @@ enum fldce_status {
   FLDCE_ERR_WORKSPACE = -5,      /* workspace NULL or smaller than required   */
   FLDCE_ERR_ALIGNMENT = -6,      /* a pointer is not 16-byte aligned          */
   FLDCE_ERR_HIP = -7,            /* a kernel launch failed                    */
-  FLDCE_ERR_UNSUPPORTED = -8     /* shape the bf16 path does not handle       */
+  FLDCE_ERR_UNSUPPORTED = -8     /* shape the bf16 path does not handle: H not
+                                    a multiple of 64, or a GEMM grid of 2^32
+                                    work-items or more                         */
 };
 
 /* Library version (FLDCE_VERSION of the build). */

@@ -134,7 +134,9 @@ Plan make_plan(int mode, int64_t N, int64_t H, int64_t V, int dtype, int64_t chu
     // largest such product over every possible number of row tiles
     p.splits = 1;
     size_t part_elems = 0;
-    for (int64_t tm = 1; tm <= cdiv(p.C, kBM); ++tm) {
+    // (choose_splits is 1 from 256 tiles on, so the loop stops there)
+    const int64_t tm_max = std::min(cdiv(p.C, kBM), cdiv(256, cdiv(H, kBN)));
+    for (int64_t tm = 1; tm <= tm_max; ++tm) {
       const int S = choose_splits(tm * cdiv(H, kBN), p.Vp / kBK, 8);
       p.splits = std::max(p.splits, S);
       if (S > 1) part_elems = std::max(part_elems, (size_t)S * std::min(tm * kBM, p.C) * H);
@@ -144,6 +146,16 @@ Plan make_plan(int mode, int64_t N, int64_t H, int64_t V, int dtype, int64_t chu
   }
   p.total = cur;
   return p;
+}
+
+// A dispatch holds fewer than 2^32 work-items per grid dimension: the
+// largest 1-D GEMM grid (logits: vocabulary tiles x chunk-row tiles; dW:
+// vocabulary tiles x H tiles; dH: row tiles x H tiles x splits) must fit.
+bool grids_fit(const Plan& p, int dtype) {
+  if (dtype != FLDCE_DTYPE_BF16) return true;
+  const int64_t lim = (int64_t(1) << 32) / kGemmThreads;
+  const int64_t tv = cdiv(p.V, kBM), tc = cdiv(std::max<int64_t>(p.C, 1), kBN), th = cdiv(p.H, kBN);
+  return tv * tc < lim && tv * th < lim && tc * th * std::max(p.splits, 1) < lim;
 }
 
 void set_gemm_attributes() {
@@ -523,7 +535,9 @@ const char* fldce_status_string(int status) {
     case FLDCE_ERR_WORKSPACE: return "workspace missing or smaller than the size query returns";
     case FLDCE_ERR_ALIGNMENT: return "a pointer is not 16-byte aligned";
     case FLDCE_ERR_HIP: return "a HIP kernel launch failed";
-    case FLDCE_ERR_UNSUPPORTED: return "shape not supported by the bf16 path (H must be a multiple of 64)";
+    case FLDCE_ERR_UNSUPPORTED:
+      return "shape not supported by the bf16 path (H must be a multiple of 64; each GEMM grid "
+             "must hold fewer than 2^32 work-items)";
     default: return "unknown status";
   }
 }
@@ -578,6 +592,7 @@ int fldce_fwd_bwd_ex(const void* h, const void* W, const void* bias, const int64
       !aligned16(workspace))
     return FLDCE_ERR_ALIGNMENT;
   const Plan p = make_plan(kFwdBwd, N, H, V, dtype, chunk_rows);
+  if (!grids_fit(p, dtype)) return FLDCE_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < p.total) return FLDCE_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   set_gemm_attributes();
@@ -646,6 +661,7 @@ int fldce_fwd(const void* h, const void* W, const void* bias, const int64_t* tar
       !aligned16(p_mask) || !aligned16(workspace))
     return FLDCE_ERR_ALIGNMENT;
   const Plan p = make_plan(kFwd, N, H, V, dtype, 0);
+  if (!grids_fit(p, dtype)) return FLDCE_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < p.total) return FLDCE_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   set_gemm_attributes();
@@ -762,6 +778,7 @@ int fldce_shard_partials(const void* h, const void* W_local, const int64_t* targ
   if (!aligned16(h) || !aligned16(W_local) || !aligned16(target) || !aligned16(workspace))
     return FLDCE_ERR_ALIGNMENT;
   const Plan p = make_plan(kShardPartials, N, H, V_local, dtype, 0);
+  if (!grids_fit(p, dtype)) return FLDCE_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < p.total) return FLDCE_ERR_WORKSPACE;
   if (N == 0) return FLDCE_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -850,6 +867,7 @@ int fldce_shard_bwd(const void* h, const void* W_local, const int64_t* target, c
       !aligned16(lse) || !aligned16(dH_partial) || !aligned16(dW_local) || !aligned16(workspace))
     return FLDCE_ERR_ALIGNMENT;
   const Plan p = make_plan(kShardBwd, N, H, V_local, dtype, chunk_rows);
+  if (!grids_fit(p, dtype)) return FLDCE_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < p.total) return FLDCE_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   set_gemm_attributes();

@@ -95,6 +95,7 @@ def test_fwd_bwd_argument_checks(L):
     assert _fwd(L, wsb=16) == -5
     assert _fwd(L, ws=None) == -5
     assert _fwd(L, H=100) == -8          # bf16 needs H % 64 == 0
+    assert _fwd(L, V=(1 << 31) - 1, N=1 << 20) == -8   # logits grid past 2^32 work-items
     assert _fwd(L, H=100, dtype=0, wsb=16) == -5   # fp32 takes any H (fails later on workspace)
 
 
