@@ -235,3 +235,38 @@ def test_vocab_shards_match_full_vocab(dtype):
         dWs.append(gw)
     assert grad_err(dH, full["dH"]) <= GRAD_RTOL[dtype]
     assert grad_err(np.concatenate(dWs), full["dW"]) <= GRAD_RTOL[dtype]
+
+
+# Edge shapes: a single token, V smaller than one 128-wide slab, one vocabulary
+# row, H = 64 (one K step), token counts one past a tile and one short of a
+# 64-row block, vocabularies one past / short of 256 and 1024, and the
+# counted mean; each against the oracle element by element.
+EDGE_CASES = [
+    synth.custom("one_token", 1, 1, 64, 300),
+    synth.custom("v_lt_slab", 2, 40, 128, 100, label_smoothing=0.1),
+    synth.custom("v_one", 1, 30, 64, 1),
+    synth.custom("h64_v257", 1, 257, 64, 257, logit_scale=0.3, total_is_N=False),
+    synth.custom("n63_v1023", 1, 63, 192, 1023, label_smoothing=0.2, reduction="sum"),
+    synth.custom("n513_v1025", 1, 513, 128, 1025, label_smoothing=0.05, logit_scale=2.0),
+    synth.custom("n1_f32", 1, 1, 33, 77, dtype="f32", label_smoothing=0.3),
+    synth.custom("v_one_f32", 1, 9, 16, 1, dtype="f32"),
+]
+
+
+@pytest.mark.parametrize("w", EDGE_CASES, ids=lambda w: w.name)
+def test_edge_shapes(w):
+    r, o, t = _run(w)
+    if w.V > 1:
+        _compare(w, r, o, t)
+        return
+    # one class: the loss and every gradient are exactly 0 mathematically; the
+    # kernels leave only rounding (lse and the stored logit differ in the last
+    # bits), bounded by 1e-2 of the gradients' natural scale c_i |W|, sum c_i |h|
+    valid = t != -100
+    _, p = synth.targets(w)
+    c = np.where(valid, w.logit_scale / (p * O.divisor(valid, w.reduction, w.total or None)), 0.0)
+    h, W = synth.hidden(w).values, synth.weight(w).values
+    assert abs(float(r["loss"].item())) <= 1e-4
+    assert np.abs(host(r["dH"])).max() <= 1e-2 * c.max() * np.abs(W).max()
+    assert np.abs(host(r["dW"])).max() <= 1e-2 * (c[:, None] * np.abs(h)).sum(axis=0).max()
+    assert np.all(host(r["dH"])[~valid] == 0.0)
