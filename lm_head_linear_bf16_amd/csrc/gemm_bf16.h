@@ -296,6 +296,98 @@ __device__ __forceinline__ int acc_col(int wn, int j, int lane) { return wn * kT
 // it is not null) is row rows[c0 + j] of h when rows != nullptr (gathered
 // here), else row j of h (h = the chunk's rows, already gathered).  The grid covers cmax tokens; tiles past the
 // count exit at once.
+// Epilogue of the logits GEMM for one wave's 128 (vocabulary) x 64 (token)
+// accumulators; kFull: all 128 vocabulary rows exist (every tile but the last
+// vocabulary tile), so no per-element bound checks.  In phases over the 4
+// token groups j, so the 4 independent reductions overlap: maxima, the
+// cross-lane exchanges, the sums of exp (and of z), the partial stores, then
+// the z stores.
+template <bool kStoreZ, bool kPart, bool kFull>
+__device__ __forceinline__ void logits_epilogue(const Acc& acc, int V, int C, int m0, int n0,
+                                                int wm, int wn, int lane, float s,
+                                                floatx2* __restrict__ part,
+                                                float* __restrict__ rpart, int64_t ldp,
+                                                bf16* __restrict__ zbuf, int64_t ldz) {
+  const int vbase = m0 + wm * kTM * 16;
+  auto in_v = [&](int i, int r) { return kFull || m0 + acc_row(wm, i, lane, r) < V; };
+  if (kPart) {
+    const float sl = s * kLog2e;
+    float mx[kTN], sum[kTN], rs[kTN];
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) {
+      mx[j] = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (in_v(i, r)) mx[j] = fmaxf(mx[j], acc[i][j][r]);
+    }
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) {
+      mx[j] = fmaxf(mx[j], __shfl_xor(mx[j], 16, 64));
+      mx[j] = fmaxf(mx[j], __shfl_xor(mx[j], 32, 64));
+    }
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) {
+      const float off = mx[j] * sl;
+      sum[j] = 0.f;
+      rs[j] = 0.f;
+#pragma unroll
+      for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (in_v(i, r)) {
+            sum[j] += fast_exp2(__builtin_fmaf(acc[i][j][r], sl, -off));
+            if (rpart != nullptr) rs[j] += acc[i][j][r];
+          }
+    }
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) {
+      sum[j] += __shfl_xor(sum[j], 16, 64);
+      sum[j] += __shfl_xor(sum[j], 32, 64);
+      if (rpart != nullptr) {
+        rs[j] += __shfl_xor(rs[j], 16, 64);
+        rs[j] += __shfl_xor(rs[j], 32, 64);
+      }
+    }
+    if (lane < 16) {
+#pragma unroll
+      for (int j = 0; j < kTN; ++j) {
+        const int tok = n0 + acc_col(wn, j, lane);
+        if (tok < C) {
+          part[(int64_t)(vbase / 128) * ldp + tok] = floatx2{mx[j] * s, sum[j]};
+          if (rpart != nullptr) rpart[(int64_t)(vbase / 128) * ldp + tok] = rs[j] * s;  // sum z
+        }
+      }
+    }
+  }
+  if (kStoreZ) {
+    // blocked layout: zblk(tok, v) = ((tok / 16) * (ldz / 4) + v / 4) * 64 + (tok % 16) * 4 + v % 4,
+    // so one store instruction (16 tokens x 16 vocabulary) writes 512 contiguous bytes
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) {
+      const int tok = n0 + acc_col(wn, j, lane);
+      if (tok >= C) continue;
+      bf16* zt = zbuf + ((int64_t)(tok >> 4) * (ldz >> 2)) * 64 + (tok & 15) * 4;
+#pragma unroll
+      for (int i = 0; i < kTM; ++i) {
+        const int row0 = m0 + acc_row(wm, i, lane, 0);
+        bf16x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = (bf16)acc[i][j][r];
+        bf16* dst = zt + (int64_t)(row0 >> 2) * 64;
+        if (kFull || row0 + 3 < V) {
+          __builtin_nontemporal_store(v, (bf16x4*)dst);  // read once, by dlogits
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (row0 + r < V) dst[r] = v[r];
+        }
+      }
+    }
+  }
+}
+
 template <bool kStoreZ, bool kPart>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_logits_bf16(
     const bf16* __restrict__ W, const bf16* __restrict__ bias, const bf16* __restrict__ h, int V,
@@ -320,7 +412,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_logits_bf16(
   const int vbase = m0 + wm * kTM * 16;
   if (vbase >= V) return;
   const bool full = vbase + kTM * 16 <= V;
-  const float sl = s * kLog2e;
   if (bias != nullptr) {  // F.linear's bias, before the logit scale
     bf16x4 bv[kTM];  // rows row0 .. row0 + 3 of sub-tile i (row0 % 4 == 0): one 8-byte load
 #pragma unroll
@@ -342,62 +433,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_logits_bf16(
         for (int j = 0; j < kTN; ++j) acc[i][j][r] += b;
       }
   }
-#pragma unroll
-  for (int j = 0; j < kTN; ++j) {
-    const int tok = n0 + acc_col(wn, j, lane);
-    if (kPart) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < kTM; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (full || m0 + acc_row(wm, i, lane, r) < V) mx = fmaxf(mx, acc[i][j][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float off = mx * sl;
-      float sum = 0.f;
-#pragma unroll
-      for (int i = 0; i < kTM; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (full || m0 + acc_row(wm, i, lane, r) < V)
-            sum += fast_exp2(__builtin_fmaf(acc[i][j][r], sl, -off));
-      sum += __shfl_xor(sum, 16, 64);
-      sum += __shfl_xor(sum, 32, 64);
-      if (lane < 16 && tok < C) part[(int64_t)(vbase / 128) * ldp + tok] = floatx2{mx * s, sum};
-      if (rpart != nullptr) {  // row sum of the logits (label-smoothing term)
-        float rs = 0.f;
-#pragma unroll
-        for (int i = 0; i < kTM; ++i)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (full || m0 + acc_row(wm, i, lane, r) < V) rs += acc[i][j][r];
-        rs += __shfl_xor(rs, 16, 64);
-        rs += __shfl_xor(rs, 32, 64);
-        if (lane < 16 && tok < C) rpart[(int64_t)(vbase / 128) * ldp + tok] = rs * s;
-      }
-    }
-    if (kStoreZ && tok < C) {
-      // blocked layout: zblk(tok, v) = ((tok / 16) * (ldz / 4) + v / 4) * 64 + (tok % 16) * 4 + v % 4,
-      // so one store instruction (16 tokens x 16 vocabulary) writes 512 contiguous bytes
-      bf16* zt = zbuf + ((int64_t)(tok >> 4) * (ldz >> 2)) * 64 + (tok & 15) * 4;
-#pragma unroll
-      for (int i = 0; i < kTM; ++i) {
-        const int row0 = m0 + acc_row(wm, i, lane, 0);
-        bf16x4 v;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = (bf16)acc[i][j][r];
-        bf16* dst = zt + (int64_t)(row0 >> 2) * 64;
-        if (full || row0 + 3 < V) {
-          __builtin_nontemporal_store(v, (bf16x4*)dst);  // read once, by dlogits
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (row0 + r < V) dst[r] = v[r];
-        }
-      }
-    }
-  }
+  if (full)
+    logits_epilogue<kStoreZ, kPart, true>(acc, V, C, m0, n0, wm, wn, lane, s, part, rpart, ldp, zbuf,
+                                          ldz);
+  else
+    logits_epilogue<kStoreZ, kPart, false>(acc, V, C, m0, n0, wm, wn, lane, s, part, rpart, ldp,
+                                           zbuf, ldz);
 }
 
 // ---------------------------------------------------------------------------
