@@ -177,6 +177,14 @@ def cpu_baseline(w, rows: int) -> dict:
             "seconds": dt}
 
 
+def env_info(torch) -> dict:
+    """Device, HIP runtime and PyTorch versions of the run."""
+    p = torch.cuda.get_device_properties(0)
+    return {"device": p.name, "arch": getattr(p, "gcnArchName", ""),
+            "compute_units": p.multi_processor_count, "hip": torch.version.hip,
+            "torch": torch.__version__}
+
+
 def _timed(fn, steps: int, warmup: int):
     """(ms per call, {stage: ms per call}) with the library's stage events."""
     import torch
@@ -318,6 +326,7 @@ def shard_bench(args, w) -> int:
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic_entry(dom, "shard"), "avg_launch_ms": cands[dom],
                      "flops_per_launch": gemm},
+        "env": env_info(torch),
     }
     print(json.dumps(result), flush=True)
     return 0
@@ -330,7 +339,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="headline")
     ap.add_argument("--chunk-rows", type=int, default=0)
-    ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--cpu-rows", type=int, default=6144,
+                    help="token rows the float64 oracle baseline runs on (~14 s on 16 cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", default="", help="comma-separated chunk sizes to time as well")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -397,13 +407,19 @@ def main() -> int:
             fldce.fldce_fwd_bwd(h, W, tgt, pm, **kw)
         torch.cuda.synchronize()
         fldce.fldce_profile_begin()
+        # one event between consecutive steps on the library's stream (the
+        # current one): per-step times without any synchronisation in the loop
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(steps):
+        ev[0].record()
+        for i in range(steps):
             fldce.fldce_fwd_bwd(h, W, tgt, pm, **kw)
+            ev[i + 1].record()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         fldce.fldce_profile_end()
+        per_step = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
         stages = {}
         for s in range(fldce.fldce_profile_num_stages()):
             ms, n = fldce.fldce_profile_read(s)
@@ -411,12 +427,16 @@ def main() -> int:
                 stages[fldce.fldce_profile_stage_name(s)] = dict(total_ms=ms, launches=n)
         loss = float(out["loss"].item())
         del ws
-        return (t1 - t0) * 1e3 / steps, stages, loss
+        dist = {"median": round(float(np.median(per_step)), 4),
+                "p10": round(float(np.percentile(per_step, 10)), 4),
+                "p90": round(float(np.percentile(per_step, 90)), 4),
+                "min": round(float(per_step.min()), 4)}
+        return (t1 - t0) * 1e3 / steps, stages, loss, dist
 
     n_valid = int(np.count_nonzero(target != synth.IGNORE_INDEX))
     C = args.chunk_rows or fldce.fldce_default_chunk_rows(N, H, V)
     log(f"timing {args.steps} steps after {args.warmup} warmup (chunk_rows={C})")
-    ms, stages, loss = run_config(args.chunk_rows, args.steps, args.warmup)
+    ms, stages, loss, dist = run_config(args.chunk_rows, args.steps, args.warmup)
     # bf16 multiplies only rows whose target != ignore_index (the others are
     # exactly zero); fp32 multiplies every row
     rows_mult = n_valid if w.dtype == "bf16" else N
@@ -459,8 +479,10 @@ def main() -> int:
         "rows_multiplied": rows_mult,
         "tflops_nominal_6NHV": round(flops_nominal / (ms * 1e-3) / 1e12, 2),
         "loss": loss,
+        "step_ms": dist,
         "stage_ms_per_step": stage_ms,
         "roofline": roofline,
+        "env": env_info(torch),
     }
     if not args.no_extras:
         result.update(extra_legs(args, w, h, W, tgt, pm, dt, rows_mult, ms, peak))
@@ -468,7 +490,7 @@ def main() -> int:
         sw = {}
         for c in [int(x) for x in args.sweep.split(",") if x]:
             log(f"sweep chunk_rows={c}")
-            m, _, _ = run_config(c, max(3, args.steps // 4), 1)
+            m, _, _, _ = run_config(c, max(3, args.steps // 4), 1)
             sw[str(c)] = {"ms_per_step": round(m, 3), "tflops": round(flops / (m * 1e-3) / 1e12, 1),
                           "tokens_per_s": round(N / (m * 1e-3), 1)}
         result["chunk_sweep"] = sw
