@@ -75,9 +75,9 @@ enum fldce_status {
   FLDCE_ERR_WORKSPACE = -5,      /* workspace NULL or smaller than required   */
   FLDCE_ERR_ALIGNMENT = -6,      /* a pointer is not 16-byte aligned          */
   FLDCE_ERR_HIP = -7,            /* a kernel launch failed                    */
-  FLDCE_ERR_UNSUPPORTED = -8     /* shape the bf16 path does not handle: H not
-                                    a multiple of 64, or a GEMM grid of 2^32
-                                    work-items or more                         */
+  FLDCE_ERR_UNSUPPORTED = -8     /* shape the kernels do not handle: bf16 with
+                                    H not a multiple of 64 or a GEMM grid of
+                                    2^32 work-items or more; fp32 with V >= 2^30 */
 };
 
 /* Library version (FLDCE_VERSION of the build). */
@@ -127,6 +127,9 @@ size_t fldce_workspace_size(int64_t N, int64_t H, int64_t V, int dtype,
  * valid rows are compacted on the device and only they go through the three
  * GEMMs; their dH rows are written as +0.
  *
+ * Sizes: 0 <= N < 2^28, 0 < V < 2^31, 0 < H <= 2^20 (FLDCE_ERR_BAD_SHAPE
+ * otherwise, and the workspace queries return 0); the same range holds for
+ * every entry point below (V_local in place of V for the shard calls).
  * bf16 requires H % 64 == 0 (FLDCE_ERR_UNSUPPORTED otherwise); all pointers
  * must be 16-byte aligned.
  */

@@ -225,21 +225,31 @@ struct StageTimer {
 
 bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// Shape range of every entry point: N < 2^28 rows, 0 < V < 2^31, 0 < H <= 2^20.
+bool sizes_in_range(int64_t N, int64_t H, int64_t V) {
+  return N >= 0 && N < (int64_t(1) << 28) && H > 0 && H <= (int64_t(1) << 20) && V > 0 &&
+         V < (int64_t(1) << 31);
+}
+
 int check_common(const void* h, const void* W, const int64_t* target, int64_t N, int64_t H,
                  int64_t V, int dtype, float logit_scale) {
   if (!W || (N > 0 && (!h || !target))) return FLDCE_ERR_NULL_POINTER;
   if (dtype != FLDCE_DTYPE_F32 && dtype != FLDCE_DTYPE_BF16) return FLDCE_ERR_BAD_DTYPE;
-  if (N < 0 || H <= 0 || V <= 0 || N > (int64_t(1) << 31) - 1 || V > (int64_t(1) << 31) - 1 ||
-      H > (int64_t(1) << 20))
-    return FLDCE_ERR_BAD_SHAPE;
+  if (!sizes_in_range(N, H, V)) return FLDCE_ERR_BAD_SHAPE;
   if (!(logit_scale > 0.f) || !std::isfinite(logit_scale)) return FLDCE_ERR_BAD_ARGUMENT;
   if (dtype == FLDCE_DTYPE_BF16 && H % kBK != 0) return FLDCE_ERR_UNSUPPORTED;
+  // fp32 kernels put 4 work-items per vocabulary row on one grid dimension
+  if (dtype == FLDCE_DTYPE_F32 && V >= (int64_t(1) << 30)) return FLDCE_ERR_UNSUPPORTED;
   return FLDCE_OK;
 }
 
 int launch_status() { return hipGetLastError() == hipSuccess ? FLDCE_OK : FLDCE_ERR_HIP; }
 
 inline unsigned grid1(int64_t n, int64_t per) { return (unsigned)cdiv(n, per); }
+// Grid of a grid-stride kernel over n items, `per` per block.
+inline unsigned grid_strided(int64_t n, int64_t per) {
+  return (unsigned)std::min<int64_t>(std::max<int64_t>(cdiv(n, per), 1), 65536);
+}
 
 void launch_transpose(const float* src, int64_t R, int64_t Cn, int64_t lds, float* dst,
                       int64_t ldd, int64_t Rp, hipStream_t st) {
@@ -325,10 +335,10 @@ int run_core_bf16(const Core& c, const Plan& p, char* ws, hipStream_t st) {
   {
     StageTimer tm(kPrep, st);
     if (c.dH_f32)
-      k_zero_ignored_rows<float><<<(unsigned)c.N, 256, 0, st>>>(c.target, c.N, c.ignore,
+      k_zero_ignored_rows<float><<<grid_strided(c.N, 1), 256, 0, st>>>(c.target, c.N, c.ignore,
                                                                (float*)c.dH, H);
     else
-      k_zero_ignored_rows<bf16><<<(unsigned)c.N, 256, 0, st>>>(c.target, c.N, c.ignore,
+      k_zero_ignored_rows<bf16><<<grid_strided(c.N, 1), 256, 0, st>>>(c.target, c.N, c.ignore,
                                                               (bf16*)c.dH, H);
   }
   for (int64_t ic = 0; ic < p.nchunks; ++ic) {
@@ -504,7 +514,7 @@ void launch_row_dots(const void* h, const void* W, const void* bias, const int64
                      int64_t N, int64_t H, int64_t V, bool bf, int64_t ignore, float s, bool smooth,
                      float* colpart, float* wsum, float* bsum, float* zt, float* R, hipStream_t st) {
   if (bf) {
-    k_rowdot<bf16><<<grid1(N, 4), 256, 0, st>>>((const bf16*)h, (const bf16*)W, (const bf16*)bias,
+    k_rowdot<bf16><<<grid_strided(N, 4), 256, 0, st>>>((const bf16*)h, (const bf16*)W, (const bf16*)bias,
                                                  H, target, 0, V, ignore, s, nullptr, nullptr, N,
                                                  zt, nullptr);
     return;
@@ -513,7 +523,7 @@ void launch_row_dots(const void* h, const void* W, const void* bias, const int64
     launch_colsum((const float*)W, V, H, colpart, wsum, st);
     if (bias != nullptr) launch_colsum((const float*)bias, V, 1, colpart, bsum, st);
   }
-  k_rowdot<float><<<grid1(N, 4), 256, 0, st>>>(
+  k_rowdot<float><<<grid_strided(N, 4), 256, 0, st>>>(
       (const float*)h, (const float*)W, (const float*)bias, H, target, 0, V, ignore, s,
       smooth ? wsum : nullptr, (smooth && bias != nullptr) ? bsum : nullptr, N, zt,
       smooth ? R : nullptr);
@@ -549,18 +559,18 @@ int64_t fldce_default_chunk_rows(int64_t N, int64_t H, int64_t V) {
 }
 
 size_t fldce_workspace_size(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_rows) {
-  if (N < 0 || H <= 0 || V <= 0 || (dtype != 0 && dtype != 1)) return 0;
+  if (!sizes_in_range(N, H, V) || (dtype != 0 && dtype != 1)) return 0;
   return make_plan(kFwdBwd, N, H, V, dtype, chunk_rows).total;
 }
 
 size_t fldce_shard_partials_workspace_size(int64_t N, int64_t H, int64_t V_local, int dtype) {
-  if (N < 0 || H <= 0 || V_local <= 0 || (dtype != 0 && dtype != 1)) return 0;
+  if (!sizes_in_range(N, H, V_local) || (dtype != 0 && dtype != 1)) return 0;
   return make_plan(kShardPartials, N, H, V_local, dtype, 0).total;
 }
 
 size_t fldce_shard_bwd_workspace_size(int64_t N, int64_t H, int64_t V_local, int dtype,
                                       int64_t chunk_rows) {
-  if (N < 0 || H <= 0 || V_local <= 0 || (dtype != 0 && dtype != 1)) return 0;
+  if (!sizes_in_range(N, H, V_local) || (dtype != 0 && dtype != 1)) return 0;
   return make_plan(kShardBwd, N, H, V_local, dtype, chunk_rows).total;
 }
 
@@ -643,7 +653,7 @@ int fldce_fwd_bwd_ex(const void* h, const void* W, const void* bias, const int64
 }
 
 size_t fldce_fwd_workspace_size(int64_t N, int64_t H, int64_t V, int dtype) {
-  if (N < 0 || H <= 0 || V <= 0 || (dtype != 0 && dtype != 1)) return 0;
+  if (!sizes_in_range(N, H, V) || (dtype != 0 && dtype != 1)) return 0;
   return make_plan(kFwd, N, H, V, dtype, 0).total;
 }
 
@@ -820,7 +830,7 @@ int fldce_shard_partials(const void* h, const void* W_local, const int64_t* targ
           nullptr, 0, row_max, row_sumexp, row_sumlogit);
     }
     StageTimer tm(kPrep, st);
-    k_rowdot<bf16><<<grid1(N, 4), 256, 0, st>>>((const bf16*)h, (const bf16*)W_local, nullptr, H,
+    k_rowdot<bf16><<<grid_strided(N, 4), 256, 0, st>>>((const bf16*)h, (const bf16*)W_local, nullptr, H,
                                                  target, vocab_start, V, ignore_index, logit_scale,
                                                  nullptr, nullptr, N, target_logit, nullptr);
   } else {
@@ -838,7 +848,7 @@ int fldce_shard_partials(const void* h, const void* W_local, const int64_t* targ
           row_max, row_sumexp, nullptr);
     }
     if (row_sumlogit) launch_colsum((const float*)W_local, V, H, colpart, wsum, st);
-    k_rowdot<float><<<grid1(N, 4), 256, 0, st>>>((const float*)h, (const float*)W_local, nullptr, H,
+    k_rowdot<float><<<grid_strided(N, 4), 256, 0, st>>>((const float*)h, (const float*)W_local, nullptr, H,
                                                   target, vocab_start, V, ignore_index, logit_scale,
                                                   row_sumlogit ? wsum : nullptr, nullptr, N,
                                                   target_logit, row_sumlogit);

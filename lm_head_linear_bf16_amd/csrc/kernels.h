@@ -112,14 +112,16 @@ __global__ __launch_bounds__(256) void k_ignored_rows_init(const int64_t* __rest
   if (c) c[i] = vc;
 }
 
-// Rows of dH that belong to ignored targets are exactly +0 (one block per row).
+// Rows of dH that belong to ignored targets are exactly +0 (one block per
+// row, grid-stride over the rows).
 template <typename T>
 __global__ __launch_bounds__(256) void k_zero_ignored_rows(const int64_t* __restrict__ target,
                                                            int64_t N, int64_t ignore,
                                                            T* __restrict__ out, int64_t H) {
-  const int64_t i = blockIdx.x;
-  if (i >= N || target[i] != ignore) return;
-  for (int64_t e = threadIdx.x; e < H; e += 256) out[i * H + e] = from_f32<T>(0.f);
+  for (int64_t i = blockIdx.x; i < N; i += gridDim.x) {
+    if (target[i] != ignore) continue;
+    for (int64_t e = threadIdx.x; e < H; e += 256) out[i * H + e] = from_f32<T>(0.f);
+  }
 }
 
 // Number of rows of a chunk: the compacted rows [c0, c0 + cmax) that exist.
@@ -238,17 +240,16 @@ __global__ __launch_bounds__(256) void k_colsum_finish(const float* __restrict__
 // logits[y]; the row sum feeds the label-smoothing term.  bias and bsum may
 // be null (no bias).
 // ---------------------------------------------------------------------------
+// One row of k_rowdot, computed by one wave.
 template <typename T>
-__global__ __launch_bounds__(256) void k_rowdot(const T* __restrict__ h, const T* __restrict__ W,
-                                                const T* __restrict__ bias, int64_t H,
-                                                const int64_t* __restrict__ target, int64_t v0,
-                                                int64_t Vl, int64_t ignore, float s,
-                                                const float* __restrict__ wsum,
-                                                const float* __restrict__ bsum, int64_t N,
-                                                float* __restrict__ zt, float* __restrict__ R) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= N) return;
+__device__ __forceinline__ void rowdot_row(const T* __restrict__ h, const T* __restrict__ W,
+                                           const T* __restrict__ bias, int64_t H,
+                                           const int64_t* __restrict__ target, int64_t v0,
+                                           int64_t Vl, int64_t ignore, float s,
+                                           const float* __restrict__ wsum,
+                                           const float* __restrict__ bsum,
+                                           float* __restrict__ zt, float* __restrict__ R,
+                                           int64_t row, int lane) {
   const int64_t y = target[row];
   const int64_t col = y - v0;
   const bool in = (y != ignore) && col >= 0 && col < Vl;
@@ -287,6 +288,20 @@ __global__ __launch_bounds__(256) void k_rowdot(const T* __restrict__ h, const T
     if (zt != nullptr) zt[row] = in ? s * a : 0.f;
     if (R != nullptr) R[row] = s * b;
   }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_rowdot(const T* __restrict__ h, const T* __restrict__ W,
+                                                const T* __restrict__ bias, int64_t H,
+                                                const int64_t* __restrict__ target, int64_t v0,
+                                                int64_t Vl, int64_t ignore, float s,
+                                                const float* __restrict__ wsum,
+                                                const float* __restrict__ bsum, int64_t N,
+                                                float* __restrict__ zt, float* __restrict__ R) {
+  const int lane = threadIdx.x & 63;
+  for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < N;
+       row += (int64_t)gridDim.x * 4)
+    rowdot_row<T>(h, W, bias, H, target, v0, Vl, ignore, s, wsum, bsum, zt, R, row, lane);
 }
 
 // ---------------------------------------------------------------------------

@@ -51,6 +51,9 @@ def test_workspace_queries(L):
     assert fldce.fldce_workspace_size(0, 64, 10, 1) > 0
     assert fldce.fldce_workspace_size(-1, 64, 10, 1) == 0
     assert fldce.fldce_workspace_size(10, 64, 10, 7) == 0
+    assert fldce.fldce_workspace_size(1 << 28, 64, 10, 1) == 0
+    assert fldce.fldce_fwd_workspace_size(10, 64, 1 << 31, 1) == 0
+    assert fldce.fldce_shard_bwd_workspace_size(10, (1 << 20) + 64, 10, 1) == 0
     assert fldce.fldce_shard_partials_workspace_size(32768, 5120, 18992, 1) > 0
     assert fldce.fldce_shard_bwd_workspace_size(32768, 5120, 18992, 1) > 0
     assert fldce.fldce_default_chunk_rows(8192, 2560, 151936) == 8192
@@ -82,6 +85,9 @@ def test_fwd_bwd_argument_checks(L):
     assert _fwd(L, N=-1) == -2
     assert _fwd(L, V=0) == -2
     assert _fwd(L, H=0) == -2
+    assert _fwd(L, N=1 << 28) == -2          # documented range: N < 2^28, V < 2^31, H <= 2^20
+    assert _fwd(L, V=1 << 31) == -2
+    assert _fwd(L, H=(1 << 20) + 64) == -2
     assert _fwd(L, red=2) == -4
     assert _fwd(L, eps=-0.1) == -4
     assert _fwd(L, eps=1.5) == -4
@@ -97,6 +103,7 @@ def test_fwd_bwd_argument_checks(L):
     assert _fwd(L, H=100) == -8          # bf16 needs H % 64 == 0
     assert _fwd(L, V=(1 << 31) - 1, N=1 << 20) == -8   # logits grid past 2^32 work-items
     assert _fwd(L, H=100, dtype=0, wsb=16) == -5   # fp32 takes any H (fails later on workspace)
+    assert _fwd(L, V=1 << 30, dtype=0) == -8    # fp32 grids hold 4 work-items per vocabulary row
 
 
 def test_shard_argument_checks(L):
