@@ -58,8 +58,8 @@ struct TileCoord {
 // the same share and neighbouring tiles share its L2.  Within the order,
 // tiles go in groups of `group_m` tile rows.  Blocks without an item are
 // inactive.
-__device__ __forceinline__ TileCoord tile_coord(int tiles_m, int tiles_n, int splits, int group_m) {
-  const int bid = blockIdx.x;
+__host__ __device__ inline TileCoord tile_coord_of(int bid, int tiles_m, int tiles_n, int splits,
+                                                   int group_m) {
   const int x = bid % 8, idx = bid / 8;
   const int tiles = tiles_m * tiles_n;
   const int A = tiles * splits;
@@ -77,6 +77,9 @@ __device__ __forceinline__ TileCoord tile_coord(int tiles_m, int tiles_n, int sp
   c.tm = first_m + w % gm;
   c.tn = w / gm;
   return c;
+}
+__device__ __forceinline__ TileCoord tile_coord(int tiles_m, int tiles_n, int splits, int group_m) {
+  return tile_coord_of(blockIdx.x, tiles_m, tiles_n, splits, group_m);
 }
 
 // 16-byte chunk position of logical chunk c (0..7) in LDS row r.
