@@ -95,7 +95,8 @@ int main() {
   const Shape shapes[] = {
       {1, 64, 100, 0},      {300, 64, 1000, 0},   {700, 192, 3001, 256}, {2048, 2560, 151936, 0},
       {8192, 2560, 151936, 0}, {8192, 2560, 151936, 1024}, {5000, 4096, 151936, 2048},
-      {3000, 5120, 18992, 0}, {4096, 128, 5000, 1000}, {600, 64 * 40, 7000, 0}};
+      {3000, 5120, 18992, 0}, {4096, 128, 5000, 1000}, {600, 64 * 40, 7000, 0},
+      {797, 320, 3000, 100}, {797, 64, 257, 333}, {1, 64, 1, 0}, {199, 192, 2, 64}};
   for (const Shape& s : shapes)
     for (int mode : {kFwdBwd, kShardBwd})
       if (check_plan(mode, s.N, s.H, s.V, s.chunk)) return 1;
