@@ -118,6 +118,47 @@ def _check(t: torch.Tensor, name: str, dtype=None) -> None:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _check_inputs(h, W, target, p_mask=None, bias=None, lse=None, w_name="W"):
+    """Size, device, layout and dtype checks of the inputs (the kernels read
+    exactly N rows of h, target, p_mask and lse and V rows of W and bias):
+    returns (N, H, V).  Sizes are checked first."""
+    if h.dim() != 2 or W.dim() != 2:
+        raise ValueError(f"h and {w_name} must be 2-D, got {tuple(h.shape)} and {tuple(W.shape)}")
+    N, H = h.shape
+    V = W.shape[0]
+    if W.shape[1] != H:
+        raise ValueError(f"{w_name} must have {H} columns like h, got {W.shape[1]}")
+    for name, t, n in (("target", target, N), ("p_mask", p_mask, N), ("lse", lse, N),
+                       ("bias", bias, V)):
+        if t is not None and t.numel() != n:
+            raise ValueError(f"{name} must hold {n} elements, got {t.numel()}")
+    _check(h, "h")
+    _check(W, w_name, h.dtype)
+    _check(target, "target", torch.int64)
+    for name, t in (("p_mask", p_mask), ("lse", lse)):
+        if t is not None:
+            _check(t, name, torch.float32)
+    if bias is not None:
+        _check(bias, "bias", h.dtype)
+    return N, H, V
+
+def _out(out: Optional[dict], name: str, numel: int, like: torch.Tensor, dtype=None,
+         shape=None) -> torch.Tensor:
+    """The caller's output tensor ``out[name]`` (checked: device, contiguous,
+    dtype and element count, so no kernel writes past it) or a new one of
+    ``shape`` (default: like ``like``)."""
+    dtype = like.dtype if dtype is None else dtype
+    t = (out or {}).get(name)
+    if t is None:
+        if shape is None:
+            return torch.empty_like(like, dtype=dtype)
+        return torch.empty(shape, dtype=dtype, device=like.device)
+    if t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements, got {t.numel()}")
+    _check(t, name, dtype)
+    return t
+
+
 def _stream(dev: torch.device) -> int:
     return torch.cuda.current_stream(dev).cuda_stream
 
@@ -183,23 +224,16 @@ def fldce_fwd_bwd(h: torch.Tensor, W: torch.Tensor, target: torch.Tensor,
     """loss, dH, dW (and per-row lse / loss with row_stats) of the fused LM-head
     cross-entropy.  h [N,H], W [V,H] (fp32 or bf16, same dtype), target int64
     [N], p_mask fp32 [N] or None.  Outputs may be passed in ``out``."""
-    N, H = h.shape
-    V = W.shape[0]
-    _check(h, "h")
-    _check(W, "W", h.dtype)
-    _check(target, "target", torch.int64)
-    if p_mask is not None:
-        _check(p_mask, "p_mask", torch.float32)
+    N, H, V = _check_inputs(h, W, target, p_mask)
     dev = h.device
     code = _dtype_code(h.dtype)
-    o = dict(out or {})
-    loss = o.get("loss") if o.get("loss") is not None else torch.empty(1, dtype=torch.float32, device=dev)
-    dH = o.get("dH") if o.get("dH") is not None else torch.empty_like(h)
-    dW = o.get("dW") if o.get("dW") is not None else torch.empty_like(W)
+    loss = _out(out, "loss", 1, h, torch.float32, (1,))
+    dH = _out(out, "dH", N * H, h)
+    dW = _out(out, "dW", V * H, W)
     lse = rl = None
     if row_stats:
-        lse = torch.empty(N, dtype=torch.float32, device=dev)
-        rl = torch.empty(N, dtype=torch.float32, device=dev)
+        lse = _out(out, "row_lse", N, h, torch.float32, (N,))
+        rl = _out(out, "row_loss", N, h, torch.float32, (N,))
     nbytes = lib().fldce_workspace_size(N, H, V, code, chunk_rows)
     ws = _workspace(nbytes, dev, workspace)
     rc = lib().fldce_fwd_bwd(_ptr(h), _ptr(W), _ptr(target), _ptr(p_mask), N, H, V, code,
@@ -224,32 +258,24 @@ def fldce_fwd_bwd_ex(h: torch.Tensor, W: torch.Tensor, target: torch.Tensor,
                      logit_scale: float = 1.0, reduction="mean", total: int = 0,
                      eob_token_id: Optional[int] = None, eob_weight: float = 1.0,
                      want_db: Optional[bool] = None, chunk_rows: int = 0,
-                     row_stats: bool = False, workspace: Optional[torch.Tensor] = None) -> dict:
+                     row_stats: bool = False, workspace: Optional[torch.Tensor] = None,
+                     out: Optional[dict] = None) -> dict:
     """fldce_fwd_bwd plus page 1's optional bias [V] (and its gradient db,
     returned when ``want_db`` or, by default, when a bias is given) and the
-    end-of-block weight (rows whose target is ``eob_token_id``)."""
-    N, H = h.shape
-    V = W.shape[0]
-    _check(h, "h")
-    _check(W, "W", h.dtype)
-    _check(target, "target", torch.int64)
-    if p_mask is not None:
-        _check(p_mask, "p_mask", torch.float32)
-    if bias is not None:
-        _check(bias, "bias", h.dtype)
-        if bias.shape != (V,):
-            raise ValueError(f"bias must have shape ({V},)")
+    end-of-block weight (rows whose target is ``eob_token_id``).  Outputs
+    may be passed in ``out`` (loss, dH, dW, db, row_lse, row_loss)."""
+    N, H, V = _check_inputs(h, W, target, p_mask, bias)
     dev = h.device
     code = _dtype_code(h.dtype)
     want_db = (bias is not None) if want_db is None else want_db
-    loss = torch.empty(1, dtype=torch.float32, device=dev)
-    dH = torch.empty_like(h)
-    dW = torch.empty_like(W)
-    db = torch.empty(V, dtype=h.dtype, device=dev) if want_db else None
+    loss = _out(out, "loss", 1, h, torch.float32, (1,))
+    dH = _out(out, "dH", N * H, h)
+    dW = _out(out, "dW", V * H, W)
+    db = _out(out, "db", V, h, h.dtype, (V,)) if want_db else None
     lse = rl = None
     if row_stats:
-        lse = torch.empty(N, dtype=torch.float32, device=dev)
-        rl = torch.empty(N, dtype=torch.float32, device=dev)
+        lse = _out(out, "row_lse", N, h, torch.float32, (N,))
+        rl = _out(out, "row_loss", N, h, torch.float32, (N,))
     nbytes = lib().fldce_workspace_size(N, H, V, code, chunk_rows)
     ws = _workspace(nbytes, dev, workspace)
     rc = lib().fldce_fwd_bwd_ex(_ptr(h), _ptr(W), _ptr(bias), _ptr(target), _ptr(p_mask), N, H, V,
@@ -275,26 +301,17 @@ def fldce_fwd(h: torch.Tensor, W: torch.Tensor, target: torch.Tensor,
               ignore_index: int = -100, label_smoothing: float = 0.0, logit_scale: float = 1.0,
               reduction="mean", total: int = 0, eob_token_id: Optional[int] = None,
               eob_weight: float = 1.0, row_stats: bool = False,
-              workspace: Optional[torch.Tensor] = None) -> dict:
-    """Forward only: loss (and per-row lse / loss with row_stats), no gradients."""
-    N, H = h.shape
-    V = W.shape[0]
-    _check(h, "h")
-    _check(W, "W", h.dtype)
-    _check(target, "target", torch.int64)
-    if p_mask is not None:
-        _check(p_mask, "p_mask", torch.float32)
-    if bias is not None:
-        _check(bias, "bias", h.dtype)
-        if bias.shape != (V,):
-            raise ValueError(f"bias must have shape ({V},)")
+              workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None) -> dict:
+    """Forward only: loss (and per-row lse / loss with row_stats), no gradients.
+    Outputs may be passed in ``out`` (loss, row_lse, row_loss)."""
+    N, H, V = _check_inputs(h, W, target, p_mask, bias)
     dev = h.device
     code = _dtype_code(h.dtype)
-    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    loss = _out(out, "loss", 1, h, torch.float32, (1,))
     lse = rl = None
     if row_stats:
-        lse = torch.empty(N, dtype=torch.float32, device=dev)
-        rl = torch.empty(N, dtype=torch.float32, device=dev)
+        lse = _out(out, "row_lse", N, h, torch.float32, (N,))
+        rl = _out(out, "row_loss", N, h, torch.float32, (N,))
     nbytes = lib().fldce_fwd_workspace_size(N, H, V, code)
     ws = _workspace(nbytes, dev, workspace)
     rc = lib().fldce_fwd(_ptr(h), _ptr(W), _ptr(bias), _ptr(target), _ptr(p_mask), N, H, V, code,
@@ -332,18 +349,17 @@ def fldce_scale_grads(grad_out: torch.Tensor, dH: Optional[torch.Tensor] = None,
 
 def fldce_shard_partials(h: torch.Tensor, W_local: torch.Tensor, target: torch.Tensor,
                          vocab_start: int, ignore_index: int = -100, logit_scale: float = 1.0,
-                         sumlogit: bool = True, workspace: Optional[torch.Tensor] = None) -> dict:
-    """Per-row (max, sum-exp, target logit, sum of logits) of one vocabulary shard."""
-    N, H = h.shape
-    V_local = W_local.shape[0]
-    _check(h, "h")
-    _check(W_local, "W_local", h.dtype)
-    _check(target, "target", torch.int64)
+                         sumlogit: bool = True, workspace: Optional[torch.Tensor] = None,
+                         out: Optional[dict] = None) -> dict:
+    """Per-row (max, sum-exp, target logit, sum of logits) of one vocabulary
+    shard.  Outputs may be passed in ``out`` (row_max, row_sumexp,
+    target_logit, row_sumlogit)."""
+    N, H, V_local = _check_inputs(h, W_local, target, w_name="W_local")
     dev = h.device
     code = _dtype_code(h.dtype)
-    f = lambda: torch.empty(N, dtype=torch.float32, device=dev)  # noqa: E731
-    m, S, t = f(), f(), f()
-    r = f() if sumlogit else None
+    f = lambda name: _out(out, name, N, h, torch.float32, (N,))  # noqa: E731
+    m, S, t = f("row_max"), f("row_sumexp"), f("target_logit")
+    r = f("row_sumlogit") if sumlogit else None
     nbytes = lib().fldce_shard_partials_workspace_size(N, H, V_local, code)
     ws = _workspace(nbytes, dev, workspace)
     rc = lib().fldce_shard_partials(_ptr(h), _ptr(W_local), _ptr(target), N, H, V_local,
@@ -358,20 +374,15 @@ def fldce_shard_bwd(h: torch.Tensor, W_local: torch.Tensor, target: torch.Tensor
                     p_mask: Optional[torch.Tensor], lse: torch.Tensor, vocab_start: int,
                     V_global: int, ignore_index: int = -100, label_smoothing: float = 0.0,
                     logit_scale: float = 1.0, reduction="mean", total: int = 0,
-                    chunk_rows: int = 0, workspace: Optional[torch.Tensor] = None) -> dict:
-    """dH_partial (fp32) and dW_local of one vocabulary shard given the global lse."""
-    N, H = h.shape
-    V_local = W_local.shape[0]
-    _check(h, "h")
-    _check(W_local, "W_local", h.dtype)
-    _check(target, "target", torch.int64)
-    _check(lse, "lse", torch.float32)
-    if p_mask is not None:
-        _check(p_mask, "p_mask", torch.float32)
+                    chunk_rows: int = 0, workspace: Optional[torch.Tensor] = None,
+                    out: Optional[dict] = None) -> dict:
+    """dH_partial (fp32) and dW_local of one vocabulary shard given the global
+    lse.  Outputs may be passed in ``out`` (dH_partial, dW_local)."""
+    N, H, V_local = _check_inputs(h, W_local, target, p_mask, lse=lse, w_name="W_local")
     dev = h.device
     code = _dtype_code(h.dtype)
-    dHp = torch.empty((N, H), dtype=torch.float32, device=dev)
-    dWl = torch.empty_like(W_local)
+    dHp = _out(out, "dH_partial", N * H, h, torch.float32, (N, H))
+    dWl = _out(out, "dW_local", V_local * H, W_local)
     nbytes = lib().fldce_shard_bwd_workspace_size(N, H, V_local, code, chunk_rows)
     ws = _workspace(nbytes, dev, workspace)
     rc = lib().fldce_shard_bwd(_ptr(h), _ptr(W_local), _ptr(target), _ptr(p_mask), _ptr(lse), N,

@@ -188,3 +188,25 @@ def test_binding_rejects_host_tensors():
     h = torch.zeros(4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fldce.fldce_fwd_bwd(h, h, torch.zeros(4, dtype=torch.int64))
+
+
+def test_binding_checks_sizes_before_any_call():
+    """Every input size a kernel relies on is checked in the binding (sizes
+    first, so the checks run here on host tensors): W's columns, target /
+    p_mask / lse / bias lengths.  Caller-given outputs: tests/test_parity_ext_gpu.py."""
+    torch = pytest.importorskip("torch")
+    bf = torch.bfloat16
+    h, W = torch.zeros(4, 64, dtype=bf), torch.zeros(10, 64, dtype=bf)
+    t = torch.zeros(4, dtype=torch.int64)
+    with pytest.raises(ValueError, match="columns"):
+        fldce.fldce_fwd_bwd(h, torch.zeros(10, 128, dtype=bf), t)
+    with pytest.raises(ValueError, match="target must hold 4"):
+        fldce.fldce_fwd_bwd(h, W, torch.zeros(3, dtype=torch.int64))
+    with pytest.raises(ValueError, match="p_mask must hold 4"):
+        fldce.fldce_fwd(h, W, t, torch.ones(5))
+    with pytest.raises(ValueError, match="bias must hold 10"):
+        fldce.fldce_fwd_bwd_ex(h, W, t, None, torch.zeros(9, dtype=bf))
+    with pytest.raises(ValueError, match="lse must hold 4"):
+        fldce.fldce_shard_bwd(h, W, t, None, torch.zeros(2), 0, 10)
+    with pytest.raises(ValueError, match="2-D"):
+        fldce.fldce_shard_partials(h.view(-1), W, t, 0)

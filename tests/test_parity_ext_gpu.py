@@ -324,3 +324,36 @@ def test_deterministic_repeat_ex_and_forward():
     for k in ("loss", "row_lse", "row_loss"):
         assert torch.equal(f1[k], f2[k]), k
         assert torch.equal(f1[k], a[k]), k  # the forward half of fwd_bwd_ex, bit for bit
+
+
+def test_binding_checks_caller_outputs():
+    """Caller-given outputs must hold exactly the elements the kernels write
+    (checked before any launch); correct ones are written in place."""
+    torch = torch_cuda()
+    from lm_head_linear_bf16_amd import fldce
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16
+    h, W = torch.zeros(4, 64, dtype=bf, device=dev), torch.zeros(10, 64, dtype=bf, device=dev)
+    t = torch.zeros(4, dtype=torch.int64, device=dev)
+    say("case caller outputs")
+    with pytest.raises(ValueError, match="dH must hold 256"):
+        fldce.fldce_fwd_bwd(h, W, t, out={"dH": torch.zeros(4, 63, dtype=bf, device=dev)})
+    with pytest.raises(ValueError, match="db must hold 10"):
+        fldce.fldce_fwd_bwd_ex(h, W, t, want_db=True,
+                               out={"db": torch.zeros(11, dtype=bf, device=dev)})
+    with pytest.raises(ValueError, match="dW_local must hold 640"):
+        fldce.fldce_shard_bwd(h, W, t, None, torch.zeros(4, device=dev), 0, 10,
+                              out={"dW_local": torch.zeros(10, 63, dtype=bf, device=dev)})
+    with pytest.raises(TypeError):
+        fldce.fldce_fwd(h, W, t, out={"loss": torch.zeros(1, dtype=torch.float64, device=dev)})
+    o = {k: torch.full(s, float("nan"), dtype=d, device=dev)
+         for k, s, d in (("loss", (1,), torch.float32), ("dH", (4, 64), bf), ("dW", (10, 64), bf),
+                         ("db", (10,), bf), ("row_lse", (4,), torch.float32),
+                         ("row_loss", (4,), torch.float32))}
+    r = fldce.fldce_fwd_bwd_ex(h, W, t, want_db=True, row_stats=True, out=o)
+    torch.cuda.synchronize()
+    for k in o:
+        assert r[k].data_ptr() == o[k].data_ptr(), k
+        assert torch.isfinite(o[k].float()).all(), k
+    # all-zero inputs: uniform softmax over 10 classes, loss = log 10
+    assert abs(float(o["loss"].item()) - float(np.log(10.0))) < 1e-5
