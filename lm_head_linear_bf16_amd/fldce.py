@@ -109,9 +109,11 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def _check(t: torch.Tensor, name: str, dtype=None) -> None:
+def _check(t: torch.Tensor, name: str, dtype=None, device=None) -> None:
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the inputs on {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
@@ -133,13 +135,14 @@ def _check_inputs(h, W, target, p_mask=None, bias=None, lse=None, w_name="W"):
         if t is not None and t.numel() != n:
             raise ValueError(f"{name} must hold {n} elements, got {t.numel()}")
     _check(h, "h")
-    _check(W, w_name, h.dtype)
-    _check(target, "target", torch.int64)
+    d = h.device
+    _check(W, w_name, h.dtype, d)
+    _check(target, "target", torch.int64, d)
     for name, t in (("p_mask", p_mask), ("lse", lse)):
         if t is not None:
-            _check(t, name, torch.float32)
+            _check(t, name, torch.float32, d)
     if bias is not None:
-        _check(bias, "bias", h.dtype)
+        _check(bias, "bias", h.dtype, d)
     return N, H, V
 
 def _out(out: Optional[dict], name: str, numel: int, like: torch.Tensor, dtype=None,
@@ -155,7 +158,7 @@ def _out(out: Optional[dict], name: str, numel: int, like: torch.Tensor, dtype=N
         return torch.empty(shape, dtype=dtype, device=like.device)
     if t.numel() != numel:
         raise ValueError(f"{name} must hold {numel} elements, got {t.numel()}")
-    _check(t, name, dtype)
+    _check(t, name, dtype, like.device)
     return t
 
 
@@ -165,6 +168,7 @@ def _stream(dev: torch.device) -> int:
 
 def _workspace(nbytes: int, dev, ws: Optional[torch.Tensor]) -> torch.Tensor:
     if ws is not None:
+        _check(ws, "workspace", None, dev)
         if ws.numel() * ws.element_size() < nbytes:
             raise ValueError(f"workspace too small: need {nbytes} bytes")
         return ws
@@ -236,10 +240,11 @@ def fldce_fwd_bwd(h: torch.Tensor, W: torch.Tensor, target: torch.Tensor,
         rl = _out(out, "row_loss", N, h, torch.float32, (N,))
     nbytes = lib().fldce_workspace_size(N, H, V, code, chunk_rows)
     ws = _workspace(nbytes, dev, workspace)
-    rc = lib().fldce_fwd_bwd(_ptr(h), _ptr(W), _ptr(target), _ptr(p_mask), N, H, V, code,
-                             ignore_index, label_smoothing, logit_scale,
-                             _reduction_code(reduction), total, _ptr(loss), _ptr(dH), _ptr(dW),
-                             _ptr(lse), _ptr(rl), chunk_rows, _ptr(ws), nbytes, _stream(dev))
+    with torch.cuda.device(dev):
+        rc = lib().fldce_fwd_bwd(_ptr(h), _ptr(W), _ptr(target), _ptr(p_mask), N, H, V, code,
+                                 ignore_index, label_smoothing, logit_scale,
+                                 _reduction_code(reduction), total, _ptr(loss), _ptr(dH), _ptr(dW),
+                                 _ptr(lse), _ptr(rl), chunk_rows, _ptr(ws), nbytes, _stream(dev))
     if rc != 0:
         raise FldceError(rc, "fldce_fwd_bwd")
     r = dict(loss=loss, dH=dH, dW=dW)
@@ -278,11 +283,12 @@ def fldce_fwd_bwd_ex(h: torch.Tensor, W: torch.Tensor, target: torch.Tensor,
         rl = _out(out, "row_loss", N, h, torch.float32, (N,))
     nbytes = lib().fldce_workspace_size(N, H, V, code, chunk_rows)
     ws = _workspace(nbytes, dev, workspace)
-    rc = lib().fldce_fwd_bwd_ex(_ptr(h), _ptr(W), _ptr(bias), _ptr(target), _ptr(p_mask), N, H, V,
-                                code, ignore_index, label_smoothing, logit_scale,
-                                _reduction_code(reduction), total, _eob_code(eob_token_id),
-                                eob_weight, _ptr(loss), _ptr(dH), _ptr(dW), _ptr(db), _ptr(lse),
-                                _ptr(rl), chunk_rows, _ptr(ws), nbytes, _stream(dev))
+    with torch.cuda.device(dev):
+        rc = lib().fldce_fwd_bwd_ex(_ptr(h), _ptr(W), _ptr(bias), _ptr(target), _ptr(p_mask), N, H, V,
+                                    code, ignore_index, label_smoothing, logit_scale,
+                                    _reduction_code(reduction), total, _eob_code(eob_token_id),
+                                    eob_weight, _ptr(loss), _ptr(dH), _ptr(dW), _ptr(db), _ptr(lse),
+                                    _ptr(rl), chunk_rows, _ptr(ws), nbytes, _stream(dev))
     if rc != 0:
         raise FldceError(rc, "fldce_fwd_bwd_ex")
     r = dict(loss=loss, dH=dH, dW=dW, db=db)
@@ -314,10 +320,11 @@ def fldce_fwd(h: torch.Tensor, W: torch.Tensor, target: torch.Tensor,
         rl = _out(out, "row_loss", N, h, torch.float32, (N,))
     nbytes = lib().fldce_fwd_workspace_size(N, H, V, code)
     ws = _workspace(nbytes, dev, workspace)
-    rc = lib().fldce_fwd(_ptr(h), _ptr(W), _ptr(bias), _ptr(target), _ptr(p_mask), N, H, V, code,
-                         ignore_index, label_smoothing, logit_scale, _reduction_code(reduction),
-                         total, _eob_code(eob_token_id), eob_weight, _ptr(loss), _ptr(lse),
-                         _ptr(rl), _ptr(ws), nbytes, _stream(dev))
+    with torch.cuda.device(dev):
+        rc = lib().fldce_fwd(_ptr(h), _ptr(W), _ptr(bias), _ptr(target), _ptr(p_mask), N, H, V, code,
+                             ignore_index, label_smoothing, logit_scale, _reduction_code(reduction),
+                             total, _eob_code(eob_token_id), eob_weight, _ptr(loss), _ptr(lse),
+                             _ptr(rl), _ptr(ws), nbytes, _stream(dev))
     if rc != 0:
         raise FldceError(rc, "fldce_fwd")
     r = dict(loss=loss)
@@ -339,10 +346,11 @@ def fldce_scale_grads(grad_out: torch.Tensor, dH: Optional[torch.Tensor] = None,
     dtype = ts[0].dtype
     for name, t in (("dH", dH), ("dW", dW), ("db", db)):
         if t is not None:
-            _check(t, name, dtype)
+            _check(t, name, dtype, grad_out.device)
     n = lambda t: 0 if t is None else t.numel()  # noqa: E731
-    rc = lib().fldce_scale_grads(_ptr(grad_out), _dtype_code(dtype), _ptr(dH), n(dH), _ptr(dW),
-                                 n(dW), _ptr(db), n(db), _stream(grad_out.device))
+    with torch.cuda.device(grad_out.device):
+        rc = lib().fldce_scale_grads(_ptr(grad_out), _dtype_code(dtype), _ptr(dH), n(dH), _ptr(dW),
+                                     n(dW), _ptr(db), n(db), _stream(grad_out.device))
     if rc != 0:
         raise FldceError(rc, "fldce_scale_grads")
 
@@ -362,9 +370,10 @@ def fldce_shard_partials(h: torch.Tensor, W_local: torch.Tensor, target: torch.T
     r = f("row_sumlogit") if sumlogit else None
     nbytes = lib().fldce_shard_partials_workspace_size(N, H, V_local, code)
     ws = _workspace(nbytes, dev, workspace)
-    rc = lib().fldce_shard_partials(_ptr(h), _ptr(W_local), _ptr(target), N, H, V_local,
-                                    vocab_start, code, ignore_index, logit_scale, _ptr(m),
-                                    _ptr(S), _ptr(t), _ptr(r), _ptr(ws), nbytes, _stream(dev))
+    with torch.cuda.device(dev):
+        rc = lib().fldce_shard_partials(_ptr(h), _ptr(W_local), _ptr(target), N, H, V_local,
+                                        vocab_start, code, ignore_index, logit_scale, _ptr(m),
+                                        _ptr(S), _ptr(t), _ptr(r), _ptr(ws), nbytes, _stream(dev))
     if rc != 0:
         raise FldceError(rc, "fldce_shard_partials")
     return dict(row_max=m, row_sumexp=S, target_logit=t, row_sumlogit=r)
@@ -385,10 +394,11 @@ def fldce_shard_bwd(h: torch.Tensor, W_local: torch.Tensor, target: torch.Tensor
     dWl = _out(out, "dW_local", V_local * H, W_local)
     nbytes = lib().fldce_shard_bwd_workspace_size(N, H, V_local, code, chunk_rows)
     ws = _workspace(nbytes, dev, workspace)
-    rc = lib().fldce_shard_bwd(_ptr(h), _ptr(W_local), _ptr(target), _ptr(p_mask), _ptr(lse), N,
-                               H, V_local, vocab_start, V_global, code, ignore_index,
-                               label_smoothing, logit_scale, _reduction_code(reduction), total,
-                               _ptr(dHp), _ptr(dWl), chunk_rows, _ptr(ws), nbytes, _stream(dev))
+    with torch.cuda.device(dev):
+        rc = lib().fldce_shard_bwd(_ptr(h), _ptr(W_local), _ptr(target), _ptr(p_mask), _ptr(lse), N,
+                                   H, V_local, vocab_start, V_global, code, ignore_index,
+                                   label_smoothing, logit_scale, _reduction_code(reduction), total,
+                                   _ptr(dHp), _ptr(dWl), chunk_rows, _ptr(ws), nbytes, _stream(dev))
     if rc != 0:
         raise FldceError(rc, "fldce_shard_bwd")
     return dict(dH_partial=dHp, dW_local=dWl)
