@@ -5,7 +5,8 @@
  * (HIP / PyTorch allocations) unless stated otherwise; the library never
  * allocates, frees or synchronises inside a call.  All work is enqueued on the
  * caller's HIP stream (`stream`, a hipStream_t passed as void*; NULL = the
- * null stream) and is asynchronous with respect to the host.
+ * null stream of the current device) and is asynchronous with respect to the
+ * host.  Every pointer of a call must be memory of that stream's device.
  *
  * What is computed (model page "fused_linear_diffusion_cross_entropy.py",
  * functions fused_linear_cross_entropy_forward, logsumexp_fwd and
