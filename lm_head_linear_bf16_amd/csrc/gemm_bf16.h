@@ -574,23 +574,53 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dw_bf16(
     }
     return;
   }
+  // Modes 1-3: the fp32 tile goes through LDS in two halves of 128 rows
+  // (128 KB each), so the accesses to acc32 (and out) are 16-byte pieces of
+  // whole 1-KB rows rather than 64-byte pieces from the accumulator layout.
+  // 16-byte chunk ch of half-tile row r sits at ch ^ sw(r): the 4-byte
+  // writes (16 lanes per row, 4 rows 4 apart) and the 16-byte reads are
+  // conflict-free.
+  float* stg = reinterpret_cast<float*>(smem);  // [128][256]
+  auto sw = [](int r) { return ((r >> 2) & 3) << 2; };
 #pragma unroll
-  for (int i = 0; i < kTM; ++i)
+  for (int half = 0; half < 2; ++half) {
+    __syncthreads();  // the operand stages, or the previous half, are no longer read
+    if (wm == half) {
 #pragma unroll
-    for (int j = 0; j < kTN; ++j) {
-      const int col = n0 + acc_col(wn, j, lane);
+      for (int i = 0; i < kTM; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = m0 + acc_row(wm, i, lane, r);
-        if (row < V && col < H) {
-          const int64_t e = (int64_t)row * H + col;
-          const float v = acc[i][j][r];
-          if (kMode == 1) acc32[e] = v;
-          else if (kMode == 2) acc32[e] += v;
-          else out[e] = (bf16)(acc32[e] + v);
+        for (int j = 0; j < kTN; ++j) {
+          const int cl = acc_col(wn, j, lane);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int rl = acc_row(0, i, lane, r);  // row within the half
+            stg[rl * kBN + ((((cl >> 2) ^ sw(rl)) << 2) | (cl & 3))] = acc[i][j][r];
+          }
+        }
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int p = 0; p < kBM / 2 * kBN / 4 / kGemmThreads; ++p) {
+      const int u = threadIdx.x + kGemmThreads * p;
+      const int rl = u / (kBN / 4), ch = u % (kBN / 4);
+      const int row = m0 + half * (kBM / 2) + rl, col = n0 + ch * 4;
+      if (row < V && col < H) {  // H % 64 == 0: a piece is wholly in or out
+        const floatx4 v = *(const floatx4*)&stg[rl * kBN + ((ch ^ sw(rl)) << 2)];
+        floatx4* a32 = (floatx4*)(acc32 + (int64_t)row * H + col);
+        if constexpr (kMode == 1) {
+          *a32 = v;
+        } else if constexpr (kMode == 2) {
+          *a32 = *a32 + v;
+        } else {
+          const floatx4 t = *a32 + v;
+          bf16x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = (bf16)t[e];
+          *(bf16x4*)(out + (int64_t)row * H + col) = o;
         }
       }
     }
+  }
 }
 
 }  // namespace fldce
