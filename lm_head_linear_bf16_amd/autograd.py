@@ -8,7 +8,8 @@ them; its backward multiplies them by the upstream gradient in place
 ``fused_linear_cross_entropy_backward`` does.
 ``FusedLinearDiffusionCrossEntropyLoss`` is the module: it flattens
 [B, L, H] inputs, defaults p_mask to ones and applies the end-of-block
-weight.  Marshalling only; every step runs in the HIP library.
+weight; without a gradient to compute (evaluation) it runs the forward
+alone.  Marshalling only; every step runs in the HIP library.
 """
 
 from __future__ import annotations
@@ -46,7 +47,16 @@ def fused_linear_cross_entropy_loss(x, target, weight, bias=None, p_mask=None,
                                     total: int = 0, eob_token_id: Optional[int] = None,
                                     eob_weight: float = 1.0):
     """x [N, H], target [N] int64, weight [V, H], bias [V] or None, p_mask [N]
-    float32 or None.  Returns the scalar loss."""
+    float32 or None.  Returns the scalar loss.  When no gradient is wanted
+    (grad mode off, or none of x, weight, bias requires one) only the
+    forward runs (fldce_fwd: a third of the flops, same loss bit for bit)."""
+    if not (torch.is_grad_enabled()
+            and any(t is not None and t.requires_grad for t in (x, weight, bias))):
+        r = fldce.fldce_fwd(x, weight, target, p_mask, bias, ignore_index=ignore_index,
+                            label_smoothing=label_smoothing, logit_scale=logit_scale,
+                            reduction=reduction, total=total, eob_token_id=eob_token_id,
+                            eob_weight=eob_weight)
+        return r["loss"].view(())
     return FusedLinearCrossEntropyFunction.apply(x, target, weight, bias, p_mask, ignore_index,
                                                  label_smoothing, logit_scale, reduction, total,
                                                  eob_token_id, eob_weight)

@@ -357,3 +357,27 @@ def test_binding_checks_caller_outputs():
         assert torch.isfinite(o[k].float()).all(), k
     # all-zero inputs: uniform softmax over 10 classes, loss = log 10
     assert abs(float(o["loss"].item()) - float(np.log(10.0))) < 1e-5
+
+
+def test_autograd_module_without_grad_runs_forward_only():
+    """Evaluation through the module (torch.no_grad, or inputs that need no
+    gradient) runs fldce_fwd: the loss is bitwise the one the training path
+    computes, and nothing is attached to the autograd graph."""
+    torch = torch_cuda()
+    from lm_head_linear_bf16_amd.autograd import FusedLinearDiffusionCrossEntropyLoss
+    dev = torch.device("cuda:0")
+    w = synth.custom("autograd_eval", 2, 100, 128, 1100, label_smoothing=0.1, logit_scale=0.5)
+    target, p_mask, _, _, _, hd, Wd, bd = _inputs(w, True, dev)
+    t = torch.from_numpy(target).to(dev)
+    pm = torch.from_numpy(p_mask).to(dev)
+    mod = FusedLinearDiffusionCrossEntropyLoss(label_smoothing=0.1, logit_scale=0.5)
+    say("case autograd module without grad")
+    x = hd.clone().requires_grad_(True)
+    train = mod(x, t, Wd, bd, pm)
+    with torch.no_grad():
+        ev1 = mod(x, t, Wd, bd, pm)
+    ev2 = mod(hd, t, Wd, bd, pm)            # nothing requires grad
+    torch.cuda.synchronize()
+    assert train.requires_grad and not ev1.requires_grad and not ev2.requires_grad
+    assert ev1.grad_fn is None and ev2.grad_fn is None
+    assert torch.equal(train.detach(), ev1) and torch.equal(ev1, ev2)
