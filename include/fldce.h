@@ -158,9 +158,14 @@ int fldce_fwd_bwd(const void* h, const void* W, const int64_t* target,
  *                    gradient multiplied by eob_weight (the page divides
  *                    their p_mask by the weight); < 0 = no such weighting
  *   eob_weight       finite and >= 0 (checked only when eob_token_id >= 0)
+ *   dH, dW           may be NULL here (not in fldce_fwd_bwd): that gradient
+ *                    is not computed and its GEMM is skipped (for instance
+ *                    a frozen LM-head weight); with dH, dW and db all NULL
+ *                    only the loss (and row statistics) is computed
  *
  * Every other argument is as in fldce_fwd_bwd, which equals this call with
- * bias = db = NULL and eob_token_id = -1.  Workspace: fldce_workspace_size.
+ * bias = db = NULL and eob_token_id = -1; whatever is computed is bit for
+ * bit what the full call computes.  Workspace: fldce_workspace_size.
  */
 int fldce_fwd_bwd_ex(const void* h, const void* W, const void* bias,
                      const int64_t* target, const float* p_mask, int64_t N,

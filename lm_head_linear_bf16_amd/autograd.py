@@ -2,8 +2,8 @@
 
 Same structure as page 1 ("fused_linear_diffusion_cross_entropy.py"):
 ``FusedLinearCrossEntropyFunction`` computes the loss and the gradients of
-x, weight and bias in its forward (one ``fldce_fwd_bwd_ex`` call) and keeps
-them; its backward multiplies them by the upstream gradient in place
+x, weight and bias in its forward (one ``fldce_fwd_bwd_ex`` call; only those
+an input requires, so a frozen weight skips the dW GEMM) and keeps them; its backward multiplies them by the upstream gradient in place
 (``fldce_scale_grads``, skipped on the device when it is 1), as the page's
 ``fused_linear_cross_entropy_backward`` does.
 ``FusedLinearDiffusionCrossEntropyLoss`` is the module: it flattens
@@ -26,10 +26,14 @@ class FusedLinearCrossEntropyFunction(torch.autograd.Function):
     def forward(ctx, x, target, weight, bias=None, p_mask=None, ignore_index=-100,
                 label_smoothing=0.0, logit_scale=1.0, reduction="mean", total=0,
                 eob_token_id=None, eob_weight=1.0):
+        # only the gradients some input needs (a frozen weight skips the dW GEMM)
         r = fldce.fldce_fwd_bwd_ex(x, weight, target, p_mask, bias, ignore_index=ignore_index,
                                    label_smoothing=label_smoothing, logit_scale=logit_scale,
                                    reduction=reduction, total=total, eob_token_id=eob_token_id,
-                                   eob_weight=eob_weight, want_db=bias is not None)
+                                   eob_weight=eob_weight,
+                                   want_db=bias is not None and ctx.needs_input_grad[3],
+                                   want_dH=ctx.needs_input_grad[0],
+                                   want_dW=ctx.needs_input_grad[2])
         ctx.save_for_backward(r["dH"], r["dW"], r["db"])
         return r["loss"].view(())
 
@@ -37,7 +41,8 @@ class FusedLinearCrossEntropyFunction(torch.autograd.Function):
     def backward(ctx, do):
         dH, dW, db = ctx.saved_tensors
         g = do.detach().to(torch.float32).reshape(1).contiguous()
-        fldce.fldce_scale_grads(g, dH, dW, db)
+        if dH is not None or dW is not None or db is not None:
+            fldce.fldce_scale_grads(g, dH, dW, db)
         return dH, None, dW, db, None, None, None, None, None, None, None, None
 
 

@@ -332,7 +332,8 @@ int run_core_bf16(const Core& c, const Plan& p, char* ws, hipStream_t st) {
   const bf16* bias = static_cast<const bf16*>(c.bias);
   const int64_t H = c.H, V = c.V, Vp = p.Vp;
   int64_t db_off = 0;  // row blocks of db partials written so far
-  {
+  const bool want_g = c.dH != nullptr || c.dW != nullptr || c.db != nullptr;
+  if (c.dH != nullptr) {
     StageTimer tm(kPrep, st);
     if (c.dH_f32)
       k_zero_ignored_rows<float><<<grid_strided(c.N, 1), 256, 0, st>>>(c.target, c.N, c.ignore,
@@ -348,16 +349,21 @@ int run_core_bf16(const Core& c, const Plan& p, char* ws, hipStream_t st) {
     {
       StageTimer tm(kHT, st);
       dim3 g((unsigned)(Cpc / 64), (unsigned)cdiv(H, 64));
-      k_transpose_gather_bf16<<<g, 256, 0, st>>>(h, c.rows, c.count, c0, cmax, H, hT, p.Cp, Cpc,
-                                                 hc);
+      // h^T only for dW
+      k_transpose_gather_bf16<<<g, 256, 0, st>>>(h, c.rows, c.count, c0, cmax, H,
+                                                 c.dW != nullptr ? hT : nullptr, p.Cp, Cpc, hc);
     }
     {  // 1. logits (+ softmax partials)
       StageTimer tm(kLogits, st);
       const int blocks = (int)(cdiv(V, kBM) * cdiv(cmax, kBN));
-      if (c.lse_in == nullptr)
+      if (c.lse_in == nullptr && want_g)
         k_logits_bf16<true, true><<<blocks, kGemmThreads, kGemmLds, st>>>(
             W, bias, hc, (int)V, (int)cmax, (int)H, c.s, nullptr, c.count, c0, part, c.rpart, p.C,
             zb, Vp, kGroupM);
+      else if (c.lse_in == nullptr)  // loss only: the logits are not stored
+        k_logits_bf16<false, true><<<blocks, kGemmThreads, kGemmLds, st>>>(
+            W, bias, hc, (int)V, (int)cmax, (int)H, c.s, nullptr, c.count, c0, part, c.rpart, p.C,
+            nullptr, Vp, kGroupM);
       else
         k_logits_bf16<true, false><<<blocks, kGemmThreads, kGemmLds, st>>>(
             W, bias, hc, (int)V, (int)cmax, (int)H, c.s, nullptr, c.count, c0, part, nullptr, p.C,
@@ -365,6 +371,7 @@ int run_core_bf16(const Core& c, const Plan& p, char* ws, hipStream_t st) {
     }
     // 2. per-row combine
     run_rows(c, p, part, coef, lsec, tcol, c0, cmax, st);
+    if (!want_g) continue;  // no gradient wanted: the loss needs nothing more
     {  // 3. dlogits: blocked z -> row-major g, zero rows up to the padded count
       StageTimer tm(kDlogits, st);
       if (c.db == nullptr) {
@@ -379,7 +386,7 @@ int run_core_bf16(const Core& c, const Plan& p, char* ws, hipStream_t st) {
         db_off += Cpc / 64;
       }
     }
-    {  // 4. dH = g W (split over the vocabulary, ordered reduction, scattered rows)
+    if (c.dH != nullptr) {  // 4. dH = g W (split over the vocabulary, ordered reduction, scattered rows)
       const int S = p.splits;
       const int blocks = (int)(cdiv(cmax, kBM) * cdiv(H, kBN) * S);
       {
@@ -399,7 +406,7 @@ int run_core_bf16(const Core& c, const Plan& p, char* ws, hipStream_t st) {
         k_splitk_scatter<bf16><<<(unsigned)std::min<int64_t>(cmax, 2048), 256, 0, st>>>(
             dHpart, S, Vp / kBK, cmax, H, c.rows, c.count, c0, (bf16*)c.dH);
     }
-    {  // 5. dW += g^T h
+    if (c.dW != nullptr) {  // 5. dW += g^T h
       StageTimer tm(kDWGemm, st);
       int mode = 0;
       if (p.nchunks > 1) mode = ic == 0 ? 1 : (ic + 1 == p.nchunks ? 3 : 2);
@@ -429,7 +436,8 @@ int run_core_f32(const Core& c, const Plan& p, char* ws, hipStream_t st) {
   const float* W = static_cast<const float*>(c.W);
   const int64_t H = c.H, V = c.V, Vp = p.Vp;
   int64_t db_off = 0;  // slabs of db partials written so far
-  {
+  const bool want_g = c.dH != nullptr || c.dW != nullptr || c.db != nullptr;
+  if (c.dH != nullptr) {  // W^T for dH
     StageTimer tm(kPrep, st);
     launch_transpose(W, V, H, H, WT, Vp, Vp, st);
   }
@@ -438,7 +446,7 @@ int run_core_f32(const Core& c, const Plan& p, char* ws, hipStream_t st) {
     const int64_t Cc = std::min(p.C, c.N - c0);
     const int64_t Cpc = round_up(Cc, 64);
     const float* hc = h + c0 * H;
-    {
+    if (c.dW != nullptr) {  // h^T for dW
       StageTimer tm(kHT, st);
       launch_transpose(hc, Cc, H, H, hT, p.Cp, Cpc, st);
     }
@@ -455,6 +463,7 @@ int run_core_f32(const Core& c, const Plan& p, char* ws, hipStream_t st) {
       }
     }
     const float* lse_c = run_rows(c, p, part, coef, nullptr, nullptr, c0, Cc, st);
+    if (!want_g) continue;  // no gradient wanted: the loss needs nothing more
     {
       StageTimer tm(kDlogits, st);
       dim3 g((unsigned)(Vp / 64), (unsigned)(Cpc / 64));
@@ -466,12 +475,12 @@ int run_core_f32(const Core& c, const Plan& p, char* ws, hipStream_t st) {
         db_off += cdiv(Cc, kColSlab);
       }
     }
-    {
+    if (c.dH != nullptr) {
       StageTimer tm(kDHGemm, st);
       dim3 g((unsigned)cdiv(H, 64), (unsigned)cdiv(Cc, 64));
       k_gemm_f32_nt<<<g, 256, 0, st>>>(zb, Vp, Cc, WT, Vp, H, V, 1.f, (float*)c.dH + c0 * H, H, 0);
     }
-    {
+    if (c.dW != nullptr) {
       StageTimer tm(kDWGemm, st);
       dim3 g((unsigned)cdiv(H, 64), (unsigned)cdiv(V, 64));
       k_gemm_f32_nt<<<g, 256, 0, st>>>(gT, p.Cp, V, hT, p.Cp, H, Cpc, 1.f, (float*)c.dW, H,
@@ -579,6 +588,7 @@ int fldce_fwd_bwd(const void* h, const void* W, const int64_t* target, const flo
                   float label_smoothing, float logit_scale, int reduction, int64_t total,
                   float* loss, void* dH, void* dW, float* row_lse, float* row_loss,
                   int64_t chunk_rows, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dW || (N > 0 && !dH)) return FLDCE_ERR_NULL_POINTER;  // both gradients are outputs here
   return fldce_fwd_bwd_ex(h, W, nullptr, target, p_mask, N, H, V, dtype, ignore_index,
                           label_smoothing, logit_scale, reduction, total, -1, 1.f, loss, dH, dW,
                           nullptr, row_lse, row_loss, chunk_rows, workspace, workspace_bytes,
@@ -593,7 +603,7 @@ int fldce_fwd_bwd_ex(const void* h, const void* W, const void* bias, const int64
                      int64_t chunk_rows, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_common(h, W, target, N, H, V, dtype, logit_scale);
   if (rc != FLDCE_OK) return rc;
-  if (!loss || !dW || (N > 0 && !dH)) return FLDCE_ERR_NULL_POINTER;
+  if (!loss) return FLDCE_ERR_NULL_POINTER;  // dH, dW, db: NULL = not wanted
   rc = check_loss_args(reduction, label_smoothing, eob_token_id, eob_weight);
   if (rc != FLDCE_OK) return rc;
   if (chunk_rows < 0) return FLDCE_ERR_BAD_ARGUMENT;
@@ -611,7 +621,7 @@ int fldce_fwd_bwd_ex(const void* h, const void* W, const void* bias, const int64
   const int esz = dtype == FLDCE_DTYPE_BF16 ? 2 : 4;
   if (N == 0) {
     zero_fill(loss, 1, 4, st);
-    zero_fill(dW, V * H, esz, st);
+    if (dW != nullptr) zero_fill(dW, V * H, esz, st);
     if (db != nullptr) zero_fill(db, V, esz, st);
     return launch_status();
   }

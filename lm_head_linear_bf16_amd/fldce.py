@@ -264,18 +264,20 @@ def fldce_fwd_bwd_ex(h: torch.Tensor, W: torch.Tensor, target: torch.Tensor,
                      eob_token_id: Optional[int] = None, eob_weight: float = 1.0,
                      want_db: Optional[bool] = None, chunk_rows: int = 0,
                      row_stats: bool = False, workspace: Optional[torch.Tensor] = None,
-                     out: Optional[dict] = None) -> dict:
+                     out: Optional[dict] = None, want_dH: bool = True,
+                     want_dW: bool = True) -> dict:
     """fldce_fwd_bwd plus page 1's optional bias [V] (and its gradient db,
     returned when ``want_db`` or, by default, when a bias is given) and the
-    end-of-block weight (rows whose target is ``eob_token_id``).  Outputs
-    may be passed in ``out`` (loss, dH, dW, db, row_lse, row_loss)."""
+    end-of-block weight (rows whose target is ``eob_token_id``).  With
+    ``want_dH`` / ``want_dW`` False that gradient is not computed (None).
+    Outputs may be passed in ``out`` (loss, dH, dW, db, row_lse, row_loss)."""
     N, H, V = _check_inputs(h, W, target, p_mask, bias)
     dev = h.device
     code = _dtype_code(h.dtype)
     want_db = (bias is not None) if want_db is None else want_db
     loss = _out(out, "loss", 1, h, torch.float32, (1,))
-    dH = _out(out, "dH", N * H, h)
-    dW = _out(out, "dW", V * H, W)
+    dH = _out(out, "dH", N * H, h) if want_dH else None
+    dW = _out(out, "dW", V * H, W) if want_dW else None
     db = _out(out, "db", V, h, h.dtype, (V,)) if want_db else None
     lse = rl = None
     if row_stats:

@@ -81,6 +81,8 @@ def test_fwd_bwd_argument_checks(L):
     assert _fwd(L, W=None) == -1
     assert _fwd(L, h=None) == -1
     assert _fwd(L, loss=None) == -1
+    assert _fwd(L, dH=None) == -1            # both gradients are required outputs here
+    assert _fwd(L, dW=None) == -1
     assert _fwd(L, dtype=3) == -3
     assert _fwd(L, N=-1) == -2
     assert _fwd(L, V=0) == -2
@@ -162,7 +164,10 @@ def test_extended_argument_checks(L, f):
     assert f(L, wsb=8) == -5
     if f is _ex:
         assert f(L, db=BAD) == -6
-        assert f(L, dH=None) == -1
+        assert f(L, dH=None, wsb=8) == -5         # dH / dW optional here: fails on the workspace
+        assert f(L, dW=None, wsb=8) == -5
+        assert f(L, dH=None, dW=None, wsb=8) == -5
+        assert f(L, dW=BAD) == -6
         assert f(L, chunk=-1) == -4
 
 

@@ -381,3 +381,62 @@ def test_autograd_module_without_grad_runs_forward_only():
     assert train.requires_grad and not ev1.requires_grad and not ev2.requires_grad
     assert ev1.grad_fn is None and ev2.grad_fn is None
     assert torch.equal(train.detach(), ev1) and torch.equal(ev1, ev2)
+
+
+PARTIAL_CASES = [
+    ("single_bf16", synth.custom("partial_bf16", 3, 150, 128, 2053, label_smoothing=0.1,
+                                 logit_scale=0.5), 0),
+    ("chunked_bf16", synth.custom("partial_chunked_bf16", 3, 150, 128, 2053,
+                                  label_smoothing=0.1, logit_scale=0.5), 128),
+    ("f32", synth.custom("partial_f32", 2, 64, 72, 777, dtype="f32", label_smoothing=0.1), 0),
+]
+
+
+@pytest.mark.parametrize("case", PARTIAL_CASES, ids=lambda c: c[0])
+def test_fwd_bwd_ex_some_gradients(case):
+    """dH, dW and db are each optional in fldce_fwd_bwd_ex: whatever is
+    computed equals the full call bit for bit (loss and row statistics too),
+    the rest is not touched; with none, only the loss."""
+    torch = torch_cuda()
+    from lm_head_linear_bf16_amd import fldce
+    name, w, chunk = case
+    dev = torch.device("cuda:0")
+    target, p_mask, _, _, _, hd, Wd, bd = _inputs(w, True, dev)
+    t, p = torch.from_numpy(target).to(dev), torch.from_numpy(p_mask).to(dev)
+    kw = dict(label_smoothing=w.label_smoothing, logit_scale=w.logit_scale, reduction=w.reduction,
+              total=w.total, eob_token_id=5, eob_weight=2.0, chunk_rows=chunk, row_stats=True)
+    say(f"case partial gradients {name}")
+    full = fldce.fldce_fwd_bwd_ex(hd, Wd, t, p, bd, want_db=True, **kw)
+    for want in [(True, False, False), (False, True, False), (False, False, True),
+                 (True, False, True), (False, False, False)]:
+        r = fldce.fldce_fwd_bwd_ex(hd, Wd, t, p, bd, want_dH=want[0], want_dW=want[1],
+                                   want_db=want[2], **kw)
+        torch.cuda.synchronize()
+        for key in ("loss", "row_lse", "row_loss"):
+            assert torch.equal(r[key], full[key]), (want, key)
+        for key, on in zip(("dH", "dW", "db"), want):
+            if on:
+                assert torch.equal(r[key], full[key]), (want, key)
+            else:
+                assert r[key] is None, (want, key)
+
+
+def test_autograd_frozen_weight():
+    """A weight that needs no gradient: only dH (and db) are computed, equal
+    to the full backward's bit for bit; weight.grad stays None."""
+    torch = torch_cuda()
+    from lm_head_linear_bf16_amd.autograd import FusedLinearDiffusionCrossEntropyLoss
+    dev = torch.device("cuda:0")
+    w = synth.custom("autograd_frozen", 2, 120, 128, 1100, label_smoothing=0.1, logit_scale=0.5)
+    target, p_mask, _, _, _, hd, Wd, bd = _inputs(w, True, dev)
+    t, pm = torch.from_numpy(target).to(dev), torch.from_numpy(p_mask).to(dev)
+    mod = FusedLinearDiffusionCrossEntropyLoss(label_smoothing=0.1, logit_scale=0.5)
+    say("case autograd frozen weight")
+    xa, Wa, ba = (hd.clone().requires_grad_(True), Wd.clone().requires_grad_(True),
+                  bd.clone().requires_grad_(True))
+    (1.5 * mod(xa, t, Wa, ba, pm)).backward()
+    xb, Wb, bb = hd.clone().requires_grad_(True), Wd.clone(), bd.clone().requires_grad_(True)
+    (1.5 * mod(xb, t, Wb, bb, pm)).backward()
+    torch.cuda.synchronize()
+    assert Wb.grad is None
+    assert torch.equal(xa.grad, xb.grad) and torch.equal(ba.grad, bb.grad)
