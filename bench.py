@@ -209,8 +209,9 @@ def _timed(fn, steps: int, warmup: int):
 
 def extra_legs(args, w, h, W, tgt, pm, dt, rows_mult: int, ms_plain: float, peak: float) -> dict:
     """The rest of page 1's interface on the same inputs: forward only
-    (fldce_fwd: 2 * rows * H * V flops) and, with --bias-leg, fwd+bwd with
-    the seeded bias and its gradient db (fldce_fwd_bwd_ex)."""
+    (fldce_fwd: 2 * rows * H * V flops), with --frozen-leg fwd+bwd without
+    dW, and with --bias-leg fwd+bwd with the seeded bias and its gradient db
+    (fldce_fwd_bwd_ex)."""
     import numpy as np
     import torch
     from lm_head_linear_bf16_amd import fldce, synth
@@ -228,6 +229,17 @@ def extra_legs(args, w, h, W, tgt, pm, dt, rows_mult: int, ms_plain: float, peak
                            "tflops": round(tf, 2), "pct_peak": round(100.0 * tf / peak, 2),
                            "stage_ms_per_step": st}
     del ws
+    if args.frozen_leg:
+        # a frozen LM-head weight: dH only (fldce_fwd_bwd_ex without dW), 4 * rows * H * V
+        ws = torch.empty(fldce.fldce_workspace_size(N, H, V, dt), dtype=torch.uint8, device=dev)
+        log(f"fwd+bwd without dW: {steps} steps")
+        m, st = _timed(lambda: fldce.fldce_fwd_bwd_ex(h, W, tgt, pm, want_dW=False, workspace=ws,
+                                                      **kw), steps, warm)
+        tf = 4.0 * rows_mult * H * V / (m * 1e-3) / 1e12
+        out["frozen_weight"] = {"ms_per_step": round(m, 4),
+                                "tokens_per_s": round(N / (m * 1e-3), 1), "tflops": round(tf, 2),
+                                "pct_peak": round(100.0 * tf / peak, 2), "stage_ms_per_step": st}
+        del ws
     if not args.bias_leg:
         return out
     bt = synth.bias(w)
@@ -351,6 +363,8 @@ def main() -> int:
     ap.add_argument("--calib-mib", type=int, default=1024, help="size of that calibration copy")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the forward-only leg (and the bias + db leg)")
+    ap.add_argument("--frozen-leg", action="store_true",
+                    help="also time fwd+bwd without dW (a frozen weight: fldce_fwd_bwd_ex)")
     ap.add_argument("--bias-leg", action="store_true",
                     help="also time fwd+bwd with the seeded bias and db (fldce_fwd_bwd_ex); off by "
                          "default so that the plain step is the only user of its logits kernel")
