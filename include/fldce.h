@@ -87,10 +87,12 @@ int fldce_version(void);
 /* Static, human-readable text for a status code. */
 const char* fldce_status_string(int status);
 
-/* Token rows processed per chunk when chunk_rows == 0 is passed: all N rows
- * while the chunk's logits buffers stay within a fixed budget, else the
- * largest multiple of 256 that fits.  Page 1 chunks rows to bound the [C, V]
- * logits buffer; 288 GB of HBM lets one chunk cover every workload here. */
+/* Token rows processed per chunk when chunk_rows == 0 is passed with bf16
+ * inputs: all N rows while the chunk's two [C, V] buffers (logits and their
+ * gradient, 2 bytes each) stay within 16 GiB, else the largest multiple of
+ * 256 that fits (fp32 inputs keep 4-byte buffers, so half as many rows when
+ * that bound binds).  Page 1 chunks rows to bound the [C, V] logits buffer;
+ * 288 GB of HBM lets one chunk cover every workload here.  H is unused. */
 int64_t fldce_default_chunk_rows(int64_t N, int64_t H, int64_t V);
 
 /* Bytes of device workspace fldce_fwd_bwd needs for these sizes (chunk_rows 0
