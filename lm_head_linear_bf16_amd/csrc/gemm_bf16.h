@@ -510,11 +510,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dh_bf16(
 }
 
 // ---------------------------------------------------------------------------
-// dW = g^T h over K = the chunk's tokens.  A = g [Kp token rows, ldg] read as
-// K rows (vocabulary columns, transposed in LDS); B = h^T [H, ldh] with the
-// chunk's tokens contiguous (a 2 * H * Kp byte copy made per chunk: reading
-// both operands transposed measured ~8% slower than one).  g rows and h^T
-// columns C..Kp-1 are zero.
+// dW = g^T h over K = the chunk's tokens, computed as its transpose
+// dW^T = h^T g: A = h^T [H, ldh] with the chunk's tokens contiguous (a
+// 2 * H * Kp byte copy made per chunk), B = g [Kp token rows, ldg] read as
+// K rows (vocabulary columns, transposed in LDS).  In this order the
+// transposed operand is the one with 4 fragments per wave rather than 8 (16
+// LDS reads per 32-wide K step instead of 20: main loop 2.62 against
+// 2.72 ms at the 4B-scale shape).  Tiles are still numbered over (vocabulary
+// tile, H tile), so the order, and what the L2 shares, are unchanged; the
+// accumulators hold the tile transposed (rows = H, columns = vocabulary),
+// and the epilogue transposes it back through LDS.  g rows and h^T columns
+// C..Kp-1 are zero.
 // kMode 0: out (bf16) = acc                      (single chunk)
 // kMode 1: acc32 = acc                           (first of several chunks)
 // kMode 2: acc32 += acc                          (middle chunk)
@@ -530,72 +536,66 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dw_bf16(
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const TileCoord tc = tile_coord((int)cdiv(V, kBM), (int)cdiv(H, kBN), 1, group_m);
   if (!tc.active) return;
-  const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
+  const int v0 = tc.tm * kBM, h0 = tc.tn * kBN;  // vocabulary rows and H columns of dW
   int Ce = cmax;
   if (count != nullptr) {
     const int64_t n = (int64_t)*count - c0;
     Ce = n < 0 ? 0 : (n < cmax ? (int)n : cmax);
   }
   const int Kp = (int)round_up(Ce, kBK);
-  Acc acc;
-  gemm_mainloop<true, false>(g, ldg, max(Kp, 1), (int)ldg, m0, hT, ldh, H, 0, n0, 0, Kp / kBK, smem,
+  Acc acc;  // acc[i][j][r] = dW[v0 + acc_col(wn, j)][h0 + acc_row(wm, i, r)]
+  gemm_mainloop<false, true>(hT, ldh, H, 0, h0, g, ldg, max(Kp, 1), (int)ldg, v0, 0, Kp / kBK, smem,
                              acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN;
   if constexpr (kMode == 0) {
-    // Stage the bf16 tile in LDS (free after the main loop) and write it out
-    // as 512-byte rows: the accumulator layout alone only gives 32-byte row
-    // pieces per store.  16-byte chunk ch of tile row r sits at ch ^ sw(r),
-    // which keeps both the 2-byte writes and the 16-byte reads conflict-free.
+    // Stage the bf16 tile in LDS as [vocabulary][H] (free after the main
+    // loop) and write it out as 512-byte rows.  A lane holds 4 consecutive H
+    // of one vocabulary row per sub-tile: one 8-byte write.  16-byte chunk
+    // ch of staged row r sits at ch ^ (r & 15), so the 16 rows one write
+    // instruction touches fall on distinct banks and the 16-byte row reads
+    // stay conflict-free.
     bf16* stg = reinterpret_cast<bf16*>(smem);  // [256][256]
-    auto sw = [](int r) { return ((r >> 2) & 3) << 1; };
     __syncthreads();  // every wave is done reading the operand stages
 #pragma unroll
     for (int i = 0; i < kTM; ++i)
 #pragma unroll
       for (int j = 0; j < kTN; ++j) {
-        const int cl = acc_col(wn, j, lane);
+        const int vl = acc_col(wn, j, lane), hl = acc_row(wm, i, lane, 0);
+        bf16x4 w;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int rl = acc_row(wm, i, lane, r);
-          stg[rl * kBN + (((cl >> 3) ^ sw(rl)) << 3) + (cl & 7)] = (bf16)acc[i][j][r];
-        }
+        for (int r = 0; r < 4; ++r) w[r] = (bf16)acc[i][j][r];
+        *(bf16x4*)&stg[vl * kBN + ((((hl >> 3) ^ (vl & 15)) << 3) | (hl & 7))] = w;
       }
     __syncthreads();
 #pragma unroll
     for (int p = 0; p < kBM * kBN / 8 / kGemmThreads; ++p) {
       const int u = threadIdx.x + kGemmThreads * p;
       const int rl = u / (kBN / 8), ch = u % (kBN / 8);
-      const int row = m0 + rl, col = n0 + ch * 8;
+      const int row = v0 + rl, col = h0 + ch * 8;
       if (row < V && col < H)  // H % 64 == 0: a chunk is wholly in or out
-        __builtin_nontemporal_store(*(const bf16x8*)&stg[rl * kBN + ((ch ^ sw(rl)) << 3)],
+        __builtin_nontemporal_store(*(const bf16x8*)&stg[rl * kBN + ((ch ^ (rl & 15)) << 3)],
                                     (bf16x8*)(out + (int64_t)row * H + col));
     }
     return;
   }
-  // Modes 1-3: the fp32 tile goes through LDS in two halves of 128 rows
-  // (128 KB each), so the accesses to acc32 (and out) are 16-byte pieces of
-  // whole 1-KB rows rather than 64-byte pieces from the accumulator layout.
-  // 16-byte chunk ch of half-tile row r sits at ch ^ sw(r): the 4-byte
-  // writes (16 lanes per row, 4 rows 4 apart) and the 16-byte reads are
-  // conflict-free.
+  // Modes 1-3: the fp32 tile goes through LDS in two halves of 128
+  // vocabulary rows (128 KB each; the waves with wn = 2 * half, 2 * half + 1
+  // hold them), so the accesses to acc32 (and out) are 16-byte pieces of
+  // whole 1-KB rows.  A lane writes 4 consecutive H (16 bytes) of one row;
+  // 16-byte chunk ch of staged row r sits at ch ^ (r & 15).
   float* stg = reinterpret_cast<float*>(smem);  // [128][256]
-  auto sw = [](int r) { return ((r >> 2) & 3) << 2; };
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     __syncthreads();  // the operand stages, or the previous half, are no longer read
-    if (wm == half) {
+    if ((wn >> 1) == half) {
 #pragma unroll
       for (int i = 0; i < kTM; ++i)
 #pragma unroll
         for (int j = 0; j < kTN; ++j) {
-          const int cl = acc_col(wn, j, lane);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int rl = acc_row(0, i, lane, r);  // row within the half
-            stg[rl * kBN + ((((cl >> 2) ^ sw(rl)) << 2) | (cl & 3))] = acc[i][j][r];
-          }
+          const int vl = acc_col(wn, j, lane) - half * (kBM / 2), hl = acc_row(wm, i, lane, 0);
+          *(floatx4*)&stg[vl * kBN + (((hl >> 2) ^ (vl & 15)) << 2)] = acc[i][j];
         }
     }
     __syncthreads();
@@ -603,9 +603,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dw_bf16(
     for (int p = 0; p < kBM / 2 * kBN / 4 / kGemmThreads; ++p) {
       const int u = threadIdx.x + kGemmThreads * p;
       const int rl = u / (kBN / 4), ch = u % (kBN / 4);
-      const int row = m0 + half * (kBM / 2) + rl, col = n0 + ch * 4;
+      const int row = v0 + half * (kBM / 2) + rl, col = h0 + ch * 4;
       if (row < V && col < H) {  // H % 64 == 0: a piece is wholly in or out
-        const floatx4 v = *(const floatx4*)&stg[rl * kBN + ((ch ^ sw(rl)) << 2)];
+        const floatx4 v = *(const floatx4*)&stg[rl * kBN + ((ch ^ (rl & 15)) << 2)];
         floatx4* a32 = (floatx4*)(acc32 + (int64_t)row * H + col);
         if constexpr (kMode == 1) {
           *a32 = v;
