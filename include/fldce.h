@@ -238,8 +238,13 @@ size_t fldce_shard_partials_workspace_size(int64_t N, int64_t H,
  * Combining over shards: M = max_k m_k, lse = M + log sum_k S_k e^{m_k - M},
  * z_target = sum_k target_logit_k, sum_j z_ij = sum_k row_sumlogit_k.
  *
- * Rows whose target is ignore_index are skipped (they need no softmax): for
- * them row_max = -INFINITY and row_sumexp = target_logit = row_sumlogit = 0.
+ * Rows whose target is ignore_index are skipped (a training step needs no
+ * softmax for them): for them row_max = -INFINITY and row_sumexp =
+ * target_logit = row_sumlogit = 0, the identity of the combine.  A caller
+ * that needs every row's partials (evaluation: every row's lse) passes an
+ * ignore_index that no target equals (e.g. INT64_MIN): then every row is
+ * computed, and a row whose target lies outside [0, V) of every shard (such
+ * as -100) simply has target_logit = 0 in each shard.
  */
 int fldce_shard_partials(const void* h, const void* W_local,
                          const int64_t* target, int64_t N, int64_t H,

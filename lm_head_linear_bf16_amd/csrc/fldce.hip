@@ -37,6 +37,12 @@ namespace {
 enum Mode { kFwdBwd = 0, kShardPartials = 1, kShardBwd = 2, kFwd = 3 };
 
 constexpr int64_t kZBudgetBytes = int64_t(16) << 30;  // chunk logits + g^T buffers
+// Label smoothing above which the backward operand is g itself, formed from
+// stored logits in one pass, rather than the exponentials E with the
+// smoothing share added to the products: that share, eps / V of every entry,
+// is more than half of a flat softmax past this point, and subtracting it
+// after E is rounded would amplify E's rounding error by 1 / (1 - eps).
+constexpr float kFusedSmoothingMax = 0.5f;
 // Tile rows per group in the XCD-aware block order (measured best per GEMM at
 // the 4B-scale shapes: 4 for logits, 2 for the two backward products).
 constexpr int kGroupM = 4;
@@ -47,10 +53,11 @@ struct Plan {
   int64_t esz = 0;
   int splits = 1;
   size_t oD = 0, oWT = 0, oColpart = 0, oWsum = 0, oZt = 0, oR = 0, oLse = 0, oRloss = 0,
-         oCoef = 0, oPart = 0, oRpart = 0, oZ = 0, oG = 0, oGT = 0, oHT = 0, oDHpart = 0,
-         oDW32 = 0, oRows = 0, oCount = 0, oLsec = 0, oTcol = 0, oBsum = 0, oDbpart = 0,
-         oHC = 0;
+         oCoef = 0, oAlpha = 0, oPart = 0, oRpart = 0, oZ = 0, oGT = 0, oHT = 0, oDHpart = 0,
+         oDW32 = 0, oRows = 0, oCount = 0, oTcol = 0, oBsum = 0, oDbpart = 0, oHC = 0,
+         oFlag = 0, oFlist = 0, oUpart = 0, oU = 0;
   int64_t db_blocks = 0;  // row blocks of db partials (64 rows each, over all chunks)
+  int64_t u_blocks = 0;   // row blocks of smoothing-term partials (64 rows each, over all chunks)
   size_t total = 0;
 };
 
@@ -62,10 +69,17 @@ size_t take(size_t& cur, size_t bytes) {
 
 int64_t default_chunk(int64_t N, int64_t V, int64_t esz) {
   const int64_t Vp = round_up(V, 64);
-  const int64_t per_row = 2 * esz * Vp;  // bf16: z and g; fp32: z/g and g^T
+  const int64_t per_row = 2 * esz * Vp;  // bf16: E and room for g-sized data; fp32: z/g and g^T
   if (round_up(std::max<int64_t>(N, 1), 64) * per_row <= kZBudgetBytes) return std::max<int64_t>(N, 1);
   int64_t c = (kZBudgetBytes / per_row) / 256 * 256;
   return std::max<int64_t>(c, 256);
+}
+
+// Row blocks of 64 over every chunk of a plan (db and smoothing-term partials).
+int64_t row_blocks(int64_t N, int64_t C) {
+  int64_t nb = 0;
+  for (int64_t c0 = 0; c0 < N; c0 += C) nb += cdiv(std::min(C, N - c0), 64);
+  return std::max<int64_t>(nb, 1);
 }
 
 Plan make_plan(int mode, int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_rows) {
@@ -83,16 +97,21 @@ Plan make_plan(int mode, int64_t N, int64_t H, int64_t V, int dtype, int64_t chu
     p.C = chunk_rows > 0 ? std::min<int64_t>(chunk_rows, std::max<int64_t>(N, 1))
                          : default_chunk(N, V, p.esz);
   }
-  p.Cp = round_up(p.C, 64);
+  // bf16: one row more than the chunk for the all-ones row of the smoothing term
+  p.Cp = round_up(p.C + (bf ? 1 : 0), 64);
   p.nchunks = N > 0 ? cdiv(N, p.C) : 0;
   size_t cur = 0;
   p.oD = take(cur, 256);
   p.oCount = take(cur, 256);
+  p.oFlag = take(cur, (size_t)std::max<int64_t>(p.nchunks, 1) * 4);  // flagged rows per chunk
   p.oRows = take(cur, (size_t)std::max<int64_t>(N, 1) * 4);  // compacted row indices
   p.oColpart = take(cur, (size_t)cdiv(V, kColSlab) * H * 4);
   p.oWsum = take(cur, (size_t)H * 4);
   p.oBsum = take(cur, 256);
-  if (bf) p.oHC = take(cur, (size_t)p.Cp * H * 2);  // gathered rows of h, the logits B operand
+  if (bf) {
+    p.oHC = take(cur, (size_t)p.Cp * H * 2);  // gathered rows of h, the logits B operand
+    p.oFlist = take(cur, (size_t)p.C * 4);    // flagged chunk rows
+  }
   p.oPart = take(cur, (size_t)p.nT * p.C * 8);
   p.oRpart = take(cur, (size_t)p.nT * p.C * 4);  // per-slab row sums of z (label smoothing)
   if (mode == kShardPartials) {
@@ -115,34 +134,37 @@ Plan make_plan(int mode, int64_t N, int64_t H, int64_t V, int dtype, int64_t chu
   p.oLse = take(cur, (size_t)N * 4);
   p.oRloss = take(cur, (size_t)N * 4);
   p.oCoef = take(cur, (size_t)p.C * 4);
-  p.oLsec = take(cur, (size_t)p.C * 4);
+  p.oAlpha = take(cur, (size_t)p.C * 4);
   p.oTcol = take(cur, (size_t)p.C * 4);
-  p.oZ = take(cur, (size_t)p.Cp * p.Vp * p.esz);
-  if (bf) {
-    p.oG = take(cur, (size_t)p.Cp * p.Vp * p.esz);  // g row-major (z is blocked)
-  } else {
-    p.oGT = take(cur, (size_t)p.Vp * p.Cp * p.esz);
-  }
+  p.oZ = take(cur, (size_t)p.Cp * p.Vp * p.esz);  // bf16: E; fp32: z, then g in place
+  if (!bf) p.oGT = take(cur, (size_t)p.Vp * p.Cp * p.esz);
   p.oHT = take(cur, (size_t)H * p.Cp * p.esz);
   if (mode == kFwdBwd) {  // db partials: bf16 per 64 rows of a chunk, fp32 per kColSlab rows
     p.db_blocks = cdiv(std::max<int64_t>(N, 1), 64) + p.nchunks;
     p.oDbpart = take(cur, (size_t)p.db_blocks * p.Vp * 4);
   }
   if (bf) {
+    // smoothing-term partials sum_t coef_t h_t (and sum_t coef_t) per 64 rows
+    p.u_blocks = row_blocks(N, p.C);
+    p.oUpart = take(cur, (size_t)p.u_blocks * (H + 1) * 4);
+    p.oU = take(cur, (size_t)(H + 1) * 4);
     // the device picks the split count S for the rows that exist (fewer than
-    // C when rows are ignored) and stores S x rows x H partials; reserve the
-    // largest such product over every possible number of row tiles
+    // C when rows are ignored, plus the all-ones row when eps > 0) and stores
+    // S x rows x H partials; reserve the largest such product over every
+    // possible number of row tiles
     p.splits = 1;
     size_t part_elems = 0;
     // (choose_splits is 1 from 256 tiles on, so the loop stops there)
-    const int64_t tm_max = std::min(cdiv(p.C, kBM), cdiv(256, cdiv(H, kBN)));
+    const int64_t tm_max = std::min(cdiv(p.C + 1, kBM), cdiv(256, cdiv(H, kBN)) + 1);
     for (int64_t tm = 1; tm <= tm_max; ++tm) {
       const int S = choose_splits(tm * cdiv(H, kBN), p.Vp / kBK, 8);
       p.splits = std::max(p.splits, S);
-      if (S > 1) part_elems = std::max(part_elems, (size_t)S * std::min(tm * kBM, p.C) * H);
+      part_elems = std::max(part_elems, (size_t)S * std::min(tm * kBM, p.C + 1) * H);
     }
     p.oDHpart = take(cur, std::max<size_t>(part_elems, 1) * 4);
-    if (p.nchunks > 1) p.oDW32 = take(cur, (size_t)V * H * 4);
+    // fp32 dW carried across chunks, whole 256 x 256 tiles in the accumulators' layout
+    if (p.nchunks > 1)
+      p.oDW32 = take(cur, (size_t)cdiv(V, kBM) * cdiv(H, kBN) * kBM * kBN * 4);
   }
   p.total = cur;
   return p;
@@ -155,37 +177,45 @@ bool grids_fit(const Plan& p, int dtype) {
   if (dtype != FLDCE_DTYPE_BF16) return true;
   const int64_t lim = (int64_t(1) << 32) / kGemmThreads;
   const int64_t tv = cdiv(p.V, kBM), tc = cdiv(std::max<int64_t>(p.C, 1), kBN), th = cdiv(p.H, kBN);
-  return tv * tc < lim && tv * th < lim && tc * th * std::max(p.splits, 1) < lim;
+  const int64_t tdh = cdiv(p.C + 1, kBM);  // dH: the chunk's rows and the all-ones row
+  return tv * tc < lim && tv * th < lim && tdh * th * std::max(p.splits, 1) < lim;
+}
+
+template <typename K>
+void allow_gemm_lds(K kernel) {
+  (void)hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            kGemmLds);
 }
 
 void set_gemm_attributes() {
   static std::once_flag once;
   std::call_once(once, [] {
-    (void)hipFuncSetAttribute((const void*)k_logits_bf16<true, true>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
-    (void)hipFuncSetAttribute((const void*)k_logits_bf16<true, false>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
-    (void)hipFuncSetAttribute((const void*)k_logits_bf16<false, true>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
-    (void)hipFuncSetAttribute((const void*)k_gemm_dh_bf16,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
-    (void)hipFuncSetAttribute((const void*)k_gemm_dw_bf16<0>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
-    (void)hipFuncSetAttribute((const void*)k_gemm_dw_bf16<1>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
-    (void)hipFuncSetAttribute((const void*)k_gemm_dw_bf16<2>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
-    (void)hipFuncSetAttribute((const void*)k_gemm_dw_bf16<3>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
+    allow_gemm_lds(k_logits_bf16<kEpiMax, kStoreNone, false>);
+    allow_gemm_lds(k_logits_bf16<kEpiMax, kStoreNone, true>);
+    allow_gemm_lds(k_logits_bf16<kEpiRef, kStoreExp, false>);
+    allow_gemm_lds(k_logits_bf16<kEpiRef, kStoreNone, false>);
+    allow_gemm_lds(k_logits_bf16<kEpiRef, kStoreRaw, false>);
+    allow_gemm_lds(k_logits_bf16<kEpiLse, kStoreExp, false>);
+    allow_gemm_lds(k_logits_bf16<kEpiLse, kStoreExp, true>);
+    allow_gemm_lds(k_logits_bf16<kEpiNone, kStoreRaw, false>);
+    allow_gemm_lds(k_gemm_dh_bf16);
+    allow_gemm_lds(k_gemm_dw_bf16<0>);
+    allow_gemm_lds(k_gemm_dw_bf16<1>);
+    allow_gemm_lds(k_gemm_dw_bf16<2>);
+    allow_gemm_lds(k_gemm_dw_bf16<3>);
   });
 }
 
 // ---------------------------------------------------------------------------
 // Stage profiling: event pairs recorded on the call's stream.
 // ---------------------------------------------------------------------------
-enum Stage { kPrep = 0, kHT, kLogits, kCombine, kDlogits, kDHGemm, kDHReduce, kDWGemm, kLoss, kNumStages };
-const char* const kStageNames[kNumStages] = {"prep", "h_transpose", "logits_gemm", "row_combine",
-                                             "dlogits", "dH_gemm", "dH_reduce", "dW_gemm", "loss"};
+enum Stage {
+  kPrep = 0, kHT, kLogits, kCombine, kDlogits, kDHGemm, kDHReduce, kDWGemm, kLoss, kFlagged, kDb,
+  kNumStages
+};
+const char* const kStageNames[kNumStages] = {
+    "prep",    "h_transpose", "logits_gemm", "row_combine", "dlogits", "dH_gemm",
+    "dH_reduce", "dW_gemm",   "loss",        "flagged_rows", "db"};
 
 struct Profiler {
   bool on = false;
@@ -294,45 +324,155 @@ struct Core {
   float eob_w;
 };
 
-// per-row stage of a chunk: lse/loss/coefficients (fwd_bwd) or coefficients
-// only (shard backward, lse given).  Chunk-local lse / target columns go to
-// lsec / tcol (bf16 path).  Returns the lse pointer the fp32 dlogits reads.
-const float* run_rows(const Core& c, const Plan& p, const floatx2* part, float* coef, float* lsec,
-                      int* tcol, int64_t c0, int64_t cmax, hipStream_t st) {
+// Row-combine arguments of a chunk common to every mode (mode 0, no chunk outputs).
+CombineArgs combine_args(const Core& c, const Plan& p, const floatx2* part, int64_t c0,
+                         int64_t cmax) {
+  CombineArgs a{};
+  a.part = part;
+  a.rpart = c.rpart;
+  a.ldp = p.C;
+  a.nT = p.nT;
+  a.cmax = cmax;
+  a.rows = c.rows;
+  a.count = c.count;
+  a.c0 = c0;
+  a.mode = 0;
+  a.target = c.target;
+  a.p_mask = c.p_mask;
+  a.ignore = c.ignore;
+  a.zt = c.zt;
+  a.R = c.R;
+  a.eps = c.eps;
+  a.Vg = (float)c.Vg;
+  a.s = c.s;
+  a.D = c.D;
+  a.eob = c.eob;
+  a.eob_w = c.eob_w;
+  a.lse_out = c.lse_out;
+  a.rloss_out = c.rloss_out;
+  a.v0 = c.v0;
+  return a;
+}
+
+// Row-combine arguments of a vocabulary shard's partials (mode 1).
+CombineArgs shard_combine_args(const floatx2* part, const float* rpart, const Plan& p,
+                               int64_t cmax, const int* rows, const int* count, int64_t c0,
+                               float* out_m, float* out_s, float* out_r) {
+  CombineArgs a{};
+  a.part = part;
+  a.rpart = rpart;
+  a.ldp = p.C;
+  a.nT = p.nT;
+  a.cmax = cmax;
+  a.rows = rows;
+  a.count = count;
+  a.c0 = c0;
+  a.mode = 1;
+  a.out_m = out_m;
+  a.out_s = out_s;
+  a.out_r = out_r;
+  return a;
+}
+
+// Grid of the logits kernels that run over a device-side list of rows: one
+// wave of blocks striding over the tiles (usually the list is empty).
+unsigned indirect_grid(int64_t V, int64_t cmax) {
+  return (unsigned)std::min<int64_t>(std::max<int64_t>(cdiv(V, kBM) * cdiv(cmax, kBN), 1), 256);
+}
+
+// Rows the combine flagged (a logit more than 30 nats above the target
+// logit, past the clamp of the reference-relative exponentials): their
+// max-shifted partials (logits GEMM over the listed rows), their lse, loss
+// and coefficients (row combine over the list) and, when E is wanted, their
+// rows of E relative to the lse with the target term.  Launched every time;
+// with no flagged row each kernel returns at once.
+void run_flagged_rows(const Core& c, const Plan& p, const LogitsArgs& la, const CombineArgs& ca,
+                      int* flist, int* nflag, bf16* E, int* tcol, int64_t cmax, hipStream_t st) {
+  StageTimer tm(kFlagged, st);
+  const unsigned g = indirect_grid(c.V, cmax);
+  LogitsArgs f = la;
+  f.gidx = flist;
+  f.gcount = nflag;
+  f.rpart = nullptr;  // the row sums of the main pass stand
+  f.E = nullptr;
+  k_logits_bf16<kEpiMax, kStoreNone, true><<<g, kGemmThreads, kGemmLds, st>>>(f);
+  CombineArgs cb = ca;
+  cb.mode = 0;
+  cb.jlist = flist;
+  cb.jcount = nflag;
+  cb.E = nullptr;
+  cb.flag_count = nullptr;
+  cb.flag_list = nullptr;
+  k_combine_rows<<<grid1(cmax, 32), 256, 0, st>>>(cb);
+  if (E == nullptr) return;
+  LogitsArgs e = f;
+  e.part = nullptr;
+  e.ref = c.lse_out;
+  e.tcol = tcol;
+  e.tsub = 1.f - c.eps;
+  e.E = E;
+  k_logits_bf16<kEpiLse, kStoreExp, true><<<g, kGemmThreads, kGemmLds, st>>>(e);
+}
+
+// per-row stage of a chunk on the fp32 path: lse/loss/coefficients
+// (fwd_bwd) or coefficients only (shard backward, lse given).  Returns the
+// lse pointer the fp32 dlogits reads.
+const float* run_rows_f32(const Core& c, const Plan& p, const floatx2* part, float* coef,
+                          int64_t c0, int64_t cmax, hipStream_t st) {
   StageTimer tm(kCombine, st);
   if (c.lse_in == nullptr) {
-    k_combine_rows<<<grid1(cmax, 32), 256, 0, st>>>(
-        part, c.rpart, p.C, p.nT, cmax, c.rows, c.count, c0, 0, c.target, c.p_mask, c.ignore,
-        c.zt, c.R, c.eps, (float)c.Vg, c.s, c.D, c.eob, c.eob_w, c.lse_out, c.rloss_out, coef,
-        lsec, tcol, c.v0, nullptr, nullptr, nullptr);
+    CombineArgs a = combine_args(c, p, part, c0, cmax);
+    a.coef_out = coef;
+    k_combine_rows<<<grid1(cmax, 32), 256, 0, st>>>(a);
     return c.lse_out + c0;
   }
-  k_coef_rows<<<grid1(cmax, 256), 256, 0, st>>>(c.target, c.p_mask, c.ignore, cmax, c.rows,
-                                                 c.count, c0, c.s, c.D, c.eob, c.eob_w, coef,
-                                                 c.lse_in, lsec, tcol, c.v0);
+  k_coef_rows<<<grid1(cmax, 256), 256, 0, st>>>(c.target, c.p_mask, c.ignore, cmax, nullptr,
+                                                 nullptr, c0, c.s, c.D, c.eob, c.eob_w, coef,
+                                                 c.lse_in, nullptr, nullptr, c.v0);
   return c.lse_in + c0;
 }
 
 // bf16: only rows with target != ignore_index are multiplied (compacted on
-// the device; kernels read the count, so there is no host synchronisation);
-// W and g are read in place, only the chunk's h is copied transposed.
+// the device; kernels read the count, so there is no host synchronisation).
+// Per chunk: the chunk's rows of h gathered once; the logits GEMM stores
+// E = exp(z - r) relative to each row's target logit r (or to the given lse
+// of a vocabulary shard) with the partials of the logsumexp; the row combine
+// finishes lse, loss, coef and alpha = coef / sum_v E and puts the target
+// term into E; dH = alpha (E W) and dW = (alpha h)^T E read E in place (W
+// too, through the LDS transpose), with the label-smoothing term added from
+// sum_v W_v (an all-ones row of E) and u = sum_t coef_t h_t.
 int run_core_bf16(const Core& c, const Plan& p, char* ws, hipStream_t st) {
-  bf16* zb = reinterpret_cast<bf16*>(ws + p.oZ);
-  bf16* gb = reinterpret_cast<bf16*>(ws + p.oG);
+  bf16* E = reinterpret_cast<bf16*>(ws + p.oZ);
   bf16* hT = reinterpret_cast<bf16*>(ws + p.oHT);
   bf16* hc = reinterpret_cast<bf16*>(ws + p.oHC);
   float* coef = reinterpret_cast<float*>(ws + p.oCoef);
-  float* lsec = reinterpret_cast<float*>(ws + p.oLsec);
   int* tcol = reinterpret_cast<int*>(ws + p.oTcol);
   floatx2* part = reinterpret_cast<floatx2*>(ws + p.oPart);
   float* dHpart = reinterpret_cast<float*>(ws + p.oDHpart);
   float* dW32 = reinterpret_cast<float*>(ws + p.oDW32);
+  int* nflag = reinterpret_cast<int*>(ws + p.oFlag);
+  int* flist = reinterpret_cast<int*>(ws + p.oFlist);
+  float* upart = reinterpret_cast<float*>(ws + p.oUpart);
+  float* u = reinterpret_cast<float*>(ws + p.oU);
   const bf16* h = static_cast<const bf16*>(c.h);
   const bf16* W = static_cast<const bf16*>(c.W);
   const bf16* bias = static_cast<const bf16*>(c.bias);
   const int64_t H = c.H, V = c.V, Vp = p.Vp;
-  int64_t db_off = 0;  // row blocks of db partials written so far
+  const bool given_lse = c.lse_in != nullptr;  // a vocabulary shard's backward
   const bool want_g = c.dH != nullptr || c.dW != nullptr || c.db != nullptr;
+  const bool smooth = c.eps > 0.f;
+  // Large label smoothing: the logits are stored and one row pass forms g
+  // (the smoothing share subtracted before rounding, alpha = 1); otherwise E
+  // holds the exponentials and the share is added to the products exactly.
+  const bool exact = c.eps > kFusedSmoothingMax;
+  // alpha (the row factor of E): coef / sum_v E, or coef itself when E is
+  // relative to the lse
+  float* alpha = (given_lse && !exact) ? coef : reinterpret_cast<float*>(ws + p.oAlpha);
+  const bool fused_smooth = smooth && !exact;
+  const int extra = (c.dH != nullptr && fused_smooth) ? 1 : 0;  // all-ones row of E: sum_v W_v
+  const bool need_u = fused_smooth && (c.dW != nullptr || c.db != nullptr);
+  const float epsV = c.eps / (float)c.Vg;
+  int64_t db_off = 0, u_off = 0;  // row blocks of db / smoothing-term partials written so far
   if (c.dH != nullptr) {
     StageTimer tm(kPrep, st);
     if (c.dH_f32)
@@ -346,80 +486,133 @@ int run_core_bf16(const Core& c, const Plan& p, char* ws, hipStream_t st) {
     const int64_t c0 = ic * p.C;
     const int64_t cmax = std::min(p.C, c.N - c0);  // rows of the chunk if none were ignored
     const int64_t Cpc = round_up(cmax, 64);
+    const bool last = ic + 1 == p.nchunks;
     {
       StageTimer tm(kHT, st);
       dim3 g((unsigned)(Cpc / 64), (unsigned)cdiv(H, 64));
-      // h^T only for dW
-      k_transpose_gather_bf16<<<g, 256, 0, st>>>(h, c.rows, c.count, c0, cmax, H,
-                                                 c.dW != nullptr ? hT : nullptr, p.Cp, Cpc, hc);
+      k_transpose_gather_bf16<<<g, 256, 0, st>>>(h, c.rows, c.count, c0, cmax, H, nullptr, 0,
+                                                 Cpc, hc);
+      if (want_g)
+        k_e_pad_rows<<<grid_strided(64 * Vp / 8, 256), 256, 0, st>>>(E, Vp, V, c.count, c0, cmax,
+                                                                     extra);
     }
-    {  // 1. logits (+ softmax partials)
+    if (given_lse) {  // coefficients and target columns come first: the epilogue needs them
+      StageTimer tm(kCombine, st);
+      k_coef_rows<<<grid1(cmax, 256), 256, 0, st>>>(c.target, c.p_mask, c.ignore, cmax, c.rows,
+                                                     c.count, c0, c.s, c.D, c.eob, c.eob_w, coef,
+                                                     c.lse_in, nullptr, tcol, c.v0);
+    }
+    LogitsArgs la{};
+    la.W = W;
+    la.bias = bias;
+    la.h = hc;
+    la.V = (int)V;
+    la.cmax = (int)cmax;
+    la.H = (int)H;
+    la.s = c.s;
+    la.count = c.count;
+    la.c0 = c0;
+    la.rows = c.rows;
+    la.part = part;
+    la.rpart = c.rpart;
+    la.ldp = p.C;
+    la.E = want_g ? E : nullptr;
+    la.ldE = Vp;
+    la.ref = given_lse ? c.lse_in : c.zt;
+    la.tcol = tcol;
+    la.tsub = 1.f - c.eps;
+    la.group_m = kGroupM;
+    {  // 1. logits, E and the logsumexp partials
       StageTimer tm(kLogits, st);
       const int blocks = (int)(cdiv(V, kBM) * cdiv(cmax, kBN));
-      if (c.lse_in == nullptr && want_g)
-        k_logits_bf16<true, true><<<blocks, kGemmThreads, kGemmLds, st>>>(
-            W, bias, hc, (int)V, (int)cmax, (int)H, c.s, nullptr, c.count, c0, part, c.rpart, p.C,
-            zb, Vp, kGroupM);
-      else if (c.lse_in == nullptr)  // loss only: the logits are not stored
-        k_logits_bf16<false, true><<<blocks, kGemmThreads, kGemmLds, st>>>(
-            W, bias, hc, (int)V, (int)cmax, (int)H, c.s, nullptr, c.count, c0, part, c.rpart, p.C,
-            nullptr, Vp, kGroupM);
-      else
-        k_logits_bf16<true, false><<<blocks, kGemmThreads, kGemmLds, st>>>(
-            W, bias, hc, (int)V, (int)cmax, (int)H, c.s, nullptr, c.count, c0, part, nullptr, p.C,
-            zb, Vp, kGroupM);
+      if (given_lse && exact)
+        k_logits_bf16<kEpiNone, kStoreRaw, false><<<blocks, kGemmThreads, kGemmLds, st>>>(la);
+      else if (given_lse)
+        k_logits_bf16<kEpiLse, kStoreExp, false><<<blocks, kGemmThreads, kGemmLds, st>>>(la);
+      else if (want_g && exact)
+        k_logits_bf16<kEpiRef, kStoreRaw, false><<<blocks, kGemmThreads, kGemmLds, st>>>(la);
+      else if (want_g)
+        k_logits_bf16<kEpiRef, kStoreExp, false><<<blocks, kGemmThreads, kGemmLds, st>>>(la);
+      else  // loss only: E is not stored
+        k_logits_bf16<kEpiRef, kStoreNone, false><<<blocks, kGemmThreads, kGemmLds, st>>>(la);
     }
-    // 2. per-row combine
-    run_rows(c, p, part, coef, lsec, tcol, c0, cmax, st);
-    if (!want_g) continue;  // no gradient wanted: the loss needs nothing more
-    {  // 3. dlogits: blocked z -> row-major g, zero rows up to the padded count
-      StageTimer tm(kDlogits, st);
-      if (c.db == nullptr) {
-        dim3 g((unsigned)cdiv(Vp, 1024), (unsigned)(Cpc / 16));
-        k_gpass_blk<16, 1024><<<g, 256, 0, st>>>(zb, Vp, cmax, c.count, c0, V, lsec, coef, tcol,
-                                                 c.eps, (float)c.Vg, gb, nullptr, c.s);
-      } else {  // db partials per 64 rows
-        dim3 g((unsigned)cdiv(Vp, 256), (unsigned)(Cpc / 64));
-        k_gpass_blk<64, 256><<<g, 256, 0, st>>>(zb, Vp, cmax, c.count, c0, V, lsec, coef, tcol,
-                                                c.eps, (float)c.Vg, gb, c.dbpart + db_off * Vp,
-                                                c.s);
-        db_off += Cpc / 64;
+    if (!given_lse) {  // 2. per-row combine (lse, loss, coef, alpha, target term), flagged rows
+      CombineArgs ca = combine_args(c, p, part, c0, cmax);
+      ca.mode = 2;
+      ca.coef_out = coef;
+      ca.alpha_out = alpha;
+      ca.tcol = tcol;
+      ca.E = exact ? nullptr : la.E;
+      ca.ldE = Vp;
+      ca.flag_count = nflag + ic;
+      ca.flag_list = flist;
+      {
+        StageTimer tm(kCombine, st);
+        k_combine_rows<<<grid1(cmax, 32), 256, 0, st>>>(ca);
       }
+      run_flagged_rows(c, p, la, ca, flist, nflag + ic, exact ? nullptr : la.E, tcol, cmax, st);
     }
-    if (c.dH != nullptr) {  // 4. dH = g W (split over the vocabulary, ordered reduction, scattered rows)
+    if (!want_g) continue;  // no gradient wanted: the loss needs nothing more
+    if (exact) {  // g over the stored logits, rounded once (alpha = 1)
+      StageTimer tm(kDlogits, st);
+      dim3 g((unsigned)std::min<int64_t>(cdiv(Vp, 2048), 64), (unsigned)std::min<int64_t>(cmax, 4096));
+      k_gpass_rows<<<g, 256, 0, st>>>(E, Vp, V, c.count, c0, cmax, c.rows,
+                                      given_lse ? c.lse_in : c.lse_out, coef, tcol, c.eps,
+                                      (float)c.Vg, c.s, alpha);
+    }
+    {  // (alpha h)^T for dW, smoothing-term partials
+      StageTimer tm(kHT, st);
+      dim3 g((unsigned)(Cpc / 64), (unsigned)cdiv(H, 64));
+      k_scale_transpose_bf16<<<g, 256, 0, st>>>(hc, c.count, c0, cmax, H, alpha, coef, hT, p.Cp,
+                                                need_u ? upart : nullptr, u_off);
+      u_off += Cpc / 64;
+      if (need_u && last)  // u = sum_t coef_t h_t and sum_t coef_t over every row
+        k_colsum_finish<float><<<grid1(H + 1, 256), 256, 0, st>>>(upart, u_off, H + 1, H + 1, u);
+    }
+    if (c.dH != nullptr) {  // 3. dH (split over the vocabulary, ordered reduction, scattered rows)
       const int S = p.splits;
-      const int blocks = (int)(cdiv(cmax, kBM) * cdiv(H, kBN) * S);
+      const int blocks = (int)(cdiv(cmax + extra, kBM) * cdiv(H, kBN) * S);
       {
         StageTimer tm(kDHGemm, st);
-        k_gemm_dh_bf16<<<blocks, kGemmThreads, kGemmLds, st>>>(gb, Vp, (int)cmax, c.count, c0, W,
-                                                               (int)V, (int)H, (int)(Vp / kBK), S,
-                                                               dHpart, kGroupMBwd, c.dH,
-                                                               c.dH_f32 ? 1 : 0, c.rows);
+        k_gemm_dh_bf16<<<blocks, kGemmThreads, kGemmLds, st>>>(
+            E, Vp, (int)cmax, extra, c.count, c0, W, (int)V, (int)H, (int)(Vp / kBK), S, dHpart,
+            kGroupMBwd, c.dH, c.dH_f32 ? 1 : 0, c.rows, alpha);
       }
       StageTimer tm(kDHReduce, st);
-      if (S == 1) {
-        // at most one split: the GEMM wrote dH itself
-      } else if (c.dH_f32)
-        k_splitk_scatter<float><<<(unsigned)std::min<int64_t>(cmax, 2048), 256, 0, st>>>(
-            dHpart, S, Vp / kBK, cmax, H, c.rows, c.count, c0, (float*)c.dH);
-      else
-        k_splitk_scatter<bf16><<<(unsigned)std::min<int64_t>(cmax, 2048), 256, 0, st>>>(
-            dHpart, S, Vp / kBK, cmax, H, c.rows, c.count, c0, (bf16*)c.dH);
+      if (S > 1 || extra) {  // (the kernel returns at once when the GEMM wrote the rows)
+        const unsigned g = (unsigned)std::min<int64_t>(cmax, 2048);
+        if (c.dH_f32)
+          k_splitk_scatter<float><<<g, 256, 0, st>>>(dHpart, S, Vp / kBK, cmax, extra, H, c.rows,
+                                                     c.count, c0, alpha, coef, epsV,
+                                                     (float*)c.dH);
+        else
+          k_splitk_scatter<bf16><<<g, 256, 0, st>>>(dHpart, S, Vp / kBK, cmax, extra, H, c.rows,
+                                                    c.count, c0, alpha, coef, epsV, (bf16*)c.dH);
+      }
     }
-    if (c.dW != nullptr) {  // 5. dW += g^T h
+    if (c.dW != nullptr) {  // 4. dW += (alpha h)^T E, the smoothing term with the final value
       StageTimer tm(kDWGemm, st);
       int mode = 0;
-      if (p.nchunks > 1) mode = ic == 0 ? 1 : (ic + 1 == p.nchunks ? 3 : 2);
+      if (p.nchunks > 1) mode = ic == 0 ? 1 : (last ? 3 : 2);
       const int blocks = (int)(cdiv(V, kBM) * cdiv(H, kBN));
       auto kern = mode == 0 ? k_gemm_dw_bf16<0>
                             : (mode == 1 ? k_gemm_dw_bf16<1> : (mode == 2 ? k_gemm_dw_bf16<2> : k_gemm_dw_bf16<3>));
-      kern<<<blocks, kGemmThreads, kGemmLds, st>>>(gb, Vp, (int)cmax, c.count, c0, (int)V, hT,
-                                                   p.Cp, (int)H, (bf16*)c.dW, dW32, kGroupMBwd);
+      kern<<<blocks, kGemmThreads, kGemmLds, st>>>(E, Vp, (int)cmax, c.count, c0, (int)V, hT, p.Cp,
+                                                   (int)H, (bf16*)c.dW, dW32, kGroupMBwd,
+                                                   fused_smooth ? u : nullptr, epsV);
+    }
+    if (c.db != nullptr) {  // 5. db partials: sum_t alpha_t E[t, :] per 64 rows
+      StageTimer tm(kDb, st);
+      dim3 g((unsigned)cdiv(Vp, 256), (unsigned)(Cpc / 64));
+      k_db_partials<<<g, 256, 0, st>>>(E, Vp, c.count, c0, cmax, alpha, c.dbpart + db_off * Vp);
+      db_off += Cpc / 64;
     }
   }
   if (c.db != nullptr) {
-    StageTimer tm(kDWGemm, st);
-    k_colsum_finish<bf16><<<grid1(V, 256), 256, 0, st>>>(c.dbpart, db_off, Vp, V, (bf16*)c.db);
+    StageTimer tm(kDb, st);
+    k_db_finish<bf16><<<grid1(V, 256), 256, 0, st>>>(c.dbpart, db_off, Vp, V,
+                                                     fused_smooth ? u + H : nullptr, epsV,
+                                                     (bf16*)c.db);
   }
   return launch_status();
 }
@@ -462,7 +655,7 @@ int run_core_f32(const Core& c, const Plan& p, char* ws, hipStream_t st) {
         k_row_partials_f32<<<g2, 64, 0, st>>>(zb, Vp, Cc, V, part, p.C);
       }
     }
-    const float* lse_c = run_rows(c, p, part, coef, nullptr, nullptr, c0, Cc, st);
+    const float* lse_c = run_rows_f32(c, p, part, coef, c0, Cc, st);
     if (!want_g) continue;  // no gradient wanted: the loss needs nothing more
     {
       StageTimer tm(kDlogits, st);
@@ -536,6 +729,126 @@ void launch_row_dots(const void* h, const void* W, const void* bias, const int64
       (const float*)h, (const float*)W, (const float*)bias, H, target, 0, V, ignore, s,
       smooth ? wsum : nullptr, (smooth && bias != nullptr) ? bsum : nullptr, N, zt,
       smooth ? R : nullptr);
+}
+
+// Argument checks of the forward-only entry points (everything but the workspace).
+int check_fwd_args(const void* h, const void* W, const void* bias, const int64_t* target,
+                   const float* p_mask, int64_t N, int64_t H, int64_t V, int dtype,
+                   float label_smoothing, float logit_scale, int reduction, int64_t eob_token_id,
+                   float eob_weight, const float* loss) {
+  int rc = check_common(h, W, target, N, H, V, dtype, logit_scale);
+  if (rc != FLDCE_OK) return rc;
+  if (!loss) return FLDCE_ERR_NULL_POINTER;
+  rc = check_loss_args(reduction, label_smoothing, eob_token_id, eob_weight);
+  if (rc != FLDCE_OK) return rc;
+  if (!aligned16(h) || !aligned16(W) || !aligned16(bias) || !aligned16(target) ||
+      !aligned16(p_mask))
+    return FLDCE_ERR_ALIGNMENT;
+  return FLDCE_OK;
+}
+
+// The forward-only path on a checked call: ws holds at least p.total bytes.
+int run_fwd(const Plan& p, const void* h, const void* W, const void* bias, const int64_t* target,
+            const float* p_mask, int64_t N, int64_t H, int64_t V, int dtype,
+            int64_t ignore_index, float label_smoothing, float logit_scale, int reduction,
+            int64_t total, int64_t eob_token_id, float eob_weight, float* loss, float* row_lse,
+            float* row_loss, char* ws, hipStream_t st) {
+  set_gemm_attributes();
+  if (N == 0) {
+    zero_fill(loss, 1, 4, st);
+    return launch_status();
+  }
+  float* D = reinterpret_cast<float*>(ws + p.oD);
+  const bool smooth = label_smoothing > 0.f;
+  const bool bf = dtype == FLDCE_DTYPE_BF16;
+  float* colpart = reinterpret_cast<float*>(ws + p.oColpart);
+  float* wsum = reinterpret_cast<float*>(ws + p.oWsum);
+  float* bsum = reinterpret_cast<float*>(ws + p.oBsum);
+  float* zt = reinterpret_cast<float*>(ws + p.oZt);
+  float* R = reinterpret_cast<float*>(ws + p.oR);
+  float* lse = row_lse ? row_lse : reinterpret_cast<float*>(ws + p.oLse);
+  float* rl = row_loss ? row_loss : reinterpret_cast<float*>(ws + p.oRloss);
+  floatx2* part = reinterpret_cast<floatx2*>(ws + p.oPart);
+  float* rpart = reinterpret_cast<float*>(ws + p.oRpart);
+  int* rows = reinterpret_cast<int*>(ws + p.oRows);
+  int* count = reinterpret_cast<int*>(ws + p.oCount);
+  int* nflag = reinterpret_cast<int*>(ws + p.oFlag);
+  {
+    StageTimer tm(kPrep, st);
+    if (bf)
+      k_prep_rows<<<1, 1024, 0, st>>>(target, N, ignore_index, rows, count, reduction, total, D,
+                                      lse, 0.f, rl, 0.f, nullptr, 0.f, nflag, 1);
+    else
+      k_divisor<<<1, 1024, 0, st>>>(target, N, ignore_index, reduction, total, D);
+    launch_row_dots(h, W, bias, target, N, H, V, bf, ignore_index, logit_scale, smooth, colpart,
+                    wsum, bsum, zt, R, st);
+  }
+  Core c{h, W, bias, target, p_mask, N, H, V, 0, V, dtype, ignore_index, label_smoothing,
+         logit_scale, nullptr, lse, rl, zt, (smooth && !bf) ? R : nullptr,
+         (smooth && bf) ? rpart : nullptr, D, bf ? rows : nullptr, bf ? count : nullptr, nullptr,
+         false, nullptr, nullptr, nullptr, eob_token_id, eob_weight};
+  if (bf) {  // logits never stored: partials from the GEMM epilogue, valid rows only
+    bf16* hc = reinterpret_cast<bf16*>(ws + p.oHC);
+    int* flist = reinterpret_cast<int*>(ws + p.oFlist);
+    {
+      StageTimer tm(kHT, st);
+      dim3 g((unsigned)(p.Cp / 64), (unsigned)cdiv(H, 64));
+      k_transpose_gather_bf16<<<g, 256, 0, st>>>((const bf16*)h, rows, count, 0, N, H, nullptr, 0,
+                                                 p.Cp, hc);
+    }
+    LogitsArgs la{};
+    la.W = (const bf16*)W;
+    la.bias = (const bf16*)bias;
+    la.h = hc;
+    la.V = (int)V;
+    la.cmax = (int)N;
+    la.H = (int)H;
+    la.s = logit_scale;
+    la.count = count;
+    la.rows = rows;
+    la.part = part;
+    la.rpart = c.rpart;
+    la.ldp = p.C;
+    la.ref = zt;
+    la.group_m = kGroupM;
+    {  // the same partials as the training path, so the loss is bit for bit the same
+      StageTimer tm(kLogits, st);
+      const int blocks = (int)(cdiv(V, kBM) * cdiv(N, kBN));
+      k_logits_bf16<kEpiRef, kStoreNone, false><<<blocks, kGemmThreads, kGemmLds, st>>>(la);
+    }
+    CombineArgs ca = combine_args(c, p, part, 0, N);
+    ca.mode = 2;
+    ca.flag_count = nflag;
+    ca.flag_list = flist;
+    {
+      StageTimer tm(kCombine, st);
+      k_combine_rows<<<grid1(N, 32), 256, 0, st>>>(ca);
+    }
+    run_flagged_rows(c, p, la, ca, flist, nflag, nullptr, nullptr, N, st);
+  } else {  // fp32: z per chunk, row partials, combine
+    float* zb = reinterpret_cast<float*>(ws + p.oZ);
+    for (int64_t c0 = 0; c0 < N; c0 += p.C) {
+      const int64_t Cc = std::min(p.C, N - c0);
+      {
+        StageTimer tm(kLogits, st);
+        dim3 g((unsigned)cdiv(V, 64), (unsigned)cdiv(Cc, 64));
+        k_gemm_f32_nt<<<g, 256, 0, st>>>((const float*)h + c0 * H, H, Cc, (const float*)W, H, V,
+                                         H, logit_scale, zb, p.Vp, 0);
+        if (bias != nullptr)
+          k_add_bias_f32<<<dim3((unsigned)cdiv(V, 256), (unsigned)std::min<int64_t>(Cc, 256)), 256,
+                           0, st>>>(zb, p.Vp, Cc, V, (const float*)bias, logit_scale);
+        dim3 g2((unsigned)cdiv(Cc, 64), (unsigned)p.nT);
+        k_row_partials_f32<<<g2, 64, 0, st>>>(zb, p.Vp, Cc, V, part, p.C);
+      }
+      StageTimer tm(kCombine, st);
+      k_combine_rows<<<grid1(Cc, 32), 256, 0, st>>>(combine_args(c, p, part, c0, Cc));
+    }
+  }
+  {
+    StageTimer tm(kLoss, st);
+    k_loss_reduce<<<1, 1024, 0, st>>>(rl, N, D, loss);
+  }
+  return launch_status();
 }
 
 }  // namespace
@@ -647,7 +960,8 @@ int fldce_fwd_bwd_ex(const void* h, const void* W, const void* bias, const int64
     StageTimer tm(kPrep, st);
     if (bf)
       k_prep_rows<<<1, 1024, 0, st>>>(target, N, ignore_index, rows, count, reduction, total, D,
-                                      lse, 0.f, rl, 0.f, nullptr, 0.f);
+                                      lse, 0.f, rl, 0.f, nullptr, 0.f,
+                                      reinterpret_cast<int*>(ws + p.oFlag), (int)p.nchunks);
     else
       k_divisor<<<1, 1024, 0, st>>>(target, N, ignore_index, reduction, total, D);
     launch_row_dots(h, W, bias, target, N, H, V, bf, ignore_index, logit_scale, smooth, colpart,
@@ -672,96 +986,16 @@ int fldce_fwd(const void* h, const void* W, const void* bias, const int64_t* tar
               int64_t ignore_index, float label_smoothing, float logit_scale, int reduction,
               int64_t total, int64_t eob_token_id, float eob_weight, float* loss, float* row_lse,
               float* row_loss, void* workspace, size_t workspace_bytes, void* stream) {
-  int rc = check_common(h, W, target, N, H, V, dtype, logit_scale);
+  int rc = check_fwd_args(h, W, bias, target, p_mask, N, H, V, dtype, label_smoothing,
+                          logit_scale, reduction, eob_token_id, eob_weight, loss);
   if (rc != FLDCE_OK) return rc;
-  if (!loss) return FLDCE_ERR_NULL_POINTER;
-  rc = check_loss_args(reduction, label_smoothing, eob_token_id, eob_weight);
-  if (rc != FLDCE_OK) return rc;
-  if (!aligned16(h) || !aligned16(W) || !aligned16(bias) || !aligned16(target) ||
-      !aligned16(p_mask) || !aligned16(workspace))
-    return FLDCE_ERR_ALIGNMENT;
+  if (!aligned16(workspace)) return FLDCE_ERR_ALIGNMENT;
   const Plan p = make_plan(kFwd, N, H, V, dtype, 0);
   if (!grids_fit(p, dtype)) return FLDCE_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < p.total) return FLDCE_ERR_WORKSPACE;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  set_gemm_attributes();
-  if (N == 0) {
-    zero_fill(loss, 1, 4, st);
-    return launch_status();
-  }
-  char* ws = static_cast<char*>(workspace);
-  float* D = reinterpret_cast<float*>(ws + p.oD);
-  const bool smooth = label_smoothing > 0.f;
-  const bool bf = dtype == FLDCE_DTYPE_BF16;
-  float* colpart = reinterpret_cast<float*>(ws + p.oColpart);
-  float* wsum = reinterpret_cast<float*>(ws + p.oWsum);
-  float* bsum = reinterpret_cast<float*>(ws + p.oBsum);
-  float* zt = reinterpret_cast<float*>(ws + p.oZt);
-  float* R = reinterpret_cast<float*>(ws + p.oR);
-  float* lse = row_lse ? row_lse : reinterpret_cast<float*>(ws + p.oLse);
-  float* rl = row_loss ? row_loss : reinterpret_cast<float*>(ws + p.oRloss);
-  floatx2* part = reinterpret_cast<floatx2*>(ws + p.oPart);
-  float* rpart = reinterpret_cast<float*>(ws + p.oRpart);
-  int* rows = reinterpret_cast<int*>(ws + p.oRows);
-  int* count = reinterpret_cast<int*>(ws + p.oCount);
-  {
-    StageTimer tm(kPrep, st);
-    if (bf)
-      k_prep_rows<<<1, 1024, 0, st>>>(target, N, ignore_index, rows, count, reduction, total, D,
-                                      lse, 0.f, rl, 0.f, nullptr, 0.f);
-    else
-      k_divisor<<<1, 1024, 0, st>>>(target, N, ignore_index, reduction, total, D);
-    launch_row_dots(h, W, bias, target, N, H, V, bf, ignore_index, logit_scale, smooth, colpart,
-                    wsum, bsum, zt, R, st);
-  }
-  const float Vf = (float)V;
-  if (bf) {  // logits never stored: partials from the GEMM epilogue, valid rows only
-    bf16* hc = reinterpret_cast<bf16*>(ws + p.oHC);
-    {
-      StageTimer tm(kHT, st);
-      dim3 g((unsigned)(p.Cp / 64), (unsigned)cdiv(H, 64));
-      k_transpose_gather_bf16<<<g, 256, 0, st>>>((const bf16*)h, rows, count, 0, N, H, nullptr, 0,
-                                                 p.Cp, hc);
-    }
-    {
-      StageTimer tm(kLogits, st);
-      const int blocks = (int)(cdiv(V, kBM) * cdiv(N, kBN));
-      k_logits_bf16<false, true><<<blocks, kGemmThreads, kGemmLds, st>>>(
-          (const bf16*)W, (const bf16*)bias, hc, (int)V, (int)N, (int)H, logit_scale, nullptr,
-          count, 0, part, smooth ? rpart : nullptr, p.C, nullptr, 0, kGroupM);
-    }
-    StageTimer tm(kCombine, st);
-    k_combine_rows<<<grid1(N, 32), 256, 0, st>>>(
-        part, smooth ? rpart : nullptr, p.C, p.nT, N, rows, count, 0, 0, target, p_mask,
-        ignore_index, zt, nullptr, label_smoothing, Vf, logit_scale, D, eob_token_id, eob_weight,
-        lse, rl, nullptr, nullptr, nullptr, 0, nullptr, nullptr, nullptr);
-  } else {  // fp32: z per chunk, row partials, combine
-    float* zb = reinterpret_cast<float*>(ws + p.oZ);
-    for (int64_t c0 = 0; c0 < N; c0 += p.C) {
-      const int64_t Cc = std::min(p.C, N - c0);
-      {
-        StageTimer tm(kLogits, st);
-        dim3 g((unsigned)cdiv(V, 64), (unsigned)cdiv(Cc, 64));
-        k_gemm_f32_nt<<<g, 256, 0, st>>>((const float*)h + c0 * H, H, Cc, (const float*)W, H, V,
-                                         H, logit_scale, zb, p.Vp, 0);
-        if (bias != nullptr)
-          k_add_bias_f32<<<dim3((unsigned)cdiv(V, 256), (unsigned)std::min<int64_t>(Cc, 256)), 256,
-                           0, st>>>(zb, p.Vp, Cc, V, (const float*)bias, logit_scale);
-        dim3 g2((unsigned)cdiv(Cc, 64), (unsigned)p.nT);
-        k_row_partials_f32<<<g2, 64, 0, st>>>(zb, p.Vp, Cc, V, part, p.C);
-      }
-      StageTimer tm(kCombine, st);
-      k_combine_rows<<<grid1(Cc, 32), 256, 0, st>>>(
-          part, nullptr, p.C, p.nT, Cc, nullptr, nullptr, c0, 0, target, p_mask, ignore_index, zt,
-          smooth ? R : nullptr, label_smoothing, Vf, logit_scale, D, eob_token_id, eob_weight, lse,
-          rl, nullptr, nullptr, nullptr, 0, nullptr, nullptr, nullptr);
-    }
-  }
-  {
-    StageTimer tm(kLoss, st);
-    k_loss_reduce<<<1, 1024, 0, st>>>(rl, N, D, loss);
-  }
-  return launch_status();
+  return run_fwd(p, h, W, bias, target, p_mask, N, H, V, dtype, ignore_index, label_smoothing,
+                 logit_scale, reduction, total, eob_token_id, eob_weight, loss, row_lse, row_loss,
+                 static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
 }
 
 int fldce_scale_grads(const float* grad_out, int dtype, void* dH, int64_t n_dH, void* dW,
@@ -828,16 +1062,26 @@ int fldce_shard_partials(const void* h, const void* W_local, const int64_t* targ
     }
     {
       StageTimer tm(kLogits, st);
-      k_logits_bf16<false, true><<<blocks, kGemmThreads, kGemmLds, st>>>(
-          (const bf16*)W_local, nullptr, hc, (int)V, (int)N, (int)H, logit_scale, nullptr, count,
-          0, part, row_sumlogit ? rpart : nullptr, p.C, nullptr, 0, kGroupM);
+      LogitsArgs la{};
+      la.W = (const bf16*)W_local;
+      la.h = hc;
+      la.V = (int)V;
+      la.cmax = (int)N;
+      la.H = (int)H;
+      la.s = logit_scale;
+      la.count = count;
+      la.rows = rows;
+      la.part = part;
+      la.rpart = row_sumlogit ? rpart : nullptr;
+      la.ldp = p.C;
+      la.group_m = kGroupM;
+      k_logits_bf16<kEpiMax, kStoreNone, false><<<blocks, kGemmThreads, kGemmLds, st>>>(la);
     }
     {
       StageTimer tm(kCombine, st);
       k_combine_rows<<<grid1(N, 32), 256, 0, st>>>(
-          part, row_sumlogit ? rpart : nullptr, p.C, p.nT, N, rows, count, 0, 1, nullptr, nullptr,
-          0, nullptr, nullptr, 0.f, 1.f, 1.f, nullptr, -1, 1.f, nullptr, nullptr, nullptr, nullptr,
-          nullptr, 0, row_max, row_sumexp, row_sumlogit);
+          shard_combine_args(part, row_sumlogit ? rpart : nullptr, p, N, rows, count, 0, row_max,
+                             row_sumexp, row_sumlogit));
     }
     StageTimer tm(kPrep, st);
     k_rowdot<bf16><<<grid_strided(N, 4), 256, 0, st>>>((const bf16*)h, (const bf16*)W_local, nullptr, H,
@@ -852,10 +1096,8 @@ int fldce_shard_partials(const void* h, const void* W_local, const int64_t* targ
                                        V, H, logit_scale, zb, p.Vp, 0);
       dim3 g2((unsigned)cdiv(Cc, 64), (unsigned)p.nT);
       k_row_partials_f32<<<g2, 64, 0, st>>>(zb, p.Vp, Cc, V, part, p.C);
-      k_combine_rows<<<grid1(Cc, 32), 256, 0, st>>>(
-          part, nullptr, p.C, p.nT, Cc, nullptr, nullptr, c0, 1, nullptr, nullptr, 0, nullptr,
-          nullptr, 0.f, 1.f, 1.f, nullptr, -1, 1.f, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
-          row_max, row_sumexp, nullptr);
+      k_combine_rows<<<grid1(Cc, 32), 256, 0, st>>>(shard_combine_args(
+          part, nullptr, p, Cc, nullptr, nullptr, c0, row_max, row_sumexp, nullptr));
     }
     if (row_sumlogit) launch_colsum((const float*)W_local, V, H, colpart, wsum, st);
     k_rowdot<float><<<grid_strided(N, 4), 256, 0, st>>>((const float*)h, (const float*)W_local, nullptr, H,

@@ -14,6 +14,13 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+// Largest sum over one 128-wide vocabulary slab of exp(z - r), r = the row's
+// target logit, for which a row's backward operand stays relative to r: 2^43.
+// Below it every such exponential is at most 2^43 (z - r <= 29.8 nats), and
+// a row's sum of up to 2^24 slabs stays far inside float32; a row with a
+// larger slab sum (some logit 25-30 nats or more above the target logit) is
+// redone relative to its logsumexp.
+constexpr float kRefSumMax = 8796093022208.0f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // Global / LDS address-space casts for the direct global->LDS load builtin.

@@ -3,9 +3,9 @@
 //
 // Every GEMM here computes C[m, n] = sum_k A(m, k) B(n, k), bf16 in, fp32
 // accumulate, with each operand read in its natural row-major layout: either
-// K contiguous (h and W for the logits, g for dH) or K as the row index (W
-// for dH, g and h for dW), the latter transposed on its way out of LDS by
-// the gfx950 transpose read.  No operand is transposed in memory.
+// K contiguous (h and W for the logits, the stored exponentials E for dH) or
+// K as the row index (W for dH, E for dW), the latter transposed on its way
+// out of LDS by the gfx950 transpose read.
 //
 // Tiling (CDNA4: 64-wide waves, 160 KB LDS, v_mfma_f32_16x16x32_bf16):
 //   * block tile 256 x 256, K step 64, 512 threads = 8 waves in a 2 (M) x 4
@@ -107,7 +107,7 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 // 16-byte LDS read.
 //
 // Tile<true>: the operand is row-major with K as the ROW index (e.g. W [V, H]
-// as the K = V operand of dH, or g [C, V] and h [C, H] as the K = C operands
+// as the K = V operand of dH, or E [C, V] as the K = C operand
 // of dW); its LDS tile is 64 K-rows x 256 columns (512 B rows, 32-byte
 // segment s of row r at position s ^ tr_swz(r)) and a fragment is gathered
 // with two ds_read_b64_tr_b16.  Within each 16-lane group that instruction
@@ -205,9 +205,10 @@ struct Tile<true> {
 
 // Main loop: acc[i][j] (wave sub-tile i along M, j along N) accumulates
 // sum_k A(m, k) B(n, k) for m in [m0, m0+256), n in [n0, n0+256) over K tiles
-// [kt0, kt0 + nk).  For a normal operand X_rows/X_cols are (valid rows,
+// [kt0, kt0 + nk), starting from zero (kZeroAcc) or from the values the
+// caller put in acc.  For a normal operand X_rows/X_cols are (valid rows,
 // unused); for a transposed one (valid K rows, valid columns).
-template <bool kATr, bool kBTr>
+template <bool kATr, bool kBTr, bool kZeroAcc = true>
 __device__ __forceinline__ void gemm_mainloop(const bf16* __restrict__ A, int64_t lda, int a_rows,
                                               int a_cols, int m0, const bf16* __restrict__ B,
                                               int64_t ldb, int b_rows, int b_cols, int n0, int64_t kt0,
@@ -216,10 +217,12 @@ __device__ __forceinline__ void gemm_mainloop(const bf16* __restrict__ A, int64_
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / kWavesN, wn = wave % kWavesN;
+  if constexpr (kZeroAcc) {
 #pragma unroll
-  for (int i = 0; i < kTM; ++i)
+    for (int i = 0; i < kTM; ++i)
 #pragma unroll
-    for (int j = 0; j < kTN; ++j) acc[i][j] = floatx4{};
+      for (int j = 0; j < kTN; ++j) acc[i][j] = floatx4{};
+  }
   if (nk <= 0) return;
 
   Tile<kATr> ta;
@@ -281,74 +284,130 @@ __device__ __forceinline__ int acc_row(int wm, int i, int lane, int r) {
 __device__ __forceinline__ int acc_col(int wn, int j, int lane) { return wn * kTN * 16 + j * 16 + (lane & 15); }
 
 // ---------------------------------------------------------------------------
-// Logits GEMM with the softmax-partials epilogue, computed transposed:
-// A = W (rows = vocabulary, M = V), B = h chunk (rows = tokens, N = C), so
-// each lane holds 32 vocabulary values of each of its 4 tokens and the
+// Logits GEMM and its epilogues, computed transposed: A = W (rows =
+// vocabulary, M = V), B = the chunk's gathered rows of h (rows = tokens),
+// so each lane holds 32 vocabulary values of each of its 4 tokens and the
 // per-token reductions over the vocabulary are in-lane plus two exchanges
-// among the 4 lanes that share a token.
+// among the 4 lanes that share a token.  With z = s * (a + b_j) (a the
+// accumulator, b the bias or 0), per token and 128-wide vocabulary slab (one
+// wave's M range), part[slab * ldp + j] for chunk row j receives:
 //
-// For each token and each 128-wide vocabulary slab (one wave's M range) it
-// writes part[slab * ldp + token] = (max_j z, sum_j exp(z - max)) with
-// z = s * (a + b_j) (b = bias, or 0 when bias == nullptr), and rpart[slab * ldp + token] = sum_j z when rpart != nullptr
-// (kPart); with kStoreZ it stores the unscaled logits a + b_j (bf16; the
-// dlogits pass applies s) into zbuf in the blocked layout below (ldz =
-// padded vocabulary, a multiple of 64).
+//   kEpiMax  (max_v z, sum_v exp(z - max))            page 1's per-block
+//            logsumexp partials (shard partials; flagged rows below)
+//   kEpiRef  (S, S), S = sum_v e_v,  e_v = exp(z - r),  r = ref[i] the
+//            row's target logit: the partials of the same logsumexp relative
+//            to a reference known before the GEMM, so e_v / sum_v e_v is the
+//            softmax and the e_v themselves can be stored (kStoreExp) as the
+//            operand of both backward products.  A row where some slab's S
+//            exceeds kRefSumMax (some logit about 30 nats or more above the
+//            target logit) is flagged by the row combine and redone with
+//            kEpiMax / kEpiLse.
+//   kEpiLse  no partials; e_v = exp(z - lse_i) with ref = lse (given or
+//            combined), minus tsub at the target column tcol[j] (page 1,
+//            cross_entropy_kernel steps 5 and 6 without the row factor): a
+//            vocabulary shard's backward, and flagged rows.
+//   kEpiNone no partials (kStoreRaw only).
+//
+// and rpart[slab * ldp + j] = sum_v z when rpart != nullptr (label
+// smoothing).  kStoreExp stores e_v, kStoreRaw the logits a + b_j (bf16)
+// into E, row-major [chunk rows, ldE] (ldE = padded vocabulary, a multiple
+// of 64); columns V .. ldE - 1 are written as 0.
+//
+// Tokens: the GEMM's token q is chunk row j = q, or j = gidx[q] when
+// kIndirect (rows listed on the device; q < *gcount); chunk row j is batch
+// row rows[c0 + j] (ref is indexed by batch row).  Without kIndirect the
+// chunk holds min(*count - c0, cmax) tokens (cmax when count is null) and the
+// grid covers cmax: tiles past the count exit at once.  With kIndirect a
+// small grid strides over the tiles (usually there are none).
 // ---------------------------------------------------------------------------
-//
-// Token rows: chunk token j (< the chunk's row count, read from `count` when
-// it is not null) is row rows[c0 + j] of h when rows != nullptr (gathered
-// here), else row j of h (h = the chunk's rows, already gathered).  The grid covers cmax tokens; tiles past the
-// count exit at once.
-// Epilogue of the logits GEMM for one wave's 128 (vocabulary) x 64 (token)
-// accumulators; kFull: all 128 vocabulary rows exist (every tile but the last
-// vocabulary tile), so no per-element bound checks.  In phases over the 4
-// token groups j, so the 4 independent reductions overlap: maxima, the
-// cross-lane exchanges, the sums of exp (and of z), the partial stores, then
-// the z stores.
-template <bool kStoreZ, bool kPart, bool kFull>
-__device__ __forceinline__ void logits_epilogue(const Acc& acc, int V, int C, int m0, int n0,
-                                                int wm, int wn, int lane, float s,
-                                                floatx2* __restrict__ part,
-                                                float* __restrict__ rpart, int64_t ldp,
-                                                bf16* __restrict__ zbuf, int64_t ldz) {
+enum { kEpiMax = 0, kEpiRef = 1, kEpiLse = 2, kEpiNone = 3 };
+enum { kStoreNone = 0, kStoreExp = 1, kStoreRaw = 2 };
+
+struct LogitsArgs {
+  const bf16* W;        // [V, H]
+  const bf16* bias;     // [V] or nullptr
+  const bf16* h;        // gathered chunk rows [>= tokens, H]
+  int V, cmax, H;
+  float s;              // logit scale
+  const int* count;     // compacted row count (nullptr: cmax rows)
+  int64_t c0;           // first compacted row of the chunk
+  const int* rows;      // chunk row j -> batch row rows[c0 + j] (nullptr: c0 + j)
+  const int* gidx;      // kIndirect: GEMM token q -> chunk row gidx[q]
+  const int* gcount;    // kIndirect: number of listed rows
+  floatx2* part;        // [slabs, ldp]
+  float* rpart;         // [slabs, ldp] or nullptr
+  int64_t ldp;
+  bf16* E;              // [rows, ldE] or nullptr
+  int64_t ldE;
+  const float* ref;     // kEpiRef / kEpiLse: per batch row
+  const int* tcol;      // kEpiLse: target column per chunk row (-1: none)
+  float tsub;           // kEpiLse: subtracted at the target column
+  int group_m;
+};
+
+template <int kEpi, int kStore, bool kFull>
+__device__ __forceinline__ void logits_epilogue(Acc& acc, const LogitsArgs& a, int C, int m0,
+                                                int n0, int wm, int wn, int lane,
+                                                const int (&jrow)[kTN], const float (&rl2)[kTN],
+                                                const int (&tc)[kTN]) {
+  const int V = a.V;
+  const float s = a.s, sl = s * kLog2e;
   const int vbase = m0 + wm * kTM * 16;
   auto in_v = [&](int i, int r) { return kFull || m0 + acc_row(wm, i, lane, r) < V; };
-  if (kPart) {
-    const float sl = s * kLog2e;
+  if constexpr (kEpi == kEpiMax || kEpi == kEpiRef) {
     float mx[kTN], sum[kTN], rs[kTN];
+    if constexpr (kEpi == kEpiMax) {
 #pragma unroll
-    for (int j = 0; j < kTN; ++j) {
-      mx[j] = -INFINITY;
+      for (int j = 0; j < kTN; ++j) {
+        mx[j] = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < kTM; ++i)
+        for (int i = 0; i < kTM; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (in_v(i, r)) mx[j] = fmaxf(mx[j], acc[i][j][r]);
-    }
+          for (int r = 0; r < 4; ++r)
+            if (in_v(i, r)) mx[j] = fmaxf(mx[j], acc[i][j][r]);
+      }
 #pragma unroll
-    for (int j = 0; j < kTN; ++j) {
-      mx[j] = fmaxf(mx[j], __shfl_xor(mx[j], 16, 64));
-      mx[j] = fmaxf(mx[j], __shfl_xor(mx[j], 32, 64));
-    }
+      for (int j = 0; j < kTN; ++j) {
+        mx[j] = fmaxf(mx[j], __shfl_xor(mx[j], 16, 64));
+        mx[j] = fmaxf(mx[j], __shfl_xor(mx[j], 32, 64));
+      }
 #pragma unroll
-    for (int j = 0; j < kTN; ++j) {
-      const float off = mx[j] * sl;
-      sum[j] = 0.f;
-      rs[j] = 0.f;
+      for (int j = 0; j < kTN; ++j) {
+        const float off = mx[j] * sl;
+        sum[j] = 0.f;
+        rs[j] = 0.f;
 #pragma unroll
-      for (int i = 0; i < kTM; ++i)
+        for (int i = 0; i < kTM; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (in_v(i, r)) {
-            sum[j] += fast_exp2(__builtin_fmaf(acc[i][j][r], sl, -off));
-            if (rpart != nullptr) rs[j] += acc[i][j][r];
+          for (int r = 0; r < 4; ++r)
+            if (in_v(i, r)) {
+              sum[j] += fast_exp2(__builtin_fmaf(acc[i][j][r], sl, -off));
+              if (a.rpart != nullptr) rs[j] += acc[i][j][r];
+            }
+      }
+    } else {  // kEpiRef: e = 2^((z - r) log2 e), replacing the accumulator with kStoreExp
+#pragma unroll
+      for (int j = 0; j < kTN; ++j) {
+        sum[j] = 0.f;
+        rs[j] = 0.f;
+#pragma unroll
+        for (int i = 0; i < kTM; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float e = fast_exp2(__builtin_fmaf(acc[i][j][r], sl, -rl2[j]));
+            if (in_v(i, r)) {
+              if (a.rpart != nullptr) rs[j] += acc[i][j][r];
+              sum[j] += e;
+            }
+            if constexpr (kStore == kStoreExp) acc[i][j][r] = e;
           }
+      }
     }
 #pragma unroll
     for (int j = 0; j < kTN; ++j) {
       sum[j] += __shfl_xor(sum[j], 16, 64);
       sum[j] += __shfl_xor(sum[j], 32, 64);
-      if (rpart != nullptr) {
+      if (a.rpart != nullptr) {
         rs[j] += __shfl_xor(rs[j], 16, 64);
         rs[j] += __shfl_xor(rs[j], 32, 64);
       }
@@ -358,73 +417,73 @@ __device__ __forceinline__ void logits_epilogue(const Acc& acc, int V, int C, in
       for (int j = 0; j < kTN; ++j) {
         const int tok = n0 + acc_col(wn, j, lane);
         if (tok < C) {
-          part[(int64_t)(vbase / 128) * ldp + tok] = floatx2{mx[j] * s, sum[j]};
-          if (rpart != nullptr) rpart[(int64_t)(vbase / 128) * ldp + tok] = rs[j] * s;  // sum z
+          const int64_t o = (int64_t)(vbase / 128) * a.ldp + jrow[j];
+          a.part[o] = kEpi == kEpiMax ? floatx2{mx[j] * s, sum[j]} : floatx2{sum[j], sum[j]};
+          if (a.rpart != nullptr) a.rpart[o] = rs[j] * s;  // sum of z over the slab
         }
       }
     }
+  } else if constexpr (kEpi == kEpiLse) {  // e = exp(z - lse), the target column minus tsub
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+      for (int j = 0; j < kTN; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float e = fast_exp2(__builtin_fmaf(acc[i][j][r], sl, -rl2[j]));
+          if (m0 + acc_row(wm, i, lane, r) == tc[j]) e -= a.tsub;
+          acc[i][j][r] = e;
+        }
   }
-  if (kStoreZ) {
-    // blocked layout: zblk(tok, v) = ((tok / 16) * (ldz / 4) + v / 4) * 64 + (tok % 16) * 4 + v % 4,
-    // so one store instruction (16 tokens x 16 vocabulary) writes 512 contiguous bytes
+  if constexpr (kStore != kStoreNone) {
+    // a lane holds 4 consecutive vocabulary entries of a token: one 8-byte
+    // store; 16 lanes write 16 tokens' rows, the next sub-tile continues them
 #pragma unroll
     for (int j = 0; j < kTN; ++j) {
       const int tok = n0 + acc_col(wn, j, lane);
       if (tok >= C) continue;
-      bf16* zt = zbuf + ((int64_t)(tok >> 4) * (ldz >> 2)) * 64 + (tok & 15) * 4;
+      bf16* er = a.E + (int64_t)jrow[j] * a.ldE;
 #pragma unroll
       for (int i = 0; i < kTM; ++i) {
         const int row0 = m0 + acc_row(wm, i, lane, 0);
         bf16x4 v;
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = (bf16)acc[i][j][r];
-        bf16* dst = zt + (int64_t)(row0 >> 2) * 64;
         if (kFull || row0 + 3 < V) {
-          __builtin_nontemporal_store(v, (bf16x4*)dst);  // read once, by dlogits
-        } else {
+          __builtin_nontemporal_store(v, (bf16x4*)(er + row0));  // read back by the backward GEMMs
+        } else if (row0 < a.ldE) {  // the padding columns V .. ldE - 1 are zero
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (row0 + r < V) dst[r] = v[r];
+          for (int r = 0; r < 4; ++r) er[row0 + r] = row0 + r < V ? v[r] : (bf16)0.f;
         }
       }
     }
   }
 }
 
-template <bool kStoreZ, bool kPart>
-__global__ __launch_bounds__(kGemmThreads, 1) void k_logits_bf16(
-    const bf16* __restrict__ W, const bf16* __restrict__ bias, const bf16* __restrict__ h, int V,
-    int cmax, int H, float s, const int* __restrict__ rows, const int* __restrict__ count,
-    int64_t c0, floatx2* __restrict__ part, float* __restrict__ rpart, int64_t ldp,
-    bf16* __restrict__ zbuf, int64_t ldz, int group_m) {
-  extern __shared__ __attribute__((aligned(1024))) char smem[];
-  int C = cmax;
-  if (count != nullptr) {
-    const int64_t n = (int64_t)*count - c0;
-    C = n < 0 ? 0 : (n < cmax ? (int)n : cmax);
-  }
-  const TileCoord tc = tile_coord((int)cdiv(V, kBM), (int)cdiv(C, kBN), 1, group_m);
-  if (!tc.active) return;
-  const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
+// One 256 x 256 logits tile (vocabulary tile tm, token tile tn) with its epilogue.
+template <int kEpi, int kStore, bool kIndirect>
+__device__ __forceinline__ void logits_tile(const LogitsArgs& a, int C, int tm, int tn,
+                                            char* smem) {
+  const int m0 = tm * kBM, n0 = tn * kBN;
   Acc acc;
-  gemm_mainloop<false, false>(W, H, V, 0, m0, h, H, C, 0, n0, 0, H / kBK, smem, acc, rows,
-                              rows != nullptr ? c0 : 0);
+  gemm_mainloop<false, false>(a.W, a.H, a.V, 0, m0, a.h, a.H, C, 0, n0, 0, a.H / kBK, smem, acc,
+                              kIndirect ? a.gidx : nullptr, 0);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN;
   const int vbase = m0 + wm * kTM * 16;
-  if (vbase >= V) return;
-  const bool full = vbase + kTM * 16 <= V;
-  if (bias != nullptr) {  // F.linear's bias, before the logit scale
+  if (vbase >= a.V) return;
+  const bool full = vbase + kTM * 16 <= a.V;
+  if (a.bias != nullptr) {  // F.linear's bias, before the logit scale
     bf16x4 bv[kTM];  // rows row0 .. row0 + 3 of sub-tile i (row0 % 4 == 0): one 8-byte load
 #pragma unroll
     for (int i = 0; i < kTM; ++i) {
       const int row0 = m0 + acc_row(wm, i, lane, 0);
-      if (row0 + 3 < V) {
-        bv[i] = *(const bf16x4*)(bias + row0);
+      if (row0 + 3 < a.V) {
+        bv[i] = *(const bf16x4*)(a.bias + row0);
       } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) bv[i][r] = row0 + r < V ? bias[row0 + r] : (bf16)0.f;
+        for (int r = 0; r < 4; ++r) bv[i][r] = row0 + r < a.V ? a.bias[row0 + r] : (bf16)0.f;
       }
     }
 #pragma unroll
@@ -436,36 +495,83 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_logits_bf16(
         for (int j = 0; j < kTN; ++j) acc[i][j][r] += b;
       }
   }
+  // the lane's 4 tokens: chunk rows, reference (log2 units) and target column
+  int jrow[kTN], tc[kTN];
+  float rl2[kTN];
+#pragma unroll
+  for (int j = 0; j < kTN; ++j) {
+    const int q = min(n0 + acc_col(wn, j, lane), C - 1);
+    jrow[j] = kIndirect ? a.gidx[q] : q;
+    rl2[j] = 0.f;
+    tc[j] = -1;
+    if constexpr (kEpi == kEpiRef || kEpi == kEpiLse) {
+      const int64_t i = a.rows != nullptr ? (int64_t)a.rows[a.c0 + jrow[j]] : a.c0 + jrow[j];
+      rl2[j] = a.ref[i] * kLog2e;
+    }
+    if constexpr (kEpi == kEpiLse) tc[j] = a.tcol[jrow[j]];
+  }
   if (full)
-    logits_epilogue<kStoreZ, kPart, true>(acc, V, C, m0, n0, wm, wn, lane, s, part, rpart, ldp, zbuf,
-                                          ldz);
+    logits_epilogue<kEpi, kStore, true>(acc, a, C, m0, n0, wm, wn, lane, jrow, rl2, tc);
   else
-    logits_epilogue<kStoreZ, kPart, false>(acc, V, C, m0, n0, wm, wn, lane, s, part, rpart, ldp,
-                                           zbuf, ldz);
+    logits_epilogue<kEpi, kStore, false>(acc, a, C, m0, n0, wm, wn, lane, jrow, rl2, tc);
+}
+
+template <int kEpi, int kStore, bool kIndirect>
+__global__ __launch_bounds__(kGemmThreads, 1) void k_logits_bf16(const LogitsArgs a) {
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  int C;
+  if constexpr (kIndirect) {
+    C = min(*a.gcount, a.cmax);
+  } else {
+    C = a.cmax;
+    if (a.count != nullptr) {
+      const int64_t n = (int64_t)*a.count - a.c0;
+      C = n < 0 ? 0 : (n < a.cmax ? (int)n : a.cmax);
+    }
+  }
+  const int tiles_v = (int)cdiv(a.V, kBM), tiles_t = (int)cdiv(C, kBN);
+  if constexpr (!kIndirect) {
+    const TileCoord tc = tile_coord(tiles_v, tiles_t, 1, a.group_m);
+    if (!tc.active) return;
+    logits_tile<kEpi, kStore, false>(a, C, tc.tm, tc.tn, smem);
+  } else {
+    for (int item = blockIdx.x; item < tiles_v * tiles_t; item += gridDim.x) {
+      logits_tile<kEpi, kStore, true>(a, C, item % tiles_v, item / tiles_v, smem);
+      __syncthreads();  // every wave is done with the LDS stages before the next tile's loads
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
-// dH = g W, split over K = vocabulary: out[split][m][n] (fp32, m < the rows
-// that exist) for this split's K tiles.  A = g [M = C tokens, ldg] (K contiguous); B = W read as
-// K rows (vocabulary rows of W [V, H], transposed in LDS).  Rows of W past
-// V are clamped: g is zero in those columns.
-// ---------------------------------------------------------------------------
-// M = chunk tokens: the grid covers M (upper bound) x max_splits; the tokens
-// that exist are min(*count - c0, M) when count != nullptr, and the split
+// dH, split over K = vocabulary: out[split][m][n] (fp32, m < the rows that
+// exist) = sum_v E[m, v] W[v, n] over this split's K tiles.  A = E [M = chunk
+// rows, ldE] (K contiguous): the stored exp(z - r) with the target entry
+// patched, so that alpha_m E[m, :] is the row's gradient g without its
+// smoothing term; B = W read as K rows (vocabulary rows of W [V, H],
+// transposed in LDS).  Rows of W past V are clamped: E is zero in those
+// columns.
+//
+// M = chunk rows: the grid covers M + extra (upper bound) x max_splits; the
+// rows that exist are min(*count - c0, M) (+ extra: the all-ones row after
+// them, whose product is sum_v W_v for the smoothing term), and the split
 // count is chosen for them (choose_splits; k_splitk_scatter recomputes it).
-// With a single split there is nothing to reduce: the epilogue writes row m
-// straight to row rows[c0 + m] of dst (fp32 when dst_f32, else bf16) and the
-// reduction kernel returns at once.
+// With a single split and no extra row there is nothing to reduce: the
+// epilogue writes alpha_m times row m straight to row rows[c0 + m] of dst
+// (fp32 when dst_f32, else bf16) and the reduction kernel returns at once.
+// ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dh_bf16(
-    const bf16* __restrict__ g, int64_t ldg, int M, const int* __restrict__ count, int64_t c0,
-    const bf16* __restrict__ W, int V, int H, int k_tiles, int max_splits, float* __restrict__ out,
-    int group_m, void* __restrict__ dst, int dst_f32, const int* __restrict__ rows) {
+    const bf16* __restrict__ E, int64_t ldE, int M, int extra, const int* __restrict__ count,
+    int64_t c0, const bf16* __restrict__ W, int V, int H, int k_tiles, int max_splits,
+    float* __restrict__ out, int group_m, void* __restrict__ dst, int dst_f32,
+    const int* __restrict__ rows, const float* __restrict__ alpha) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   int Me = M;
   if (count != nullptr) {
     const int64_t n = (int64_t)*count - c0;
     Me = n < 0 ? 0 : (n < M ? (int)n : M);
   }
+  const int Mr = Me;  // real rows
+  Me += extra;
   const int splits = choose_splits(cdiv(Me, kBM) * cdiv(H, kBN), k_tiles, max_splits);
   const TileCoord tc = tile_coord((int)cdiv(Me, kBM), (int)cdiv(H, kBN), splits, group_m);
   if (!tc.active) return;
@@ -473,24 +579,25 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dh_bf16(
   const int kt0 = (int)((int64_t)k_tiles * tc.split / splits);
   const int kt1 = (int)((int64_t)k_tiles * (tc.split + 1) / splits);
   Acc acc;
-  gemm_mainloop<false, true>(g, ldg, Me, 0, m0, W, H, V, H, n0, kt0, kt1 - kt0, smem, acc);
+  gemm_mainloop<false, true>(E, ldE, Me, 0, m0, W, H, V, H, n0, kt0, kt1 - kt0, smem, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN;
-  if (splits == 1) {  // nothing to reduce: rows go straight to their place in dH
+  if (splits == 1 && extra == 0) {  // nothing to reduce: rows go straight to their place in dH
 #pragma unroll
     for (int i = 0; i < kTM; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = m0 + acc_row(wm, i, lane, r);
-        if (row >= Me) continue;
+        if (row >= Mr) continue;
         const int64_t drow = (int64_t)rows[c0 + row] * H;
+        const float al = alpha[row];
 #pragma unroll
         for (int j = 0; j < kTN; ++j) {
           const int col = n0 + acc_col(wn, j, lane);
           if (col >= H) continue;
-          if (dst_f32) static_cast<float*>(dst)[drow + col] = acc[i][j][r];
-          else static_cast<bf16*>(dst)[drow + col] = (bf16)acc[i][j][r];
+          if (dst_f32) static_cast<float*>(dst)[drow + col] = al * acc[i][j][r];
+          else static_cast<bf16*>(dst)[drow + col] = (bf16)(al * acc[i][j][r]);
         }
       }
     return;
@@ -511,28 +618,38 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dh_bf16(
 
 // ---------------------------------------------------------------------------
 // dW = g^T h over K = the chunk's tokens, computed as its transpose
-// dW^T = h^T g: A = h^T [H, ldh] with the chunk's tokens contiguous (a
-// 2 * H * Kp byte copy made per chunk), B = g [Kp token rows, ldg] read as
-// K rows (vocabulary columns, transposed in LDS).  In this order the
+// dW^T = (alpha h)^T E: A = (alpha h)^T [H, ldh] with the chunk's tokens
+// contiguous (each token's row of h times its alpha, a 2 * H * Kp byte copy
+// made per chunk), B = E [Kp token rows, ldE] read as K rows (vocabulary
+// columns, transposed in LDS): alpha_t E[t, v] is g[t, v] without its
+// smoothing term, which is the same for every vocabulary row,
+// -(eps / V) sum_t c_t h_t = -epsV * usum, and is subtracted from the
+// final value (modes 0 and 3) when usum != nullptr.  In this order the
 // transposed operand is the one with 4 fragments per wave rather than 8 (16
 // LDS reads per 32-wide K step instead of 20: main loop 2.62 against
 // 2.72 ms at the 4B-scale shape).  Tiles are still numbered over (vocabulary
 // tile, H tile), so the order, and what the L2 shares, are unchanged; the
 // accumulators hold the tile transposed (rows = H, columns = vocabulary),
-// and the epilogue transposes it back through LDS.  g rows and h^T columns
-// C..Kp-1 are zero.
+// and the epilogue transposes it back through LDS.  h^T columns C..Kp-1 are
+// zero (E rows there are finite).
 // kMode 0: out (bf16) = acc                      (single chunk)
 // kMode 1: acc32 = acc                           (first of several chunks)
 // kMode 2: acc32 += acc                          (middle chunk)
 // kMode 3: out (bf16) = acc32 + acc              (last chunk)
+// acc32 keeps each tile in the accumulators' own register layout (tile,
+// then sub-tile (i, j), then thread, 4 floats each), so a thread reads and
+// writes its 128 values as 32 coalesced 16-byte pieces.  Modes 2 and 3
+// load them into the accumulators before the main loop, which then adds
+// this chunk's products on top (the loads overlap the first operand
+// loads); modes 1 and 2 end with plain stores.
 // ---------------------------------------------------------------------------
 // The chunk's tokens: Kp = the padded count (multiple of 64), or, when
 // count != nullptr, min(*count - c0, cmax) rounded up to 64.
 template <int kMode>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dw_bf16(
-    const bf16* __restrict__ g, int64_t ldg, int cmax, const int* __restrict__ count, int64_t c0,
+    const bf16* __restrict__ E, int64_t ldE, int cmax, const int* __restrict__ count, int64_t c0,
     int V, const bf16* __restrict__ hT, int64_t ldh, int H, bf16* __restrict__ out,
-    float* __restrict__ acc32, int group_m) {
+    float* __restrict__ acc32, int group_m, const float* __restrict__ usum, float epsV) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const TileCoord tc = tile_coord((int)cdiv(V, kBM), (int)cdiv(H, kBN), 1, group_m);
   if (!tc.active) return;
@@ -544,12 +661,30 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dw_bf16(
   }
   const int Kp = (int)round_up(Ce, kBK);
   Acc acc;  // acc[i][j][r] = dW[v0 + acc_col(wn, j)][h0 + acc_row(wm, i, r)]
-  gemm_mainloop<false, true>(hT, ldh, H, 0, h0, g, ldg, max(Kp, 1), (int)ldg, v0, 0, Kp / kBK, smem,
-                             acc);
+  floatx4* t32 = reinterpret_cast<floatx4*>(acc32) +
+                 ((int64_t)tc.tm * cdiv(H, kBN) + tc.tn) * (kTM * kTN * kGemmThreads) + threadIdx.x;
+  if constexpr (kMode >= 2) {
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+      for (int j = 0; j < kTN; ++j) acc[i][j] = __builtin_nontemporal_load(t32 + (i * kTN + j) * kGemmThreads);
+    gemm_mainloop<false, true, false>(hT, ldh, H, 0, h0, E, ldE, max(Kp, 1), (int)ldE, v0, 0,
+                                      Kp / kBK, smem, acc);
+  } else {
+    gemm_mainloop<false, true>(hT, ldh, H, 0, h0, E, ldE, max(Kp, 1), (int)ldE, v0, 0, Kp / kBK,
+                               smem, acc);
+  }
+  if constexpr (kMode == 1 || kMode == 2) {  // carried to the next chunk in fp32
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+      for (int j = 0; j < kTN; ++j) __builtin_nontemporal_store(acc[i][j], t32 + (i * kTN + j) * kGemmThreads);
+    return;
+  }
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN;
-  if constexpr (kMode == 0) {
+  {
     // Stage the bf16 tile in LDS as [vocabulary][H] (free after the main
     // loop) and write it out as 512-byte rows.  A lane holds 4 consecutive H
     // of one vocabulary row per sub-tile: one 8-byte write.  16-byte chunk
@@ -563,9 +698,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dw_bf16(
 #pragma unroll
       for (int j = 0; j < kTN; ++j) {
         const int vl = acc_col(wn, j, lane), hl = acc_row(wm, i, lane, 0);
+        floatx4 corr = floatx4{};  // the smoothing term, the same for every vocabulary row
+        if (usum != nullptr) corr = epsV * *(const floatx4*)(usum + h0 + hl);
         bf16x4 w;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) w[r] = (bf16)acc[i][j][r];
+        for (int r = 0; r < 4; ++r) w[r] = (bf16)(acc[i][j][r] - corr[r]);
         *(bf16x4*)&stg[vl * kBN + ((((hl >> 3) ^ (vl & 15)) << 3) | (hl & 7))] = w;
       }
     __syncthreads();
@@ -579,47 +716,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dw_bf16(
                                     (bf16x8*)(out + (int64_t)row * H + col));
     }
     return;
-  }
-  // Modes 1-3: the fp32 tile goes through LDS in two halves of 128
-  // vocabulary rows (128 KB each; the waves with wn = 2 * half, 2 * half + 1
-  // hold them), so the accesses to acc32 (and out) are 16-byte pieces of
-  // whole 1-KB rows.  A lane writes 4 consecutive H (16 bytes) of one row;
-  // 16-byte chunk ch of staged row r sits at ch ^ (r & 15).
-  float* stg = reinterpret_cast<float*>(smem);  // [128][256]
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    __syncthreads();  // the operand stages, or the previous half, are no longer read
-    if ((wn >> 1) == half) {
-#pragma unroll
-      for (int i = 0; i < kTM; ++i)
-#pragma unroll
-        for (int j = 0; j < kTN; ++j) {
-          const int vl = acc_col(wn, j, lane) - half * (kBM / 2), hl = acc_row(wm, i, lane, 0);
-          *(floatx4*)&stg[vl * kBN + (((hl >> 2) ^ (vl & 15)) << 2)] = acc[i][j];
-        }
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int p = 0; p < kBM / 2 * kBN / 4 / kGemmThreads; ++p) {
-      const int u = threadIdx.x + kGemmThreads * p;
-      const int rl = u / (kBN / 4), ch = u % (kBN / 4);
-      const int row = v0 + half * (kBM / 2) + rl, col = h0 + ch * 4;
-      if (row < V && col < H) {  // H % 64 == 0: a piece is wholly in or out
-        const floatx4 v = *(const floatx4*)&stg[rl * kBN + ((ch ^ (rl & 15)) << 2)];
-        floatx4* a32 = (floatx4*)(acc32 + (int64_t)row * H + col);
-        if constexpr (kMode == 1) {
-          *a32 = v;
-        } else if constexpr (kMode == 2) {
-          *a32 = *a32 + v;
-        } else {
-          const floatx4 t = *a32 + v;
-          bf16x4 o;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = (bf16)t[e];
-          *(bf16x4*)(out + (int64_t)row * H + col) = o;
-        }
-      }
-    }
   }
 }
 

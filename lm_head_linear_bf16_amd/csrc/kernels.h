@@ -41,17 +41,20 @@ __global__ __launch_bounds__(1024) void k_divisor(const int64_t* __restrict__ ta
 // consecutive rows per pass and a block-wide prefix sum gives their
 // positions, so the order (and everything after it) is deterministic.
 // In the same pass, when the pointers are not null: the divisor D as
-// k_divisor computes it (the count is the number of non-ignored rows), and
+// k_divisor computes it (the count is the number of non-ignored rows),
 // a[i] = va, b[i] = vb, c[i] = vc on ignored rows (outputs no later kernel
-// writes for them).
+// writes for them), and zeros[0 .. nzeros) = 0 (the per-chunk counters of
+// flagged rows).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void k_prep_rows(const int64_t* __restrict__ target, int64_t N,
                                                     int64_t ignore, int* __restrict__ rows,
                                                     int* __restrict__ count, int reduction,
                                                     int64_t total, float* __restrict__ D, float* a,
                                                     float va, float* b, float vb, float* c,
-                                                    float vc) {
+                                                    float vc, int* zeros = nullptr,
+                                                    int nzeros = 0) {
   __shared__ int wtot[16];
+  for (int k = threadIdx.x; k < nzeros; k += 1024) zeros[k] = 0;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int base = 0;
   for (int64_t s0 = 0; s0 < N; s0 += 4096) {
@@ -330,91 +333,144 @@ __global__ __launch_bounds__(64) void k_row_partials_f32(const float* __restrict
 //
 // R_i (the row sum of the logits) is R[i] when R != nullptr, else the sum of
 // rpart over the slabs when rpart != nullptr (fixed order), else 0.
-// mode 0 (loss):  lse_i = M + log S, and with p_i, D, eps:
+// mode 0 (max-shifted partials (m, S)): lse_i = M + log S, then the loss:
 //     l_i   = w_i [(1-eps)(lse_i - zt_i) + eps(lse_i - R_i / Vg)] / p_i   (0 if ignored)
 //     coef_i = w_i s / (p_i D)                                            (0 if ignored)
-//   (page 1, cross_entropy_kernel steps 4 and the label-smoothing combine;
+//   (page 1, cross_entropy_kernel step 4 and the label-smoothing combine;
 //    the whole smoothed CE is divided by p_i).  w_i = eob_w on rows whose
 //   target is the end-of-block token eob >= 0 (the module's forward divides
-//   their p_mask by the weight), else 1.  Writes lse[i], rloss[i], coef[i]
-//   (chunk-local).
+//   their p_mask by the weight), else 1.  alpha_i = coef_i.
 // mode 1 (shard): writes out_m[i] = M, out_s[i] = S (sum relative to M) and,
-// when out_r != nullptr, out_r[i] = R_i.
+//   when out_r != nullptr, out_r[i] = R_i.
+// mode 2 (partials (S_t, S_t) relative to the reference r_i = zt_i, S_t =
+//   sum over slab t of exp(z - r)): a row with some S_t > kRefSumMax is
+//   appended to flag_list (flag_count counts them) and nothing else is
+//   written for it; otherwise S = sum_t S_t, lse_i = r_i + log S,
+//   the loss and coef_i as in mode 0, alpha_i = coef_i / S (so alpha_i e_v =
+//   coef_i softmax_v) and the stored E[j, y_i - v0] (= e at the target) is
+//   replaced by e - (1 - eps) S, which puts the target term of the gradient
+//   into E (page 1, cross_entropy_kernel step 6).
 // ---------------------------------------------------------------------------
 //
 // Rows: chunk row j (< the chunk's row count) is row i = rows[c0 + j] of the
-// batch when rows != nullptr (compacted chunk), else i = c0 + j.  Per-row
-// inputs and the lse / rloss / out_* outputs use i; coef_out, lsec and tcol
-// (when not null) use j: the chunk's coefficient, lse and target column
-// (target - v0, or -1 for an ignored row).
-__global__ __launch_bounds__(256) void k_combine_rows(
-    const floatx2* __restrict__ part, const float* __restrict__ rpart, int64_t ldp, int64_t nT,
-    int64_t cmax, const int* __restrict__ rows, const int* __restrict__ count, int64_t c0,
-    int mode, const int64_t* __restrict__ target, const float* __restrict__ p_mask,
-    int64_t ignore, const float* __restrict__ zt, const float* __restrict__ R, float eps, float Vg,
-    float s, const float* __restrict__ D, int64_t eob, float eob_w, float* __restrict__ lse_out,
-    float* __restrict__ rloss_out, float* __restrict__ coef_out, float* __restrict__ lsec,
-    int* __restrict__ tcol, int64_t v0, float* __restrict__ out_m, float* __restrict__ out_s,
-    float* __restrict__ out_r) {
+// batch when rows != nullptr (compacted chunk), else i = c0 + j; with jlist
+// the rows combined are the chunk rows jlist[q], q < *jcount.  Per-row inputs
+// and the lse / rloss / out_* outputs use i; coef_out, alpha_out and tcol
+// (when not null) use j: the chunk's coefficient, gradient scale and target
+// column (target - v0, or -1 for an ignored row).
+struct CombineArgs {
+  const floatx2* part;
+  const float* rpart;
+  int64_t ldp, nT, cmax;
+  const int* rows;
+  const int* count;
+  int64_t c0;
+  const int* jlist;
+  const int* jcount;
+  int mode;
+  const int64_t* target;
+  const float* p_mask;
+  int64_t ignore;
+  const float* zt;
+  const float* R;
+  float eps, Vg, s;
+  const float* D;
+  int64_t eob;
+  float eob_w;
+  float* lse_out;
+  float* rloss_out;
+  float* coef_out;
+  float* alpha_out;
+  int* tcol;
+  int64_t v0;
+  bf16* E;
+  int64_t ldE;
+  int* flag_count;
+  int* flag_list;
+  float* out_m;
+  float* out_s;
+  float* out_r;
+};
+
+__global__ __launch_bounds__(256) void k_combine_rows(const CombineArgs a) {
   __shared__ float sm[8][32], ss[8][32], sr[8][32];
   const int tx = threadIdx.x & 31, grp = threadIdx.x >> 5;
-  const int64_t C = chunk_rows(count, c0, cmax);
-  const int64_t j = (int64_t)blockIdx.x * 32 + tx;
+  const int64_t C = a.jlist != nullptr ? (int64_t)*a.jcount : chunk_rows(a.count, a.c0, a.cmax);
+  const int64_t q = (int64_t)blockIdx.x * 32 + tx;
+  const int64_t j = q < C ? (a.jlist != nullptr ? (int64_t)a.jlist[q] : q) : 0;
+  const bool ref = a.mode == 2;
   float m = -INFINITY, sum = 0.f, rsum = 0.f;
-  if (j < C) {
+  auto merge = [&](float m2, float s2) {
+    if (ref) {
+      m = fmaxf(m, m2);
+      sum += s2;
+    } else {
+      lse_merge(m, sum, m2, s2);
+    }
+  };
+  if (q < C) {
     // slabs grp, grp + 8, ... in order; eight loads in flight per batch
     int64_t t = grp;
-    for (; t + 56 < nT; t += 64) {
+    for (; t + 56 < a.nT; t += 64) {
       floatx2 pv[8];
       float rv[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        pv[u] = part[(t + 8 * u) * ldp + j];
-        rv[u] = rpart != nullptr ? rpart[(t + 8 * u) * ldp + j] : 0.f;
+        pv[u] = a.part[(t + 8 * u) * a.ldp + j];
+        rv[u] = a.rpart != nullptr ? a.rpart[(t + 8 * u) * a.ldp + j] : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        lse_merge(m, sum, pv[u][0], pv[u][1]);
+        merge(pv[u][0], pv[u][1]);
         rsum += rv[u];
       }
     }
-    for (; t < nT; t += 8) {
-      const floatx2 pv = part[t * ldp + j];
-      lse_merge(m, sum, pv[0], pv[1]);
-      if (rpart != nullptr) rsum += rpart[t * ldp + j];
+    for (; t < a.nT; t += 8) {
+      const floatx2 pv = a.part[t * a.ldp + j];
+      merge(pv[0], pv[1]);
+      if (a.rpart != nullptr) rsum += a.rpart[t * a.ldp + j];
     }
   }
   sm[grp][tx] = m;
   ss[grp][tx] = sum;
   sr[grp][tx] = rsum;
   __syncthreads();
-  if (grp != 0 || j >= C) return;
+  if (grp != 0 || q >= C) return;
   for (int g = 1; g < 8; ++g) {
-    lse_merge(m, sum, sm[g][tx], ss[g][tx]);
+    merge(sm[g][tx], ss[g][tx]);
     rsum += sr[g][tx];
   }
-  const int64_t i = rows != nullptr ? (int64_t)rows[c0 + j] : c0 + j;
-  if (mode == 1) {
-    out_m[i] = m;
-    out_s[i] = sum;
-    if (out_r != nullptr) out_r[i] = rsum;
+  const int64_t i = a.rows != nullptr ? (int64_t)a.rows[a.c0 + j] : a.c0 + j;
+  if (a.mode == 1) {
+    a.out_m[i] = m;
+    a.out_s[i] = sum;
+    if (a.out_r != nullptr) a.out_r[i] = rsum;
     return;
   }
-  const float lse = m + logf(sum);
-  const bool valid = target[i] != ignore;
-  const float p = (p_mask != nullptr && valid) ? p_mask[i] : 1.f;
+  if (ref && !(m <= kRefSumMax)) {  // the reference is too far below the row's maximum
+    a.flag_list[atomicAdd(a.flag_count, 1)] = (int)j;
+    return;
+  }
+  const float lse = ref ? a.zt[i] + logf(sum) : m + logf(sum);
+  const bool valid = a.target[i] != a.ignore;
+  const float p = (a.p_mask != nullptr && valid) ? a.p_mask[i] : 1.f;
   float l = 0.f, cf = 0.f;
   if (valid) {
-    const float rs = (R != nullptr) ? R[i] : rsum;
-    const float wt = (eob >= 0 && target[i] == eob) ? eob_w : 1.f;
-    l = wt * (((1.f - eps) * (lse - zt[i]) + eps * (lse - rs / Vg)) / p);
-    cf = wt * (s / (p * D[0]));
+    const float rs = (a.R != nullptr) ? a.R[i] : rsum;
+    const float wt = (a.eob >= 0 && a.target[i] == a.eob) ? a.eob_w : 1.f;
+    l = wt * (((1.f - a.eps) * (lse - a.zt[i]) + a.eps * (lse - rs / a.Vg)) / p);
+    cf = wt * (a.s / (p * a.D[0]));
   }
-  lse_out[i] = valid ? lse : 0.f;
-  rloss_out[i] = l;
-  if (coef_out != nullptr) coef_out[j] = cf;
-  if (lsec != nullptr) lsec[j] = lse;
-  if (tcol != nullptr) tcol[j] = valid ? (int)(target[i] - v0) : -1;
+  a.lse_out[i] = valid ? lse : 0.f;
+  a.rloss_out[i] = l;
+  const int64_t col = valid ? a.target[i] - a.v0 : -1;
+  if (a.coef_out != nullptr) a.coef_out[j] = cf;
+  if (a.alpha_out != nullptr) a.alpha_out[j] = ref ? cf / sum : cf;
+  if (a.tcol != nullptr) a.tcol[j] = (int)col;
+  if (ref && a.E != nullptr && valid) {
+    bf16* e = a.E + j * a.ldE + col;
+    *e = (bf16)((float)*e - (1.f - a.eps) * sum);
+  }
 }
 
 // coef_j = w_i s / (p_i D), 0 on ignored rows (shard backward, lse given;
@@ -527,129 +583,6 @@ __global__ __launch_bounds__(256) void k_gpass(T* __restrict__ z, int64_t ldz, i
   }
 }
 
-// ---------------------------------------------------------------------------
-// dlogits for the bf16 path (same formula as k_gpass), reading the unscaled
-// logits (z = zscale * stored value) from the blocked layout the logits GEMM
-// writes: element (token t, column v) at
-// ((t / 16) * (ldz / 4) + v / 4) * 64 + (t % 16) * 4 + v % 4, and writing g
-// row-major [rows, ldz] for both backward GEMMs.  Chunk rows are given by the
-// device-side count (chunk_rows); rows C .. round_up(C, 64) - 1 and columns
-// >= V are written as zeros.  lse, coef and tcol are per chunk row.  With
-// dbpart, block (x, y) also writes the column sums of its kGpassTok rows of g
-// (as stored, bf16) to dbpart[y * ldz + column], zeros for blocks past the
-// rows.
-//
-// One block = kGpassTok tokens (a multiple of 16 dividing 64) x kGpassCols
-// columns, 256 threads (16 x 1024 streams best; 64 x 256 when db is wanted,
-// so the column-sum partials cover 64 rows each).  Thread -> two fixed
-// tokens (their lse, coefficient and target stay in registers) and eight
-// 16-byte units of z (a wave reads 1 KB contiguous per step); g goes out
-// through LDS as row segments of 2 * kGpassCols bytes.  z is read once and g
-// is read by the next kernels from HBM anyway (1.4 GB each at the 4B-scale
-// sizes, far past the caches), so both use non-temporal accesses.
-// ---------------------------------------------------------------------------
-template <int kGpassTok, int kGpassCols>
-__global__ __launch_bounds__(256) void k_gpass_blk(const bf16* __restrict__ zblk, int64_t ldz,
-                                                   int64_t cmax, const int* __restrict__ count,
-                                                   int64_t c0, int64_t V,
-                                                   const float* __restrict__ lse,
-                                                   const float* __restrict__ coef,
-                                                   const int* __restrict__ tcol, float eps,
-                                                   float Vg, bf16* __restrict__ g,
-                                                   float* __restrict__ dbpart, float zscale) {
-  constexpr int kTG = kGpassTok / 16;      // 16-token groups of the blocked layout
-  constexpr int kVBO = 32 / kTG;           // column blocks a thread row covers per step
-  constexpr int kSteps = kGpassCols / 4 / kVBO;
-  constexpr int kUnits = kGpassCols / 8;   // 16-byte units per token row
-  static_assert(kGpassTok * kUnits == 256 * 8, "eight 16-byte output units per thread");
-  __shared__ bf16 tile[kGpassTok][kGpassCols + 8];  // [token][column]
-  const int tid = threadIdx.x;
-  const int64_t C = chunk_rows(count, c0, cmax);
-  const int64_t i0 = (int64_t)blockIdx.y * kGpassTok, j0 = (int64_t)blockIdx.x * kGpassCols;
-  const int64_t nvb = min((int64_t)kGpassCols / 4, (ldz - j0) / 4);  // column blocks in range
-  // dbpart (when not null): this block's column sums of g, row block y
-  float* dbrow = dbpart != nullptr ? dbpart + (int64_t)blockIdx.y * ldz + j0 : nullptr;
-  if (i0 >= round_up(C, 64)) {  // rows past the chunk's padded count are never read
-    if (dbrow != nullptr)
-      for (int col = tid; col < nvb * 4; col += 256) dbrow[col] = 0.f;
-    return;
-  }
-  const float epsV = eps / Vg;
-  const float zl2 = zscale * kLog2e;
-  const int tb = tid / (256 / kTG), vbo = (tid >> 3) % kVBO, w = tid & 7;
-  const int tl0 = tb * 16 + w * 2;  // tokens tl0, tl0 + 1 of the tile
-  float cf[2], l2[2], tg[2];
-  int64_t yc[2];
-  bool any = false;
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int64_t i = i0 + tl0 + q;
-    cf[q] = (i < C) ? coef[i] : 0.f;
-    l2[q] = (cf[q] != 0.f) ? lse[i] * kLog2e : 0.f;
-    yc[q] = (cf[q] != 0.f && tcol[i] >= 0) ? (int64_t)tcol[i] - j0 : -1;  // column within this tile
-    tg[q] = cf[q] * (1.f - eps);
-    any |= cf[q] != 0.f;
-  }
-  const bf16* zsrc = zblk + ((i0 / 16 + tb) * (ldz >> 2) + j0 / 4) * 64 + w * 8;
-  bf16x8 zin[kSteps];
-#pragma unroll
-  for (int p = 0; p < kSteps; ++p) {  // all loads in flight before any math
-    const int vb = vbo + kVBO * p;
-    zin[p] = (any && vb < nvb) ? __builtin_nontemporal_load((const bf16x8*)(zsrc + (int64_t)vb * 64)) : bf16x8{};
-  }
-  const bool inside = j0 + kGpassCols <= V;  // no column of this tile is past V
-  float ce[2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) ce[q] = cf[q] * epsV;
-#pragma unroll
-  for (int p = 0; p < kSteps; ++p) {
-    const int vb = vbo + kVBO * p;  // column block (4 columns) within the tile
-    bf16x4 out[2] = {bf16x4{}, bf16x4{}};
-    const bf16x8 zv = zin[p];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      if (cf[q] == 0.f) continue;  // ignored or padding row: stays +0
-      float v[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        v[e] = __builtin_fmaf(cf[q], fast_exp2(__builtin_fmaf((float)zv[q * 4 + e], zl2, -l2[q])),
-                              -ce[q]);
-      const int64_t d = yc[q] - vb * 4;  // the target column, when it is in this block
-      if (d >= 0 && d < 4) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (e == d) v[e] -= tg[q];
-      }
-      if (!inside) {  // after the target: a shard's out-of-range target column may fall here
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (j0 + vb * 4 + e >= V) v[e] = 0.f;
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) out[q][e] = (bf16)v[e];
-    }
-    if (vb < nvb) {
-#pragma unroll
-      for (int q = 0; q < 2; ++q) *(bf16x4*)&tile[tl0 + q][vb * 4] = out[q];
-    }
-  }
-  __syncthreads();
-  if (dbrow != nullptr)  // page 1: db += c_logits.sum(0)
-    for (int col = tid; col < nvb * 4; col += 256) {
-      float acc = 0.f;
-#pragma unroll 8
-      for (int r = 0; r < kGpassTok; ++r) acc += (float)tile[r][col];
-      dbrow[col] = acc;
-    }
-  const int units = (int)nvb / 2;  // 16-byte units per token row in range
-#pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const int unit = tid + 256 * p;
-    const int r = unit / kUnits, c = unit % kUnits;
-    if (c < units) __builtin_nontemporal_store(*(const bf16x8*)&tile[r][c * 8], (bf16x8*)(g + (i0 + r) * ldz + j0 + c * 8));
-  }
-}
-
 // fp32 path: z[i, j] += s * b[j] for i < C, j < V (the bias of F.linear,
 // before the logit scale).
 __global__ __launch_bounds__(256) void k_add_bias_f32(float* __restrict__ z, int64_t ldz, int64_t C,
@@ -683,37 +616,212 @@ __global__ __launch_bounds__(256) void k_scale_grad(const float* __restrict__ gr
   }
 }
 
-// dH rows of a compacted chunk: out[rows[c0 + j], :] = sum_s part[s][j][:]
-// (s ascending) for j < the chunk's row count; S = choose_splits for that
-// count, exactly as the dH GEMM chose it.
+// dH rows of a compacted chunk: out[rows[c0 + j], :] = alpha_j P_j - coef_j
+// epsV P_C for j < C, the chunk's row count, with P_m = sum_s part[s][m][:]
+// (s ascending) and P_C the product of the all-ones row after the C rows
+// (sum_v W_v) when extra == 1; S = choose_splits for C + extra rows, exactly
+// as the dH GEMM chose it (nothing to do when it wrote the rows itself).
 template <typename Tout>
 __global__ __launch_bounds__(256) void k_splitk_scatter(const float* __restrict__ part,
                                                         int max_splits, int64_t k_tiles,
-                                                        int64_t cmax, int64_t H,
+                                                        int64_t cmax, int extra, int64_t H,
                                                         const int* __restrict__ rows,
                                                         const int* __restrict__ count, int64_t c0,
+                                                        const float* __restrict__ alpha,
+                                                        const float* __restrict__ coef, float epsV,
                                                         Tout* __restrict__ out) {
   const int64_t C = chunk_rows(count, c0, cmax);
-  const int S = choose_splits(cdiv(C, 256) * cdiv(H, 256), k_tiles, max_splits);
-  if (S == 1) return;  // one split: the GEMM wrote the rows itself
-  const int64_t MN = C * H;  // partials [split][C][H]
-  for (int64_t j = blockIdx.x; j < C; j += gridDim.x)  // chunk rows, grid-strided
-  for (int64_t e = (int64_t)threadIdx.x * 4; e < H; e += 256 * 4) {
+  const int64_t Me = C + extra;
+  const int S = choose_splits(cdiv(Me, 256) * cdiv(H, 256), k_tiles, max_splits);
+  if (S == 1 && extra == 0) return;  // one split: the GEMM wrote the rows itself
+  const int64_t MN = Me * H;  // partials [split][Me][H]
+  for (int64_t j = blockIdx.x; j < C; j += gridDim.x) {  // chunk rows, grid-strided
     const int64_t dst = (int64_t)rows[c0 + j] * H;
-    const int64_t src = j * H + e;
-    if (e + 4 <= H) {
-      floatx4 acc = *(const floatx4*)(part + src);
-      for (int s = 1; s < S; ++s) acc += *(const floatx4*)(part + (int64_t)s * MN + src);
+    const float al = alpha[j], ce = extra ? coef[j] * epsV : 0.f;
+    for (int64_t e = (int64_t)threadIdx.x * 4; e < H; e += 256 * 4) {
+      const int64_t src = j * H + e;
+      if (e + 4 <= H) {
+        floatx4 acc = *(const floatx4*)(part + src);
+        for (int s = 1; s < S; ++s) acc += *(const floatx4*)(part + (int64_t)s * MN + src);
+        floatx4 ws = floatx4{};
+        if (extra)
+          for (int s = 0; s < S; ++s) ws += *(const floatx4*)(part + (int64_t)s * MN + C * H + e);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) out[dst + e + k] = from_f32<Tout>(acc[k]);
-    } else {
-      for (int64_t k = 0; e + k < H; ++k) {
-        float a = part[src + k];
-        for (int s = 1; s < S; ++s) a += part[(int64_t)s * MN + src + k];
-        out[dst + e + k] = from_f32<Tout>(a);
+        for (int k = 0; k < 4; ++k) out[dst + e + k] = from_f32<Tout>(al * acc[k] - ce * ws[k]);
+      } else {
+        for (int64_t k = 0; e + k < H; ++k) {
+          float a = part[src + k], w = 0.f;
+          for (int s = 1; s < S; ++s) a += part[(int64_t)s * MN + src + k];
+          if (extra)
+            for (int s = 0; s < S; ++s) w += part[(int64_t)s * MN + C * H + e + k];
+          out[dst + e + k] = from_f32<Tout>(al * a - ce * w);
+        }
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// The gradient rows of a chunk formed in place over the stored logits z =
+// a + b (bf16, row-major [rows, ldE], ldE % 8 == 0), for chunk rows j < n:
+//   E[j, v] = coef_j (exp(s z - lse_i) - eps/Vg) - coef_j (1 - eps) [v == tcol_j]
+// for v < V, 0 for V <= v < ldE (page 1, cross_entropy_kernel steps 5 and 6,
+// rounded once), and alpha[j] = 1.  Used when label smoothing is large:
+// there the smoothing share eps/Vg is most of a flat softmax, and it has to
+// be subtracted before the one rounding to bf16.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_gpass_rows(bf16* __restrict__ E, int64_t ldE, int64_t V,
+                                                    const int* __restrict__ count, int64_t c0,
+                                                    int64_t cmax, const int* __restrict__ rows,
+                                                    const float* __restrict__ lse,
+                                                    const float* __restrict__ coef,
+                                                    const int* __restrict__ tcol, float eps,
+                                                    float Vg, float s, float* __restrict__ alpha) {
+  const int64_t n = chunk_rows(count, c0, cmax);
+  const float epsV = eps / Vg, sl = s * kLog2e;
+  for (int64_t j = blockIdx.y; j < n; j += gridDim.y) {
+    const int64_t i = rows != nullptr ? (int64_t)rows[c0 + j] : c0 + j;
+    const float cf = coef[j], l2 = lse[i] * kLog2e, tg = cf * (1.f - eps);
+    const int64_t tc = tcol[j];
+    if (blockIdx.x == 0 && threadIdx.x == 0) alpha[j] = 1.f;
+    bf16* er = E + j * ldE;
+    for (int64_t v0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8; v0 < ldE;
+         v0 += (int64_t)gridDim.x * 256 * 8) {
+      const bf16x8 z = *(const bf16x8*)(er + v0);
+      bf16x8 g;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float x = cf * (fast_exp2(__builtin_fmaf((float)z[e], sl, -l2)) - epsV);
+        if (v0 + e == tc) x -= tg;
+        g[e] = v0 + e < V ? (bf16)x : (bf16)0.f;
+      }
+      *(bf16x8*)(er + v0) = g;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Rows the logits GEMM does not write of the chunk's E [rows, ldE] (ldE % 8
+// == 0): rows n .. round_up(n + extra, 64) - 1, n = the chunk's row count,
+// are zero, except, with extra, row n = 1 in columns < V: its product with W
+// in the dH GEMM is sum_v W_v, the smoothing term of every row's dH.  Only
+// these rows of E past n are read (dW's K padding, dH's extra row).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_e_pad_rows(bf16* __restrict__ E, int64_t ldE, int64_t V,
+                                                    const int* __restrict__ count, int64_t c0,
+                                                    int64_t cmax, int extra) {
+  const int64_t n = chunk_rows(count, c0, cmax);
+  const int64_t n_end = round_up(n + extra, 64);
+  const int64_t per_row = ldE / 8, units = (n_end - n) * per_row;
+  for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < units;
+       u += (int64_t)gridDim.x * 256) {
+    const int64_t row = n + u / per_row, col = (u % per_row) * 8;
+    bf16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (extra && row == n && col + e < V) ? (bf16)1.f : (bf16)0.f;
+    *(bf16x8*)(E + row * ldE + col) = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The B operand of dW for a chunk: hT[c, j] = bf16(alpha_j hc[j, c]) for
+// chunk rows j < n (n = the chunk's row count), 0 for n <= j < round_up(n,
+// 64); hc = the chunk's gathered rows [>= round_up(n, 64), Cn].  With upart,
+// block (x, y) also writes the column sums over its 64 rows of coef_j hc[j, c]
+// to upart[(boff + x) * (Cn + 1) + c] and, for y == 0, sum_j coef_j to
+// column Cn (fixed order; zeros past n): their sum over the row blocks is
+// u = sum_t coef_t h_t, the smoothing term of dW and db.  64 x 64 tiles
+// through LDS, 16-byte accesses (Cn % 8 == 0).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_scale_transpose_bf16(
+    const bf16* __restrict__ hc, const int* __restrict__ count, int64_t c0, int64_t cmax,
+    int64_t Cn, const float* __restrict__ alpha, const float* __restrict__ coef,
+    bf16* __restrict__ hT, int64_t ldd, float* __restrict__ upart, int64_t boff) {
+  __shared__ bf16 tile[64][64 + 8];
+  const int tx = threadIdx.x & 7, ty = threadIdx.x >> 3;
+  const int64_t n = chunk_rows(count, c0, cmax);
+  const int64_t r0 = (int64_t)blockIdx.x * 64, cb = (int64_t)blockIdx.y * 64;
+  float* up = upart != nullptr ? upart + (boff + blockIdx.x) * (Cn + 1) : nullptr;
+  if (r0 >= round_up(n, 64)) {  // no row of this block exists: zero partials only
+    if (up != nullptr) {
+      for (int c = threadIdx.x; c < 64; c += 256) up[cb + c] = 0.f;
+      if (blockIdx.y == 0 && threadIdx.x == 0) up[Cn] = 0.f;
+    }
+    return;
+  }
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int lr = ty + 32 * p;
+    bf16x8 v = bf16x8{};
+    if (r0 + lr < n) v = *(const bf16x8*)(hc + (r0 + lr) * Cn + cb + tx * 8);
+    *(bf16x8*)&tile[lr][tx * 8] = v;
+  }
+  __syncthreads();
+  float al[8], cf[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int64_t r = r0 + tx * 8 + e;
+    al[e] = r < n ? alpha[r] : 0.f;
+    cf[e] = r < n ? coef[r] : 0.f;
+  }
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int lc = ty + 32 * p;
+    bf16x8 v;
+    float us = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = (float)tile[tx * 8 + e][lc];
+      v[e] = (bf16)(al[e] * x);
+      us += cf[e] * x;
+    }
+    *(bf16x8*)(hT + (cb + lc) * ldd + r0 + tx * 8) = v;
+    if (up != nullptr) {  // the 8 row groups of this column, added in a fixed order
+      us += __shfl_xor(us, 1, 64);
+      us += __shfl_xor(us, 2, 64);
+      us += __shfl_xor(us, 4, 64);
+      if (tx == 0) up[cb + lc] = us;
+    }
+  }
+  if (up != nullptr && blockIdx.y == 0 && threadIdx.x == 0) {
+    float cs = 0.f;
+    for (int64_t r = r0; r < min(n, r0 + 64); ++r) cs += coef[r];
+    up[Cn] = cs;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// db partials of a chunk (page 1: db += c_logits.sum(0)): dbpart[y * ldE + v]
+// = sum over the 64 chunk rows j of row block y (j < n) of alpha_j E[j, v],
+// for every column v < ldE; zeros for blocks past the rows.  The smoothing
+// term is subtracted once at the end (k_db_finish).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_db_partials(const bf16* __restrict__ E, int64_t ldE,
+                                                     const int* __restrict__ count, int64_t c0,
+                                                     int64_t cmax, const float* __restrict__ alpha,
+                                                     float* __restrict__ dbpart) {
+  const int64_t n = chunk_rows(count, c0, cmax);
+  const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.y * 64;
+  if (v >= ldE) return;
+  float acc = 0.f;
+  for (int64_t r = r0; r < min(n, r0 + 64); ++r) acc += alpha[r] * (float)E[r * ldE + v];
+  dbpart[(int64_t)blockIdx.y * ldE + v] = acc;
+}
+
+// db[v] = sum_b part[b * ld + v] (b ascending) - epsV * (*csum when csum is
+// not null), rounded once to T.
+template <typename T>
+__global__ __launch_bounds__(256) void k_db_finish(const float* __restrict__ part, int64_t nb,
+                                                   int64_t ld, int64_t V,
+                                                   const float* __restrict__ csum, float epsV,
+                                                   T* __restrict__ out) {
+  const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (v >= V) return;
+  float s = 0.f;
+  for (int64_t b = 0; b < nb; ++b) s += part[b * ld + v];
+  if (csum != nullptr) s -= epsV * *csum;
+  out[v] = from_f32<T>(s);
 }
 
 // loss = (sum_i rloss[i]) / D, float64 partial sums, fixed tree (page 1:

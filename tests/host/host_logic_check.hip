@@ -8,9 +8,11 @@
 //   2. choose_splits: within [1, max_splits], one split from 256 tiles on,
 //      at least 8 K tiles per split;
 //   3. make_plan: for every number of rows the device may find in a chunk
-//      (any count of non-ignored rows), the dH GEMM's grid covers its work
-//      items and the split-K partials it writes fit the space reserved for
-//      them in the workspace.
+//      (any count of non-ignored rows), with and without the all-ones row of
+//      the label-smoothing term, the dH GEMM's grid covers its work items,
+//      the split-K partials it writes fit the space reserved for them, the
+//      rows of E past the chunk's rows fit its allocation, and the
+//      smoothing-term partials fit theirs.
 // Prints "ok" and exits 0, or prints the first failure and exits 1.
 #include "../../lm_head_linear_bf16_amd/csrc/fldce.hip"
 
@@ -72,17 +74,25 @@ int check_plan(int mode, int64_t N, int64_t H, int64_t V, int64_t chunk) {
   if (end < p.oDHpart) return fail("plan layout", N, H, V, chunk);
   const size_t reserved = end - p.oDHpart;
   const int64_t th = cdiv(H, kBN), k_tiles = p.Vp / kBK;
+  int64_t ublocks = 0;
   for (int64_t ic = 0; ic < p.nchunks; ++ic) {
     const int64_t cmax = std::min(p.C, N - ic * p.C);
-    const int64_t grid = cdiv(cmax, kBM) * th * p.splits;
-    for (int64_t n = 0; n <= cmax; ++n) {  // rows the device may find in this chunk
-      const int64_t tiles = cdiv(n, kBM) * th;
-      const int S = choose_splits(tiles, k_tiles, p.splits);
-      if (tiles * S > grid) return fail("dH grid too small", N, H, n, S);
-      const size_t need = S > 1 ? (size_t)S * n * H * 4 : 0;
-      if (need > reserved) return fail("dH partials exceed the workspace", N, H, n, (long long)need);
+    ublocks += cdiv(cmax, 64);
+    for (int extra = 0; extra <= 1; ++extra) {  // the all-ones row (label smoothing)
+      const int64_t grid = cdiv(cmax + extra, kBM) * th * p.splits;
+      for (int64_t n = 0; n <= cmax; ++n) {  // rows the device may find in this chunk
+        const int64_t Me = n + extra;
+        const int64_t tiles = cdiv(Me, kBM) * th;
+        const int S = choose_splits(tiles, k_tiles, p.splits);
+        if (tiles * S > grid) return fail("dH grid too small", N, H, n, S);
+        const size_t need = (S > 1 || extra) ? (size_t)S * Me * H * 4 : 0;
+        if (need > reserved) return fail("dH partials exceed the workspace", N, H, n, (long long)need);
+        // E rows written or read past the chunk's rows, and h^T columns
+        if (round_up(Me, 64) > p.Cp) return fail("E rows exceed the workspace", N, H, n, p.Cp);
+      }
     }
   }
+  if (ublocks > p.u_blocks) return fail("smoothing partial blocks", N, H, ublocks, p.u_blocks);
   return 0;
 }
 

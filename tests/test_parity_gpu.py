@@ -108,6 +108,78 @@ def test_no_ignored_rows():
     _compare(w, r, o, t)
 
 
+def _far_target_inputs(w, seed):
+    """N(0, 1) raw logits times a large logit scale on the second half of the
+    rows (spreads of about a hundred nats between a row's best logit and a
+    random target), raw logits 50 times smaller on the first half."""
+    rng = np.random.default_rng(seed)
+    h = rng.standard_normal((w.N, w.H)).astype(np.float32)
+    h[: w.N // 2] *= 0.02
+    W = (rng.standard_normal((w.V, w.H)) / np.sqrt(w.H)).astype(np.float32)
+    return synth._as_dtype(h, w.dtype), synth._as_dtype(W, w.dtype)
+
+
+@pytest.mark.parametrize("chunk", [0, 128])
+def test_targets_far_below_the_row_maximum(chunk):
+    """Rows whose best logit lies more than 30 nats above the target logit
+    are recomputed relative to their logsumexp (the stored exponentials of
+    the other rows are relative to the target logit): loss, lse, dH and dW
+    against the oracle with both kinds of rows in one batch, and the
+    forward-only loss equal bit for bit."""
+    w = synth.custom("far_targets_bf16", 2, 150, 128, 3001, label_smoothing=0.1,
+                     logit_scale=20.0, w_std=1.0 / np.sqrt(128), total_is_N=False)
+    h, W = _far_target_inputs(w, seed=21)
+    t, p = synth.targets(w)
+    r, o, _ = _run(w, chunk_rows=chunk, target=t, p_mask=p, h=h, W=W)
+    z = O.scaled_logits(h.values, W.values, w.logit_scale)
+    v = t != -100
+    gap = z.max(axis=1) - z[np.arange(w.N), np.where(v, t, 0)]
+    assert np.any(v & (gap > 35.0)) and np.any(v & (gap < 25.0))  # both kinds of rows
+    _compare(w, r, o, t)
+    torch = torch_cuda()
+    from lm_head_linear_bf16_amd import fldce
+    dev = torch.device("cuda:0")
+    f = fldce.fldce_fwd(to_dev(h, dev), to_dev(W, dev), torch.from_numpy(t).to(dev),
+                        torch.from_numpy(p).to(dev), label_smoothing=w.label_smoothing,
+                        logit_scale=w.logit_scale, reduction=w.reduction, total=w.total,
+                        row_stats=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(f["row_lse"]), host(r["row_lse"]))
+    assert float(f["loss"].item()) == float(r["loss"].item())
+
+
+@pytest.mark.parametrize("eps", [0.5, 0.75, 1.0])
+@pytest.mark.parametrize("chunk", [0, 100])
+def test_large_label_smoothing_flat_softmax(eps, chunk):
+    """Label smoothing up to 1 on nearly flat softmax rows (tiny logits), where
+    the smoothing share eps / V is most of every gradient entry: up to 1/2 the
+    exponentials are the backward operand and the share is added to the
+    products; above it the gradient is formed from the stored logits before
+    its one rounding.  fwd_bwd (one chunk and chunked) and a vocabulary
+    shard's backward against the oracle."""
+    w = synth.custom(f"flat_eps_bf16", 1, 160, 128, 2000, label_smoothing=eps, logit_scale=0.5,
+                     reduction="sum", index=410)
+    r, o, t = _run(w, chunk_rows=chunk)
+    _compare(w, r, o, t)
+    torch = torch_cuda()
+    from lm_head_linear_bf16_amd import fldce
+    dev = torch.device("cuda:0")
+    h, W = synth.hidden(w), synth.weight(w)
+    tt, p = synth.targets(w)
+    v0, Vl = 500, 777
+    say(f"case shard bwd eps={eps}")
+    b = fldce.fldce_shard_bwd(to_dev(h, dev), to_dev(W, dev)[v0:v0 + Vl].contiguous(),
+                              torch.from_numpy(tt).to(dev), torch.from_numpy(p).to(dev),
+                              torch.from_numpy(o["lse"].astype(np.float32)).to(dev), v0, w.V,
+                              label_smoothing=eps, logit_scale=0.5, reduction="sum",
+                              chunk_rows=chunk)
+    torch.cuda.synchronize()
+    odh, odw = O.shard_backward(h.values, W.values[v0:v0 + Vl], tt, p, o["lse"], v0, w.V, 1.0,
+                                eps, 0.5)
+    assert grad_err(host(b["dH_partial"]), odh) <= GRAD_RTOL["bf16"]
+    assert grad_err(host(b["dW_local"]), odw) <= GRAD_RTOL["bf16"]
+
+
 def test_all_ignored():
     w = synth.custom("all_ignored_bf16", 1, 200, 128, 500, total_is_N=False)
     t = np.full(w.N, -100, dtype=np.int64)
@@ -202,7 +274,8 @@ def test_vocab_shards_match_full_vocab(dtype):
         assert np.all(np.isneginf(m[~valid])) and np.all(S[~valid] == 0)
         assert np.all(tl[~valid] == 0) and np.all(rs[~valid] == 0)
         np.testing.assert_allclose(m[valid], om[valid], atol=tol * 4, rtol=0)
-        np.testing.assert_allclose((np.log(S) + m)[valid], (np.log(oS) + om)[valid], atol=tol * 4, rtol=0)
+        np.testing.assert_allclose(np.log(S[valid]) + m[valid], np.log(oS[valid]) + om[valid],
+                                   atol=tol * 4, rtol=0)
         np.testing.assert_allclose(tl, ot, atol=tol * 4, rtol=0)
         np.testing.assert_allclose(rs[valid], orr[valid], atol=tol * 40, rtol=tol)
         assert np.all(tl[(t < v0) | (t >= v0 + w.V_local)] == 0.0)
