@@ -3,9 +3,12 @@
 Same structure as page 1 ("fused_linear_diffusion_cross_entropy.py"):
 ``FusedLinearCrossEntropyFunction`` computes the loss and the gradients of
 x, weight and bias in its forward (one ``fldce_fwd_bwd_ex`` call; only those
-an input requires, so a frozen weight skips the dW GEMM) and keeps them; its backward multiplies them by the upstream gradient in place
+an input requires, so a frozen weight skips the dW GEMM) and keeps them; its
+backward multiplies them by the upstream gradient in place
 (``fldce_scale_grads``, skipped on the device when it is 1), as the page's
-``fused_linear_cross_entropy_backward`` does.
+``fused_linear_cross_entropy_backward`` does.  Because the scaling is in
+place, a second backward through the same graph (``retain_graph=True``)
+raises instead of scaling the gradients twice.
 ``FusedLinearDiffusionCrossEntropyLoss`` is the module: it flattens
 [B, L, H] inputs, defaults p_mask to ones and applies the end-of-block
 weight; without a gradient to compute (evaluation) it runs the forward
@@ -35,10 +38,16 @@ class FusedLinearCrossEntropyFunction(torch.autograd.Function):
                                    want_dH=ctx.needs_input_grad[0],
                                    want_dW=ctx.needs_input_grad[2])
         ctx.save_for_backward(r["dH"], r["dW"], r["db"])
+        ctx.scaled = False
         return r["loss"].view(())
 
     @staticmethod
     def backward(ctx, do):
+        if ctx.scaled:
+            raise RuntimeError("a second backward through the fused LM-head loss is not supported: "
+                               "its gradients were already scaled in place by the first one; "
+                               "recompute the loss instead")
+        ctx.scaled = True
         dH, dW, db = ctx.saved_tensors
         g = do.detach().to(torch.float32).reshape(1).contiguous()
         if dH is not None or dW is not None or db is not None:
@@ -72,7 +81,7 @@ class FusedLinearDiffusionCrossEntropyLoss(torch.nn.Module):
                  logit_scale: float = 1.0, reduction: str = "mean"):
         super().__init__()
         if reduction not in ("mean", "sum"):
-            raise ValueError(f"reduction: {reduction} is not supported")
+            raise ValueError(f"reduction must be 'mean' or 'sum', got {reduction!r}")
         self.ignore_index = ignore_index
         self.label_smoothing = label_smoothing
         self.logit_scale = logit_scale

@@ -245,8 +245,10 @@ def test_autograd_module():
     mod = FusedLinearDiffusionCrossEntropyLoss(label_smoothing=0.1, logit_scale=0.5)
     loss = mod(x, torch.from_numpy(target).to(dev).view(w.B, w.L), Wp, bp,
                torch.from_numpy(p_mask).to(dev).view(w.B, w.L), eob_token_id=eob, eob_weight=1.5)
-    (2.5 * loss).backward()
+    (2.5 * loss).backward(retain_graph=True)
     torch.cuda.synchronize()
+    with pytest.raises(RuntimeError, match="second backward"):  # it would scale them twice
+        loss.backward()
     o = O.forward_backward(h.values, W.values, target, p_mask, label_smoothing=0.1,
                            logit_scale=0.5, reduction="mean", bias=b.values, eob_token_id=eob,
                            eob_weight=1.5)
