@@ -85,11 +85,11 @@ def _counter_per_kernel(path: str, counter: str) -> dict:
 
 # the kernel instance each stage launches: plain fwd+bwd, and for the vocab
 # shard workload the shard partials and the shard backward
-STAGE_KERNELS = {"logits_gemm": "k_logits_bf16<true, true>", "dH_gemm": "k_gemm_dh_bf16",
-                 "dW_gemm": "k_gemm_dw_bf16<0>", "dlogits": "k_gpass_blk<16, 1024>"}
-SHARD_STAGE_KERNELS = {"partials_logits": "k_logits_bf16<false, true>",
-                       "bwd_logits": "k_logits_bf16<true, false>", "dH_gemm": "k_gemm_dh_bf16",
-                       "dW_gemm": "k_gemm_dw_bf16<0>", "dlogits": "k_gpass_blk<16, 1024>"}
+STAGE_KERNELS = {"logits_gemm": "k_logits_bf16<1, true, false>", "dH_gemm": "k_gemm_dh_bf16",
+                 "dW_gemm": "k_gemm_dw_bf16<0>"}
+SHARD_STAGE_KERNELS = {"partials_logits": "k_logits_bf16<0, false, false>",
+                       "bwd_logits": "k_logits_bf16<2, true, false>", "dH_gemm": "k_gemm_dh_bf16",
+                       "dW_gemm": "k_gemm_dw_bf16<0>"}
 
 
 WORKLOAD_NAMES = ("tiny", "4b", "headline", "block", "shard")
@@ -149,8 +149,107 @@ def traffic_summary(fetch_csv: str, write_csv: str, workload: str, calib_mib: in
     return 0
 
 
+def _durations(trace_csv: str) -> dict:
+    """{dispatch id: kernel duration in ns} from a rocprofv3 kernel-trace CSV."""
+    import csv
+    out = {}
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            out[r["Dispatch_Id"]] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    return out
+
+
+def counter_summary(run_dirs, workload: str, cmd: str) -> int:
+    """Per stage kernel, averages over its launches of the counters of several
+    rocprofv3 --pmc --kernel-trace runs (one directory each): the average
+    shader clock (GRBM_GUI_ACTIVE cycles over the launch's duration), MFMA
+    busy (SQ_VALU_MFMA_BUSY_CYCLES over 4 SIMDs x 256 CUs x those cycles),
+    VALU busy (SQ_ACTIVE_INST_VALU over 256 CUs x cycles, rocprofv3's VALUBusy),
+    LDS active (SQ_LDS_IDX_ACTIVE over 256 CUs x cycles), the MFMA bf16 work,
+    and the requests the L2 sent to DRAM addresses against all its read
+    requests.  Writes profiles/<workload>_counters.md."""
+    import csv
+    import glob
+    vals: dict = {}     # (kernel, counter) -> [per-dispatch values]
+    durs: dict = {}     # kernel -> [ns]
+    for d in run_dirs:
+        cc = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        kt = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+        if not cc:
+            print(f"no counter CSV under {d}", file=sys.stderr)
+            return 1
+        dur = _durations(kt[0]) if kt else {}
+        per: dict = {}
+        names: dict = {}
+        for path in cc:
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    key = (r["Dispatch_Id"], r["Counter_Name"])
+                    per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+                    names[r["Dispatch_Id"]] = r["Kernel_Name"]
+        for (disp, cname), v in per.items():
+            vals.setdefault((names[disp], cname), []).append(v)
+        if "GRBM_GUI_ACTIVE" in {c for (_, c) in per}:
+            for disp, name in names.items():
+                if disp in dur:
+                    durs.setdefault(name, []).append(dur[disp])
+    avg = lambda xs: sum(xs) / len(xs) if xs else float("nan")  # noqa: E731
+    kernels = SHARD_STAGE_KERNELS if workload == "shard" else STAGE_KERNELS
+    lines = [f"# Counters per launch of the stage kernels, {workload} workload", "",
+             "rocprofv3 --pmc runs with --kernel-trace (one counter group per run), each", "",
+             f"    {cmd}", "",
+             "clock = GRBM_GUI_ACTIVE / launch duration; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / "
+             "(1024 SIMDs x GRBM_GUI_ACTIVE) (rocprofv3's MfmaUtil); VALU busy = "
+             "SQ_ACTIVE_INST_VALU / (256 CUs x GRBM_GUI_ACTIVE) (rocprofv3's VALUBusy); LDS "
+             "active = SQ_LDS_IDX_ACTIVE / (256 CUs x GRBM_GUI_ACTIVE) (rocprofv3's LdsUtil); "
+             "MFMA TFLOP = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; DRAM share = TCC_EA0_RDREQ_DRAM / "
+             "TCC_EA0_RDREQ and TCC_EA0_WRREQ_DRAM / TCC_EA0_WRREQ (L2 requests to local HBM "
+             "addresses, which the memory-side MALL may serve; no counter here separates "
+             "MALL hits); fetch / write = FETCH_SIZE / WRITE_SIZE.", "",
+             "| stage | kernel | launches | ms | clock GHz | MFMA busy % | MFMA TFLOP/s | "
+             "VALU busy % | LDS active % | fetch GB | write GB | DRAM read / write share |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for stage, kname in kernels.items():
+        ks = [k for (k, _) in vals if kname in k]
+        if not ks:
+            continue
+        k = ks[0]
+        g = lambda c: avg(vals.get((k, c), []))  # noqa: E731
+        gui = g("GRBM_GUI_ACTIVE")
+        ms = avg(durs.get(k, [])) * 1e-6
+        clock = gui / (ms * 1e6) if ms == ms and ms > 0 else float("nan")
+        mfma = 100.0 * g("SQ_VALU_MFMA_BUSY_CYCLES") / (1024.0 * gui)
+        valu = 100.0 * g("SQ_ACTIVE_INST_VALU") / (256.0 * gui)
+        lds = 100.0 * g("SQ_LDS_IDX_ACTIVE") / (256.0 * gui)
+        tf = g("SQ_INSTS_VALU_MFMA_MOPS_BF16") * 512.0 / (ms * 1e-3) / 1e12
+        fetch = g("FETCH_SIZE") * 1024 / 1e9
+        write = g("WRITE_SIZE") * 1024 / 1e9
+        rd = g("TCC_EA0_RDREQ_DRAM_sum") / g("TCC_EA0_RDREQ_sum")
+        wr = g("TCC_EA0_WRREQ_DRAM_sum") / g("TCC_EA0_WRREQ_sum")
+        lines.append(f"| {stage} | {kname} | {len(durs.get(k, []))} | {ms:.3f} | {clock:.2f} | "
+                     f"{mfma:.1f} | {tf:.0f} | {valu:.1f} | {lds:.1f} | {fetch:.2f} | {write:.2f} | "
+                     f"{rd:.3f} / {wr:.3f} |")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"{workload}_counters.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    return 0
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, rows: int) -> dict:
-    """The float64 oracle on the first `rows` token rows of the same workload."""
+    """The float64 oracle on the first `rows` token rows of the same workload
+    (all of them by default: one full call)."""
     import numpy as np
     try:
         from threadpoolctl import threadpool_info
@@ -171,10 +270,12 @@ def cpu_baseline(w, rows: int) -> dict:
                             logit_scale=w.logit_scale, reduction=w.reduction,
                             total=w.total or None, row_block=1024)
     dt = time.perf_counter() - t0
+    what = (f"the whole workload, all {w.N} token rows: one full call" if rows == w.N else
+            f"first {rows} of {w.N} token rows of the same workload")
     return {"value": rows / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {rows} of {w.N} token rows of the same workload (full vocabulary, "
-                      f"loss + dH + dW rows' contributions), float64 NumPy, {dt:.2f} s",
-            "seconds": dt}
+            "sample": f"{what} (full vocabulary; loss, dH, dW), float64 NumPy, {dt:.2f} s",
+            "seconds": dt, "cpu_model": cpu_model(),
+            "host_threads": len(os.sched_getaffinity(0))}
 
 
 def env_info(torch) -> dict:
@@ -351,16 +452,23 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="headline")
     ap.add_argument("--chunk-rows", type=int, default=0)
-    ap.add_argument("--cpu-rows", type=int, default=6144,
-                    help="token rows the float64 oracle baseline runs on (~14 s on 16 cores)")
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="token rows the float64 oracle baseline runs on (0 = the whole "
+                         "workload: one full call, about 18 s on 16 cores at the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--sweep", default="", help="comma-separated chunk sizes to time as well")
+    ap.add_argument("--sweep", default="1024,2048,4096,8192",
+                    help="comma-separated row-chunk sizes to time as well ('' = none; headline "
+                         "workload only)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device copy of this many MiB first (counter calibration)")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a "
                          "run with --calib-copy-mib into profiles/traffic.json and exit")
     ap.add_argument("--calib-mib", type=int, default=1024, help="size of that calibration copy")
+    ap.add_argument("--counter-summary", nargs="+", metavar="RUN_DIR",
+                    help="summarise rocprofv3 --pmc --kernel-trace runs (one directory each) "
+                         "into profiles/<workload>_counters.md and exit")
+    ap.add_argument("--counter-cmd", default="", help="the profiling command, for the summary")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the forward-only leg (and the bias + db leg)")
     ap.add_argument("--frozen-leg", action="store_true",
@@ -369,6 +477,8 @@ def main() -> int:
                     help="also time fwd+bwd with the seeded bias and db (fldce_fwd_bwd_ex); off by "
                          "default so that the plain step is the only user of its logits kernel")
     args = ap.parse_args()
+    if args.counter_summary:
+        return counter_summary(args.counter_summary, args.workload, args.counter_cmd)
     if args.traffic_summary:
         return traffic_summary(args.traffic_summary[0], args.traffic_summary[1], args.workload,
                                args.calib_mib)
@@ -409,7 +519,11 @@ def main() -> int:
     pm = torch.from_numpy(p_mask).to(dev)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
 
-    def run_config(chunk_rows: int, steps: int, warmup: int):
+    def run_config(chunk_rows: int, steps: int, warmup: int, stages_pass: bool = True):
+        """(ms per step, stage times, loss, per-step distribution).  The timed
+        steps run with the library's stage events off; with stages_pass, the
+        same number of steps then runs again with them on (not part of the
+        timed figure) to give each stage's launch times."""
         out = dict(loss=torch.empty(1, dtype=torch.float32, device=dev),
                    dH=torch.empty_like(h), dW=torch.empty_like(W))
         nbytes = fldce.fldce_workspace_size(N, H, V, dt, chunk_rows)
@@ -420,7 +534,6 @@ def main() -> int:
         for _ in range(warmup):
             fldce.fldce_fwd_bwd(h, W, tgt, pm, **kw)
         torch.cuda.synchronize()
-        fldce.fldce_profile_begin()
         # one event between consecutive steps on the library's stream (the
         # current one): per-step times without any synchronisation in the loop
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
@@ -432,14 +545,23 @@ def main() -> int:
             ev[i + 1].record()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        fldce.fldce_profile_end()
         per_step = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
-        stages = {}
-        for s in range(fldce.fldce_profile_num_stages()):
-            ms, n = fldce.fldce_profile_read(s)
-            if n:
-                stages[fldce.fldce_profile_stage_name(s)] = dict(total_ms=ms, launches=n)
         loss = float(out["loss"].item())
+        stages = {}
+        if stages_pass:
+            fldce.fldce_profile_begin()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                fldce.fldce_fwd_bwd(h, W, tgt, pm, **kw)
+            e1.record()
+            torch.cuda.synchronize()
+            fldce.fldce_profile_end()
+            for s in range(fldce.fldce_profile_num_stages()):
+                ms, n = fldce.fldce_profile_read(s)
+                if n:
+                    stages[fldce.fldce_profile_stage_name(s)] = dict(total_ms=ms, launches=n)
+            stages["_step_ms_with_stage_events"] = e0.elapsed_time(e1) / steps
         del ws
         dist = {"median": round(float(np.median(per_step)), 4),
                 "p10": round(float(np.percentile(per_step, 10)), 4),
@@ -451,6 +573,7 @@ def main() -> int:
     C = args.chunk_rows or fldce.fldce_default_chunk_rows(N, H, V)
     log(f"timing {args.steps} steps after {args.warmup} warmup (chunk_rows={C})")
     ms, stages, loss, dist = run_config(args.chunk_rows, args.steps, args.warmup)
+    step_ms_profiled = stages.pop("_step_ms_with_stage_events")
     # bf16 multiplies only rows whose target != ignore_index (the others are
     # exactly zero); fp32 multiplies every row
     rows_mult = n_valid if w.dtype == "bf16" else N
@@ -470,6 +593,7 @@ def main() -> int:
                 "traffic": traffic_entry(dom, w.name), "avg_launch_ms": round(avg_ms, 4),
                 "flops_per_launch": per_launch_flops}
     stage_ms = {k: round(v["total_ms"] / args.steps, 4) for k, v in stages.items()}
+    stage_ms["step_with_stage_events"] = round(step_ms_profiled, 4)
     result = {
         "metric": "fused LM-head CE fwd+bwd tokens/s and TFLOP/s (% bf16 MFMA peak), 1 GPU",
         "value": round(N / (ms * 1e-3), 1),
@@ -500,18 +624,22 @@ def main() -> int:
     }
     if not args.no_extras:
         result.update(extra_legs(args, w, h, W, tgt, pm, dt, rows_mult, ms, peak))
-    if args.sweep:
+    if args.sweep and w.name == "headline":
+        # rows per chunk, taken over the compacted rows (page 1 chunks the rows
+        # to bound the [C, V] buffer); C >= the rows with a target is one chunk
         sw = {}
         for c in [int(x) for x in args.sweep.split(",") if x]:
             log(f"sweep chunk_rows={c}")
-            m, _, _, _ = run_config(c, max(3, args.steps // 4), 1)
-            sw[str(c)] = {"ms_per_step": round(m, 3), "tflops": round(flops / (m * 1e-3) / 1e12, 1),
+            m, _, _, d = run_config(c, max(4, args.steps // 4), 1, stages_pass=False)
+            sw[str(c)] = {"ms_per_step": round(m, 3), "step_ms_median": d["median"],
+                          "chunks": -(-rows_mult // c), "vs_default": round(m / ms, 3),
+                          "tflops": round(flops / (m * 1e-3) / 1e12, 1),
                           "tokens_per_s": round(N / (m * 1e-3), 1)}
         result["chunk_sweep"] = sw
     if not args.no_cpu_baseline:
         del h, W
         torch.cuda.empty_cache()
-        result["cpu_baseline"] = cpu_baseline(w, min(args.cpu_rows, N))
+        result["cpu_baseline"] = cpu_baseline(w, min(args.cpu_rows or N, N))
     print(json.dumps(result), flush=True)
     return 0
 
