@@ -76,10 +76,15 @@ enum fldce_status {
   FLDCE_ERR_WORKSPACE = -5,      /* workspace NULL or smaller than required   */
   FLDCE_ERR_ALIGNMENT = -6,      /* a pointer is not 16-byte aligned          */
   FLDCE_ERR_HIP = -7,            /* a kernel launch failed                    */
-  FLDCE_ERR_UNSUPPORTED = -8     /* shape the kernels do not handle: bf16 with
+  FLDCE_ERR_UNSUPPORTED = -8,    /* shape the kernels do not handle: bf16 with
                                     H not a multiple of 64 or a GEMM grid of
                                     2^32 work-items or more; fp32 with V >= 2^30 */
+  FLDCE_ERR_SCRATCH_TOO_SMALL = -9 /* fldce_fwd_noalloc: the call needs more
+                                    than FLDCE_NOALLOC_SCRATCH_BYTES */
 };
+
+/* Device memory fldce_fwd_noalloc may use (64 MiB per device). */
+#define FLDCE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 /* Library version (FLDCE_VERSION of the build). */
 int fldce_version(void);
@@ -196,6 +201,33 @@ int fldce_fwd(const void* h, const void* W, const void* bias,
               int64_t total, int64_t eob_token_id, float eob_weight,
               float* loss, float* row_lse, float* row_loss, void* workspace,
               size_t workspace_bytes, void* stream);
+
+/*
+ * fldce_fwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): no
+ * workspace argument; the call uses a device array inside the library of
+ * FLDCE_NOALLOC_SCRATCH_BYTES, which each device holds from the library's
+ * load until the process ends.  It calls no allocating routine.
+ *
+ * Arguments, results and errors as in fldce_fwd (the same kernels; results
+ * are bit for bit those of fldce_fwd), except:
+ *   - FLDCE_ERR_SCRATCH_TOO_SMALL, before anything is enqueued, when
+ *     fldce_fwd_workspace_size(N, H, V, dtype) > FLDCE_NOALLOC_SCRATCH_BYTES
+ *     (bf16 at H = 2560, V = 151936: N <= 3378 rows);
+ *   - the array is looked up on the calling thread's current device, which
+ *     must be the device of `stream` and of every pointer;
+ *   - every call on one device shares that device's array: calls that
+ *     overlap in time on one device (other streams, other threads) race and
+ *     give undefined results; calls one after another on a stream are fine
+ *     (nothing in the array has to start at any value).
+ */
+int fldce_fwd_noalloc(const void* h, const void* W, const void* bias,
+                      const int64_t* target, const float* p_mask, int64_t N,
+                      int64_t H, int64_t V, int dtype, int64_t ignore_index,
+                      float label_smoothing, float logit_scale, int reduction,
+                      int64_t total, int64_t eob_token_id, float eob_weight,
+                      float* loss, float* row_lse, float* row_loss,
+                      void* stream);
 
 /*
  * Upstream-gradient scaling (page 1, fused_linear_cross_entropy_backward):

@@ -207,6 +207,34 @@ void set_gemm_attributes() {
 }
 
 // ---------------------------------------------------------------------------
+// Device memory of fldce_fwd_noalloc, for callers that cannot allocate: a
+// file-scope array each device holds from module load until the process
+// ends.  Host code never passes the array's name to a kernel (on the host it
+// is only a stand-in for the symbol): the address of each device's copy is
+// looked up once per device with hipGetSymbolAddress and kept here.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[FLDCE_NOALLOC_SCRATCH_BYTES];
+
+// Address of the current device's copy of `scratch` (looked up on the first
+// call made on that device).
+int scratch_of_current_device(char** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FLDCE_ERR_HIP;
+  static std::mutex mu;
+  static std::vector<char*> ptrs;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)ptrs.size() <= dev) ptrs.resize(dev + 1, nullptr);
+  if (ptrs[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return FLDCE_ERR_HIP;
+    ptrs[dev] = static_cast<char*>(ptr);
+  }
+  *out = ptrs[dev];
+  return FLDCE_OK;
+}
+
+// ---------------------------------------------------------------------------
 // Stage profiling: event pairs recorded on the call's stream.
 // ---------------------------------------------------------------------------
 enum Stage {
@@ -870,6 +898,9 @@ const char* fldce_status_string(int status) {
     case FLDCE_ERR_UNSUPPORTED:
       return "shape not supported by the bf16 path (H must be a multiple of 64; each GEMM grid "
              "must hold fewer than 2^32 work-items)";
+    case FLDCE_ERR_SCRATCH_TOO_SMALL:
+      return "the call needs more than the FLDCE_NOALLOC_SCRATCH_BYTES of the allocation-free "
+             "entry point (use fldce_fwd with a workspace)";
     default: return "unknown status";
   }
 }
@@ -996,6 +1027,25 @@ int fldce_fwd(const void* h, const void* W, const void* bias, const int64_t* tar
   return run_fwd(p, h, W, bias, target, p_mask, N, H, V, dtype, ignore_index, label_smoothing,
                  logit_scale, reduction, total, eob_token_id, eob_weight, loss, row_lse, row_loss,
                  static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+}
+
+int fldce_fwd_noalloc(const void* h, const void* W, const void* bias, const int64_t* target,
+                      const float* p_mask, int64_t N, int64_t H, int64_t V, int dtype,
+                      int64_t ignore_index, float label_smoothing, float logit_scale,
+                      int reduction, int64_t total, int64_t eob_token_id, float eob_weight,
+                      float* loss, float* row_lse, float* row_loss, void* stream) {
+  int rc = check_fwd_args(h, W, bias, target, p_mask, N, H, V, dtype, label_smoothing,
+                          logit_scale, reduction, eob_token_id, eob_weight, loss);
+  if (rc != FLDCE_OK) return rc;
+  const Plan p = make_plan(kFwd, N, H, V, dtype, 0);
+  if (!grids_fit(p, dtype)) return FLDCE_ERR_UNSUPPORTED;
+  if (p.total > FLDCE_NOALLOC_SCRATCH_BYTES) return FLDCE_ERR_SCRATCH_TOO_SMALL;
+  char* ws = nullptr;
+  rc = scratch_of_current_device(&ws);
+  if (rc != FLDCE_OK) return rc;
+  return run_fwd(p, h, W, bias, target, p_mask, N, H, V, dtype, ignore_index, label_smoothing,
+                 logit_scale, reduction, total, eob_token_id, eob_weight, loss, row_lse, row_loss,
+                 ws, static_cast<hipStream_t>(stream));
 }
 
 int fldce_scale_grads(const float* grad_out, int dtype, void* dH, int64_t n_dH, void* dW,

@@ -39,6 +39,9 @@ _SIGNATURES = {
     "fldce_fwd": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_int, _c_i64,
                            _c_f, _c_f, _c_int, _c_i64, _c_i64, _c_f, _c_p, _c_p, _c_p, _c_p, _c_sz,
                            _c_p]),
+    "fldce_fwd_noalloc": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_int,
+                                   _c_i64, _c_f, _c_f, _c_int, _c_i64, _c_i64, _c_f, _c_p, _c_p,
+                                   _c_p, _c_p]),
     "fldce_scale_grads": (_c_int, [_c_p, _c_int, _c_p, _c_i64, _c_p, _c_i64, _c_p, _c_i64, _c_p]),
     "fldce_shard_partials_workspace_size": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_int]),
     "fldce_shard_partials": (_c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_int,
@@ -329,6 +332,41 @@ def fldce_fwd(h: torch.Tensor, W: torch.Tensor, target: torch.Tensor,
                              _ptr(rl), _ptr(ws), nbytes, _stream(dev))
     if rc != 0:
         raise FldceError(rc, "fldce_fwd")
+    r = dict(loss=loss)
+    if row_stats:
+        r.update(row_lse=lse, row_loss=rl)
+    return r
+
+
+# bytes of the library's own device array that fldce_fwd_noalloc uses
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def fldce_fwd_noalloc(h: torch.Tensor, W: torch.Tensor, target: torch.Tensor,
+                      p_mask: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
+                      ignore_index: int = -100, label_smoothing: float = 0.0,
+                      logit_scale: float = 1.0, reduction="mean", total: int = 0,
+                      eob_token_id: Optional[int] = None, eob_weight: float = 1.0,
+                      row_stats: bool = False, out: Optional[dict] = None) -> dict:
+    """fldce_fwd without a workspace: the library's own per-device array
+    (NOALLOC_SCRATCH_BYTES) holds the intermediates.  The caller passes every
+    output in ``out`` (loss, and row_lse / row_loss with row_stats) so that
+    nothing is allocated; missing ones are created here (convenience only)."""
+    N, H, V = _check_inputs(h, W, target, p_mask, bias)
+    dev = h.device
+    code = _dtype_code(h.dtype)
+    loss = _out(out, "loss", 1, h, torch.float32, (1,))
+    lse = rl = None
+    if row_stats:
+        lse = _out(out, "row_lse", N, h, torch.float32, (N,))
+        rl = _out(out, "row_loss", N, h, torch.float32, (N,))
+    with torch.cuda.device(dev):
+        rc = lib().fldce_fwd_noalloc(_ptr(h), _ptr(W), _ptr(bias), _ptr(target), _ptr(p_mask), N,
+                                     H, V, code, ignore_index, label_smoothing, logit_scale,
+                                     _reduction_code(reduction), total, _eob_code(eob_token_id),
+                                     eob_weight, _ptr(loss), _ptr(lse), _ptr(rl), _stream(dev))
+    if rc != 0:
+        raise FldceError(rc, "fldce_fwd_noalloc")
     r = dict(loss=loss)
     if row_stats:
         r.update(row_lse=lse, row_loss=rl)

@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported_and_bound(L):
 
 def test_status_strings(L):
     assert fldce.status_string(0) == "ok"
-    for s in range(-8, 0):
+    for s in range(-9, 0):
         assert fldce.status_string(s) != "unknown status"
     assert fldce.status_string(-99) == "unknown status"
     assert fldce.fldce_version() == 2
@@ -146,6 +146,37 @@ def _fwd_only(L, **kw):
              wsb=1 << 40, stream=None)
     a.update(kw)
     return L.fldce_fwd(*a.values())
+
+
+def _fwd_noalloc(L, **kw):
+    a = dict(h=P, W=P, bias=None, target=P, p_mask=None, N=16, H=64, V=100, dtype=1, ignore=-100,
+             eps=0.0, s=1.0, red=1, total=0, eob=-1, eob_w=1.0, loss=P, lse=None, rl=None,
+             stream=None)
+    a.update(kw)
+    return L.fldce_fwd_noalloc(*a.values())
+
+
+def test_noalloc_argument_checks(L):
+    """The allocation-free forward rejects what fldce_fwd rejects, and any
+    call whose intermediates exceed its fixed device array, before it looks
+    at a device."""
+    f = _fwd_noalloc
+    assert f(L, W=None) == -1
+    assert f(L, loss=None) == -1
+    assert f(L, dtype=2) == -3
+    assert f(L, N=-1) == -2
+    assert f(L, red=3) == -4
+    assert f(L, s=0.0) == -4
+    assert f(L, eob=5, eob_w=-1.0) == -4
+    assert f(L, bias=BAD) == -6
+    assert f(L, H=96) == -8
+    lim = fldce.NOALLOC_SCRATCH_BYTES
+    assert fldce.fldce_fwd_workspace_size(3378, 2560, 151936, 1) <= lim
+    assert fldce.fldce_fwd_workspace_size(3379, 2560, 151936, 1) > lim
+    assert f(L, N=3379, H=2560, V=151936) == -9
+    assert f(L, N=8192, H=2560, V=151936) == -9
+    assert "FLDCE_NOALLOC_SCRATCH_BYTES" in fldce.status_string(-9)
+    assert f"((size_t){lim >> 20} << 20)" in open(HEADER).read()
 
 
 @pytest.mark.parametrize("f", [_ex, _fwd_only])
