@@ -345,15 +345,37 @@ struct LogitsArgs {
   int group_m;
 };
 
+// active: the wave's 128 vocabulary rows start below V (else it only takes
+// part in the block-wide E store, with zeros).
+//
+// With a store, the tile goes through LDS as [token][vocabulary] (free after
+// the main loop) and E is written as whole 512-byte row pieces.  A lane
+// holds 4 consecutive vocabulary entries of one token per sub-tile: one
+// 8-byte LDS write as soon as they are computed; 16-byte chunk ch of staged
+// row t sits at ch ^ (t & 15), so the 16 tokens one write instruction touches
+// fall on distinct bank groups and the 16-byte row reads are conflict-free.
+// Entries past V are zero.
 template <int kEpi, int kStore, bool kFull>
 __device__ __forceinline__ void logits_epilogue(Acc& acc, const LogitsArgs& a, int C, int m0,
-                                                int n0, int wm, int wn, int lane,
+                                                int n0, int wm, int wn, int lane, bool active,
                                                 const int (&jrow)[kTN], const float (&rl2)[kTN],
-                                                const int (&tc)[kTN]) {
+                                                const int (&tc)[kTN], char* smem) {
   const int V = a.V;
   const float s = a.s, sl = s * kLog2e;
   const int vbase = m0 + wm * kTM * 16;
   auto in_v = [&](int i, int r) { return kFull || m0 + acc_row(wm, i, lane, r) < V; };
+  bf16* stg = reinterpret_cast<bf16*>(smem);  // [256][256]
+  if constexpr (kStore != kStoreNone) {
+    __syncthreads();  // every wave is done with the operand stages
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  auto put = [&](int i, int j, const floatx4& v) {
+    const int tl = acc_col(wn, j, lane), vl = acc_row(wm, i, lane, 0);
+    bf16x4 b;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) b[r] = (kFull || m0 + vl + r < V) ? (bf16)v[r] : (bf16)0.f;
+    *(bf16x4*)&stg[tl * kBM + ((((vl >> 3) ^ (tl & 15)) << 3) | (vl & 7))] = b;
+  };
   if constexpr (kEpi == kEpiMax || kEpi == kEpiRef) {
     float mx[kTN], sum[kTN], rs[kTN];
     if constexpr (kEpi == kEpiMax) {
@@ -385,22 +407,32 @@ __device__ __forceinline__ void logits_epilogue(Acc& acc, const LogitsArgs& a, i
               if (a.rpart != nullptr) rs[j] += acc[i][j][r];
             }
       }
-    } else {  // kEpiRef: e = 2^((z - r) log2 e), replacing the accumulator with kStoreExp
+    } else {  // kEpiRef: e = 2^((z - r) log2 e)
+#pragma unroll
+      for (int j = 0; j < kTN; ++j) {  // row sums of z first, so each e frees its accumulator
+        rs[j] = 0.f;
+        if (a.rpart != nullptr) {
+#pragma unroll
+          for (int i = 0; i < kTM; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (in_v(i, r)) rs[j] += acc[i][j][r];
+        }
+      }
 #pragma unroll
       for (int j = 0; j < kTN; ++j) {
         sum[j] = 0.f;
-        rs[j] = 0.f;
 #pragma unroll
-        for (int i = 0; i < kTM; ++i)
+        for (int i = 0; i < kTM; ++i) {
+          floatx4 e;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float e = fast_exp2(__builtin_fmaf(acc[i][j][r], sl, -rl2[j]));
-            if (in_v(i, r)) {
-              if (a.rpart != nullptr) rs[j] += acc[i][j][r];
-              sum[j] += e;
-            }
-            if constexpr (kStore == kStoreExp) acc[i][j][r] = e;
+            e[r] = fast_exp2(__builtin_fmaf(acc[i][j][r], sl, -rl2[j]));
+            if (in_v(i, r)) sum[j] += e[r];
           }
+          if constexpr (kStore == kStoreExp) put(i, j, e);
+          if constexpr (kStore == kStoreRaw) put(i, j, acc[i][j]);
+        }
       }
     }
 #pragma unroll
@@ -412,7 +444,7 @@ __device__ __forceinline__ void logits_epilogue(Acc& acc, const LogitsArgs& a, i
         rs[j] += __shfl_xor(rs[j], 32, 64);
       }
     }
-    if (lane < 16) {
+    if (active && lane < 16) {
 #pragma unroll
       for (int j = 0; j < kTN; ++j) {
         const int tok = n0 + acc_col(wn, j, lane);
@@ -427,34 +459,33 @@ __device__ __forceinline__ void logits_epilogue(Acc& acc, const LogitsArgs& a, i
 #pragma unroll
     for (int i = 0; i < kTM; ++i)
 #pragma unroll
-      for (int j = 0; j < kTN; ++j)
+      for (int j = 0; j < kTN; ++j) {
+        floatx4 e;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float e = fast_exp2(__builtin_fmaf(acc[i][j][r], sl, -rl2[j]));
-          if (m0 + acc_row(wm, i, lane, r) == tc[j]) e -= a.tsub;
-          acc[i][j][r] = e;
+          e[r] = fast_exp2(__builtin_fmaf(acc[i][j][r], sl, -rl2[j]));
+          if (m0 + acc_row(wm, i, lane, r) == tc[j]) e[r] -= a.tsub;
         }
+        put(i, j, e);
+      }
+  } else {  // kEpiNone: the logits themselves
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+      for (int j = 0; j < kTN; ++j) put(i, j, acc[i][j]);
   }
   if constexpr (kStore != kStoreNone) {
-    // a lane holds 4 consecutive vocabulary entries of a token: one 8-byte
-    // store; 16 lanes write 16 tokens' rows, the next sub-tile continues them
-#pragma unroll
-    for (int j = 0; j < kTN; ++j) {
-      const int tok = n0 + acc_col(wn, j, lane);
-      if (tok >= C) continue;
-      bf16* er = a.E + (int64_t)jrow[j] * a.ldE;
-#pragma unroll
-      for (int i = 0; i < kTM; ++i) {
-        const int row0 = m0 + acc_row(wm, i, lane, 0);
-        bf16x4 v;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = (bf16)acc[i][j][r];
-        if (kFull || row0 + 3 < V) {
-          __builtin_nontemporal_store(v, (bf16x4*)(er + row0));  // read back by the backward GEMMs
-        } else if (row0 < a.ldE) {  // the padding columns V .. ldE - 1 are zero
-#pragma unroll
-          for (int r = 0; r < 4; ++r) er[row0 + r] = row0 + r < V ? v[r] : (bf16)0.f;
-        }
+    __syncthreads();
+#pragma unroll 4
+    for (int p = 0; p < kBM * kBN / 8 / kGemmThreads; ++p) {
+      const int u = threadIdx.x + kGemmThreads * p;
+      const int tl = u / (kBM / 8), ch = u % (kBM / 8);
+      const int tok = n0 + tl;
+      const int64_t col = m0 + ch * 8;
+      if (tok < C && col < a.ldE) {  // ldE % 64 == 0: a chunk is wholly in or out
+        const int jr = a.gidx != nullptr ? a.gidx[tok] : tok;
+        __builtin_nontemporal_store(*(const bf16x8*)&stg[tl * kBM + ((ch ^ (tl & 15)) << 3)],
+                                    (bf16x8*)(a.E + (int64_t)jr * a.ldE + col));
       }
     }
   }
@@ -472,7 +503,9 @@ __device__ __forceinline__ void logits_tile(const LogitsArgs& a, int C, int tm, 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN;
   const int vbase = m0 + wm * kTM * 16;
-  if (vbase >= a.V) return;
+  const bool active = vbase < a.V;  // uniform over the wave
+  // waves past V return, unless the E store's barriers need every wave
+  if (kStore == kStoreNone && !active) return;
   const bool full = vbase + kTM * 16 <= a.V;
   if (a.bias != nullptr) {  // F.linear's bias, before the logit scale
     bf16x4 bv[kTM];  // rows row0 .. row0 + 3 of sub-tile i (row0 % 4 == 0): one 8-byte load
@@ -511,9 +544,11 @@ __device__ __forceinline__ void logits_tile(const LogitsArgs& a, int C, int tm, 
     if constexpr (kEpi == kEpiLse) tc[j] = a.tcol[jrow[j]];
   }
   if (full)
-    logits_epilogue<kEpi, kStore, true>(acc, a, C, m0, n0, wm, wn, lane, jrow, rl2, tc);
+    logits_epilogue<kEpi, kStore, true>(acc, a, C, m0, n0, wm, wn, lane, active, jrow, rl2, tc,
+                                        smem);
   else
-    logits_epilogue<kEpi, kStore, false>(acc, a, C, m0, n0, wm, wn, lane, jrow, rl2, tc);
+    logits_epilogue<kEpi, kStore, false>(acc, a, C, m0, n0, wm, wn, lane, active, jrow, rl2, tc,
+                                         smem);
 }
 
 template <int kEpi, int kStore, bool kIndirect>
@@ -638,10 +673,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dh_bf16(
 // kMode 3: out (bf16) = acc32 + acc              (last chunk)
 // acc32 keeps each tile in the accumulators' own register layout (tile,
 // then sub-tile (i, j), then thread, 4 floats each), so a thread reads and
-// writes its 128 values as 32 coalesced 16-byte pieces.  Modes 2 and 3
-// load them into the accumulators before the main loop, which then adds
-// this chunk's products on top (the loads overlap the first operand
-// loads); modes 1 and 2 end with plain stores.
+// writes its 128 values as 32 coalesced 16-byte pieces.  Mode 2 loads them
+// into the accumulators before the main loop, which then adds this chunk's
+// products on top (the loads overlap the first operand loads), and ends with
+// plain stores, as mode 1 does; mode 3 adds them after its main loop (a
+// preload there leaves too few registers for its bf16 epilogue).
 // ---------------------------------------------------------------------------
 // The chunk's tokens: Kp = the padded count (multiple of 64), or, when
 // count != nullptr, min(*count - c0, cmax) rounded up to 64.
@@ -663,7 +699,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dw_bf16(
   Acc acc;  // acc[i][j][r] = dW[v0 + acc_col(wn, j)][h0 + acc_row(wm, i, r)]
   floatx4* t32 = reinterpret_cast<floatx4*>(acc32) +
                  ((int64_t)tc.tm * cdiv(H, kBN) + tc.tn) * (kTM * kTN * kGemmThreads) + threadIdx.x;
-  if constexpr (kMode >= 2) {
+  if constexpr (kMode == 2) {
 #pragma unroll
     for (int i = 0; i < kTM; ++i)
 #pragma unroll
@@ -673,6 +709,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dw_bf16(
   } else {
     gemm_mainloop<false, true>(hT, ldh, H, 0, h0, E, ldE, max(Kp, 1), (int)ldE, v0, 0, Kp / kBK,
                                smem, acc);
+  }
+  if constexpr (kMode == 3) {  // (after the main loop, where the operand registers are free)
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+      for (int j = 0; j < kTN; ++j) acc[i][j] += __builtin_nontemporal_load(t32 + (i * kTN + j) * kGemmThreads);
   }
   if constexpr (kMode == 1 || kMode == 2) {  // carried to the next chunk in fp32
 #pragma unroll
