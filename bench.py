@@ -159,7 +159,7 @@ def _durations(trace_csv: str) -> dict:
     return out
 
 
-def counter_summary(run_dirs, workload: str, cmd: str) -> int:
+def counter_summary(run_dirs, workload: str, cmd: str, calib_mib: int) -> int:
     """Per stage kernel, averages over its launches of the counters of several
     rocprofv3 --pmc --kernel-trace runs (one directory each): the average
     shader clock (GRBM_GUI_ACTIVE cycles over the launch's duration), MFMA
@@ -194,6 +194,13 @@ def counter_summary(run_dirs, workload: str, cmd: str) -> int:
                 if disp in dur:
                     durs.setdefault(name, []).append(dur[disp])
     avg = lambda xs: sum(xs) / len(xs) if xs else float("nan")  # noqa: E731
+    # FETCH_SIZE / WRITE_SIZE scaled by what they read for the calibration copy
+    # of calib_mib MiB (the run's first device copy)
+    scale = {}
+    for cname in ("FETCH_SIZE", "WRITE_SIZE"):
+        cal = [v for (k, c), v in vals.items() if c == cname and
+               ("copy" in k.lower() or "elementwise" in k.lower())]
+        scale[cname] = calib_mib * 1024.0 / max(cal[0]) if cal and calib_mib else 1.0
     kernels = SHARD_STAGE_KERNELS if workload == "shard" else STAGE_KERNELS
     lines = [f"# Counters per launch of the stage kernels, {workload} workload", "",
              "rocprofv3 --pmc runs with --kernel-trace (one counter group per run), each", "",
@@ -205,7 +212,9 @@ def counter_summary(run_dirs, workload: str, cmd: str) -> int:
              "MFMA TFLOP = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; DRAM share = TCC_EA0_RDREQ_DRAM / "
              "TCC_EA0_RDREQ and TCC_EA0_WRREQ_DRAM / TCC_EA0_WRREQ (L2 requests to local HBM "
              "addresses, which the memory-side MALL may serve; no counter here separates "
-             "MALL hits); fetch / write = FETCH_SIZE / WRITE_SIZE.", "",
+             f"MALL hits); fetch / write = FETCH_SIZE / WRITE_SIZE scaled by what they read for "
+             f"a {calib_mib} MiB device copy (read x {scale['FETCH_SIZE']:.3f}, write x "
+             f"{scale['WRITE_SIZE']:.3f}).", "",
              "| stage | kernel | launches | ms | clock GHz | MFMA busy % | MFMA TFLOP/s | "
              "VALU busy % | LDS active % | fetch GB | write GB | DRAM read / write share |",
              "|---|---|---|---|---|---|---|---|---|---|---|---|"]
@@ -222,8 +231,8 @@ def counter_summary(run_dirs, workload: str, cmd: str) -> int:
         valu = 100.0 * g("SQ_ACTIVE_INST_VALU") / (256.0 * gui)
         lds = 100.0 * g("SQ_LDS_IDX_ACTIVE") / (256.0 * gui)
         tf = g("SQ_INSTS_VALU_MFMA_MOPS_BF16") * 512.0 / (ms * 1e-3) / 1e12
-        fetch = g("FETCH_SIZE") * 1024 / 1e9
-        write = g("WRITE_SIZE") * 1024 / 1e9
+        fetch = g("FETCH_SIZE") * 1024 * scale["FETCH_SIZE"] / 1e9
+        write = g("WRITE_SIZE") * 1024 * scale["WRITE_SIZE"] / 1e9
         rd = g("TCC_EA0_RDREQ_DRAM_sum") / g("TCC_EA0_RDREQ_sum")
         wr = g("TCC_EA0_WRREQ_DRAM_sum") / g("TCC_EA0_WRREQ_sum")
         lines.append(f"| {stage} | {kname} | {len(durs.get(k, []))} | {ms:.3f} | {clock:.2f} | "
@@ -478,7 +487,8 @@ def main() -> int:
                          "default so that the plain step is the only user of its logits kernel")
     args = ap.parse_args()
     if args.counter_summary:
-        return counter_summary(args.counter_summary, args.workload, args.counter_cmd)
+        return counter_summary(args.counter_summary, args.workload, args.counter_cmd,
+                               args.calib_mib)
     if args.traffic_summary:
         return traffic_summary(args.traffic_summary[0], args.traffic_summary[1], args.workload,
                                args.calib_mib)

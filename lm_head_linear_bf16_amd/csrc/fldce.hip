@@ -55,7 +55,7 @@ struct Plan {
   size_t oD = 0, oWT = 0, oColpart = 0, oWsum = 0, oZt = 0, oR = 0, oLse = 0, oRloss = 0,
          oCoef = 0, oAlpha = 0, oPart = 0, oRpart = 0, oZ = 0, oGT = 0, oHT = 0, oDHpart = 0,
          oDW32 = 0, oRows = 0, oCount = 0, oTcol = 0, oBsum = 0, oDbpart = 0, oHC = 0,
-         oFlag = 0, oFlist = 0, oUpart = 0, oU = 0;
+         oFlag = 0, oFlist = 0, oUpart = 0, oU = 0, oWcolpart = 0;
   int64_t db_blocks = 0;  // row blocks of db partials (64 rows each, over all chunks)
   int64_t u_blocks = 0;   // row blocks of smoothing-term partials (64 rows each, over all chunks)
   size_t total = 0;
@@ -148,6 +148,7 @@ Plan make_plan(int mode, int64_t N, int64_t H, int64_t V, int dtype, int64_t chu
     p.u_blocks = row_blocks(N, p.C);
     p.oUpart = take(cur, (size_t)p.u_blocks * (H + 1) * 4);
     p.oU = take(cur, (size_t)(H + 1) * 4);
+    p.oWcolpart = take(cur, (size_t)cdiv(V, 256) * H * 4);  // 256-row slabs of sum_v W_v
     // the device picks the split count S for the rows that exist (fewer than
     // C when rows are ignored, plus the all-ones row when eps > 0) and stores
     // S x rows x H partials; reserve the largest such product over every
@@ -497,7 +498,20 @@ int run_core_bf16(const Core& c, const Plan& p, char* ws, hipStream_t st) {
   // relative to the lse
   float* alpha = (given_lse && !exact) ? coef : reinterpret_cast<float*>(ws + p.oAlpha);
   const bool fused_smooth = smooth && !exact;
-  const int extra = (c.dH != nullptr && fused_smooth) ? 1 : 0;  // all-ones row of E: sum_v W_v
+  // sum_v W_v for the smoothing term of dH: from an all-ones row of E with
+  // one chunk (free unless the row count is a multiple of 256), else from a
+  // column sum of W once per call (an extra row would add a token tile to
+  // every full chunk)
+  const int extra = (c.dH != nullptr && fused_smooth && p.nchunks == 1) ? 1 : 0;
+  float* wsum = nullptr;
+  if (c.dH != nullptr && fused_smooth && p.nchunks > 1) {
+    StageTimer tm(kPrep, st);
+    wsum = reinterpret_cast<float*>(ws + p.oWsum);
+    float* colpart = reinterpret_cast<float*>(ws + p.oWcolpart);
+    dim3 g((unsigned)cdiv(V, 256), (unsigned)cdiv(H, 2048));
+    k_colsum_slabs_bf16<<<g, 256, 0, st>>>(W, V, H, colpart);
+    k_colsum_finish<float><<<grid1(H, 256), 256, 0, st>>>(colpart, cdiv(V, 256), H, H, wsum);
+  }
   const bool need_u = fused_smooth && (c.dW != nullptr || c.db != nullptr);
   const float epsV = c.eps / (float)c.Vg;
   int64_t db_off = 0, u_off = 0;  // row blocks of db / smoothing-term partials written so far
@@ -604,18 +618,19 @@ int run_core_bf16(const Core& c, const Plan& p, char* ws, hipStream_t st) {
         StageTimer tm(kDHGemm, st);
         k_gemm_dh_bf16<<<blocks, kGemmThreads, kGemmLds, st>>>(
             E, Vp, (int)cmax, extra, c.count, c0, W, (int)V, (int)H, (int)(Vp / kBK), S, dHpart,
-            kGroupMBwd, c.dH, c.dH_f32 ? 1 : 0, c.rows, alpha);
+            kGroupMBwd, c.dH, c.dH_f32 ? 1 : 0, c.rows, alpha, coef, wsum, epsV);
       }
       StageTimer tm(kDHReduce, st);
       if (S > 1 || extra) {  // (the kernel returns at once when the GEMM wrote the rows)
         const unsigned g = (unsigned)std::min<int64_t>(cmax, 2048);
         if (c.dH_f32)
           k_splitk_scatter<float><<<g, 256, 0, st>>>(dHpart, S, Vp / kBK, cmax, extra, H, c.rows,
-                                                     c.count, c0, alpha, coef, epsV,
+                                                     c.count, c0, alpha, coef, epsV, wsum,
                                                      (float*)c.dH);
         else
           k_splitk_scatter<bf16><<<g, 256, 0, st>>>(dHpart, S, Vp / kBK, cmax, extra, H, c.rows,
-                                                    c.count, c0, alpha, coef, epsV, (bf16*)c.dH);
+                                                    c.count, c0, alpha, coef, epsV, wsum,
+                                                    (bf16*)c.dH);
       }
     }
     if (c.dW != nullptr) {  // 4. dW += (alpha h)^T E, the smoothing term with the final value

@@ -591,14 +591,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_logits_bf16(const LogitsArg
 // them, whose product is sum_v W_v for the smoothing term), and the split
 // count is chosen for them (choose_splits; k_splitk_scatter recomputes it).
 // With a single split and no extra row there is nothing to reduce: the
-// epilogue writes alpha_m times row m straight to row rows[c0 + m] of dst
-// (fp32 when dst_f32, else bf16) and the reduction kernel returns at once.
+// epilogue writes alpha_m times row m, minus coef_m epsV wsum when wsum is
+// given, straight to row rows[c0 + m] of dst (fp32 when dst_f32, else bf16)
+// and the reduction kernel returns at once.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dh_bf16(
     const bf16* __restrict__ E, int64_t ldE, int M, int extra, const int* __restrict__ count,
     int64_t c0, const bf16* __restrict__ W, int V, int H, int k_tiles, int max_splits,
     float* __restrict__ out, int group_m, void* __restrict__ dst, int dst_f32,
-    const int* __restrict__ rows, const float* __restrict__ alpha) {
+    const int* __restrict__ rows, const float* __restrict__ alpha, const float* __restrict__ coef,
+    const float* __restrict__ wsum, float epsV) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   int Me = M;
   if (count != nullptr) {
@@ -626,13 +628,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dh_bf16(
         const int row = m0 + acc_row(wm, i, lane, r);
         if (row >= Mr) continue;
         const int64_t drow = (int64_t)rows[c0 + row] * H;
-        const float al = alpha[row];
+        const float al = alpha[row], ce = wsum != nullptr ? coef[row] * epsV : 0.f;
 #pragma unroll
         for (int j = 0; j < kTN; ++j) {
           const int col = n0 + acc_col(wn, j, lane);
           if (col >= H) continue;
-          if (dst_f32) static_cast<float*>(dst)[drow + col] = al * acc[i][j][r];
-          else static_cast<bf16*>(dst)[drow + col] = (bf16)(al * acc[i][j][r]);
+          const float v = al * acc[i][j][r] - (wsum != nullptr ? ce * wsum[col] : 0.f);
+          if (dst_f32) static_cast<float*>(dst)[drow + col] = v;
+          else static_cast<bf16*>(dst)[drow + col] = (bf16)v;
         }
       }
     return;

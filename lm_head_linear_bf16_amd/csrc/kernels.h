@@ -214,6 +214,27 @@ __global__ __launch_bounds__(256) void k_transpose_gather_bf16(const bf16* __res
   }
 }
 
+// Column sums of each 256-row slab of a bf16 matrix src [R, Cn] (Cn % 8 ==
+// 0): colpart[slab, c] in float32, rows in order.  Eight columns per thread
+// (16-byte loads), 256 threads = 2048 columns per block.  Used for
+// sum_v W_v, the label-smoothing term of dH, when it is not taken from an
+// all-ones row of the dH GEMM.
+__global__ __launch_bounds__(256) void k_colsum_slabs_bf16(const bf16* __restrict__ src, int64_t R,
+                                                           int64_t Cn,
+                                                           float* __restrict__ colpart) {
+  const int64_t c = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 8;
+  if (c >= Cn) return;
+  const int64_t r0 = (int64_t)blockIdx.x * 256, r1 = min(R, r0 + 256);
+  float acc[8] = {};
+  for (int64_t r = r0; r < r1; ++r) {
+    const bf16x8 v = *(const bf16x8*)(src + r * Cn + c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += (float)v[e];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) colpart[(int64_t)blockIdx.x * Cn + c + e] = acc[e];
+}
+
 // out[c] = sum_b part[b * ld + c] for c < Cn, b ascending, cast to T.
 template <typename T>
 __global__ __launch_bounds__(256) void k_colsum_finish(const float* __restrict__ part, int64_t nb,
@@ -617,10 +638,11 @@ __global__ __launch_bounds__(256) void k_scale_grad(const float* __restrict__ gr
 }
 
 // dH rows of a compacted chunk: out[rows[c0 + j], :] = alpha_j P_j - coef_j
-// epsV P_C for j < C, the chunk's row count, with P_m = sum_s part[s][m][:]
-// (s ascending) and P_C the product of the all-ones row after the C rows
-// (sum_v W_v) when extra == 1; S = choose_splits for C + extra rows, exactly
-// as the dH GEMM chose it (nothing to do when it wrote the rows itself).
+// epsV w for j < C, the chunk's row count, with P_m = sum_s part[s][m][:]
+// (s ascending) and w = sum_v W_v: the product P_C of the all-ones row after
+// the C rows when extra == 1, else wsum when given, else 0; S =
+// choose_splits for C + extra rows, exactly as the dH GEMM chose it (nothing
+// to do when it wrote the rows itself).
 template <typename Tout>
 __global__ __launch_bounds__(256) void k_splitk_scatter(const float* __restrict__ part,
                                                         int max_splits, int64_t k_tiles,
@@ -629,6 +651,7 @@ __global__ __launch_bounds__(256) void k_splitk_scatter(const float* __restrict_
                                                         const int* __restrict__ count, int64_t c0,
                                                         const float* __restrict__ alpha,
                                                         const float* __restrict__ coef, float epsV,
+                                                        const float* __restrict__ wsum,
                                                         Tout* __restrict__ out) {
   const int64_t C = chunk_rows(count, c0, cmax);
   const int64_t Me = C + extra;
@@ -637,7 +660,7 @@ __global__ __launch_bounds__(256) void k_splitk_scatter(const float* __restrict_
   const int64_t MN = Me * H;  // partials [split][Me][H]
   for (int64_t j = blockIdx.x; j < C; j += gridDim.x) {  // chunk rows, grid-strided
     const int64_t dst = (int64_t)rows[c0 + j] * H;
-    const float al = alpha[j], ce = extra ? coef[j] * epsV : 0.f;
+    const float al = alpha[j], ce = (extra || wsum != nullptr) ? coef[j] * epsV : 0.f;
     for (int64_t e = (int64_t)threadIdx.x * 4; e < H; e += 256 * 4) {
       const int64_t src = j * H + e;
       if (e + 4 <= H) {
@@ -646,6 +669,8 @@ __global__ __launch_bounds__(256) void k_splitk_scatter(const float* __restrict_
         floatx4 ws = floatx4{};
         if (extra)
           for (int s = 0; s < S; ++s) ws += *(const floatx4*)(part + (int64_t)s * MN + C * H + e);
+        else if (wsum != nullptr)
+          ws = *(const floatx4*)(wsum + e);
 #pragma unroll
         for (int k = 0; k < 4; ++k) out[dst + e + k] = from_f32<Tout>(al * acc[k] - ce * ws[k]);
       } else {
@@ -654,6 +679,8 @@ __global__ __launch_bounds__(256) void k_splitk_scatter(const float* __restrict_
           for (int s = 1; s < S; ++s) a += part[(int64_t)s * MN + src + k];
           if (extra)
             for (int s = 0; s < S; ++s) w += part[(int64_t)s * MN + C * H + e + k];
+          else if (wsum != nullptr)
+            w = wsum[e + k];
           out[dst + e + k] = from_f32<Tout>(al * a - ce * w);
         }
       }
