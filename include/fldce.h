@@ -77,8 +77,9 @@ enum fldce_status {
   FLDCE_ERR_ALIGNMENT = -6,      /* a pointer is not 16-byte aligned          */
   FLDCE_ERR_HIP = -7,            /* a kernel launch failed                    */
   FLDCE_ERR_UNSUPPORTED = -8,    /* shape the kernels do not handle: bf16 with
-                                    H not a multiple of 64 or a GEMM grid of
-                                    2^32 work-items or more; fp32 with V >= 2^30 */
+                                    H not a multiple of 64, V >= 2^23 or a GEMM
+                                    grid of 2^32 work-items or more; fp32 with
+                                    V >= 2^30 */
   FLDCE_ERR_SCRATCH_TOO_SMALL = -9 /* fldce_fwd_noalloc: the call needs more
                                     than FLDCE_NOALLOC_SCRATCH_BYTES */
 };
@@ -93,10 +94,10 @@ int fldce_version(void);
 const char* fldce_status_string(int status);
 
 /* Token rows processed per chunk when chunk_rows == 0 is passed with bf16
- * inputs: all N rows while the chunk's two [C, V] buffers (logits and their
- * gradient, 2 bytes each) stay within 16 GiB, else the largest multiple of
- * 256 that fits (fp32 inputs keep 4-byte buffers, so half as many rows when
- * that bound binds).  Page 1 chunks rows to bound the [C, V] logits buffer;
+ * inputs: all N rows while twice the chunk's [C, V] bf16 buffer of the
+ * backward operand stays within 16 GiB, else the largest multiple of 256
+ * that fits, and at most 2^22 (fp32 inputs keep two 4-byte buffers, so half
+ * as many rows when that bound binds).  Page 1 chunks rows to bound the [C, V] logits buffer;
  * 288 GB of HBM lets one chunk cover every workload here.  H is unused. */
 int64_t fldce_default_chunk_rows(int64_t N, int64_t H, int64_t V);
 
@@ -138,8 +139,10 @@ size_t fldce_workspace_size(int64_t N, int64_t H, int64_t V, int dtype,
  * Sizes: 0 <= N < 2^28, 0 < V < 2^31, 0 < H <= 2^20 (FLDCE_ERR_BAD_SHAPE
  * otherwise, and the workspace queries return 0); the same range holds for
  * every entry point below (V_local in place of V for the shard calls).
- * bf16 requires H % 64 == 0 (FLDCE_ERR_UNSUPPORTED otherwise); all pointers
- * must be 16-byte aligned.
+ * bf16 requires H % 64 == 0 and V < 2^23 (FLDCE_ERR_UNSUPPORTED otherwise;
+ * the same bound applies to V_local below); all pointers must be 16-byte
+ * aligned.  bf16 chunks hold at most 2^22 rows (a larger chunk_rows is
+ * lowered to it).
  */
 int fldce_fwd_bwd(const void* h, const void* W, const int64_t* target,
                   const float* p_mask, int64_t N, int64_t H, int64_t V,

@@ -37,6 +37,10 @@ namespace {
 enum Mode { kFwdBwd = 0, kShardPartials = 1, kShardBwd = 2, kFwd = 3 };
 
 constexpr int64_t kZBudgetBytes = int64_t(16) << 30;  // chunk logits + g^T buffers
+// bf16: largest vocabulary, and most rows per chunk (the (alpha h)^T operand
+// of dW has a row of chunk length; 256 of them must span less than 4 GiB)
+constexpr int64_t kMaxVocabBf16 = int64_t(1) << 23;
+constexpr int64_t kMaxChunkBf16 = int64_t(1) << 22;
 // Label smoothing above which the backward operand is g itself, formed from
 // stored logits in one pass, rather than the exponentials E with the
 // smoothing share added to the products: that share, eps / V of every entry,
@@ -96,6 +100,7 @@ Plan make_plan(int mode, int64_t N, int64_t H, int64_t V, int dtype, int64_t chu
   } else {
     p.C = chunk_rows > 0 ? std::min<int64_t>(chunk_rows, std::max<int64_t>(N, 1))
                          : default_chunk(N, V, p.esz);
+    if (bf) p.C = std::min(p.C, kMaxChunkBf16);
   }
   // bf16: one row more than the chunk for the all-ones row of the smoothing term
   p.Cp = round_up(p.C + (bf ? 1 : 0), 64);
@@ -297,6 +302,9 @@ int check_common(const void* h, const void* W, const int64_t* target, int64_t N,
   if (!sizes_in_range(N, H, V)) return FLDCE_ERR_BAD_SHAPE;
   if (!(logit_scale > 0.f) || !std::isfinite(logit_scale)) return FLDCE_ERR_BAD_ARGUMENT;
   if (dtype == FLDCE_DTYPE_BF16 && H % kBK != 0) return FLDCE_ERR_UNSUPPORTED;
+  // bf16 operand tiles are read through buffers: 256 rows of the longest row
+  // (V, padded) must span less than 4 GiB
+  if (dtype == FLDCE_DTYPE_BF16 && V >= kMaxVocabBf16) return FLDCE_ERR_UNSUPPORTED;
   // fp32 kernels put 4 work-items per vocabulary row on one grid dimension
   if (dtype == FLDCE_DTYPE_F32 && V >= (int64_t(1) << 30)) return FLDCE_ERR_UNSUPPORTED;
   return FLDCE_OK;
@@ -911,8 +919,8 @@ const char* fldce_status_string(int status) {
     case FLDCE_ERR_ALIGNMENT: return "a pointer is not 16-byte aligned";
     case FLDCE_ERR_HIP: return "a HIP kernel launch failed";
     case FLDCE_ERR_UNSUPPORTED:
-      return "shape not supported by the bf16 path (H must be a multiple of 64; each GEMM grid "
-             "must hold fewer than 2^32 work-items)";
+      return "shape not supported by the bf16 path (H must be a multiple of 64, V below 2^23; "
+             "each GEMM grid must hold fewer than 2^32 work-items)";
     case FLDCE_ERR_SCRATCH_TOO_SMALL:
       return "the call needs more than the FLDCE_NOALLOC_SCRATCH_BYTES of the allocation-free "
              "entry point (use fldce_fwd with a workspace)";
@@ -923,7 +931,7 @@ const char* fldce_status_string(int status) {
 int64_t fldce_default_chunk_rows(int64_t N, int64_t H, int64_t V) {
   (void)H;
   if (N < 0 || V <= 0) return 0;
-  return default_chunk(N, V, 2);
+  return std::min(default_chunk(N, V, 2), kMaxChunkBf16);
 }
 
 size_t fldce_workspace_size(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_rows) {

@@ -28,8 +28,9 @@
 //     are walked in groups of `group_m` rows of tiles, so operand slabs are
 //     shared in that XCD's L2.
 //
-// Rows past M (or N) are loaded from the last valid row (loads stay in
-// bounds) and masked in the epilogues.  K must be a multiple of 64.
+// Rows past M (or N) are read as zeros (the buffer range ends at the last
+// valid row; gathered rows are clamped to the last valid one) and masked in
+// the epilogues.  K must be a multiple of 64.
 #pragma once
 
 #include "fldce_common.h"
@@ -118,33 +119,55 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int tr_swz(int r) { return (r & 3) | (((r >> 3) & 1) << 2); }
 
-template <bool kTr>
+// Buffer resources for the operand loads.  A raw buffer load takes its base
+// and byte range from a descriptor in scalar registers, a per-lane byte
+// offset from a vector register and a wave-uniform byte offset from a scalar
+// register; lanes whose vector offset is at or past the range read zero
+// without touching memory (the scalar offset is not range-checked).  So the
+// per-lane offsets are computed once per tile and each K step changes only
+// scalars.  Third descriptor word: raw 32-bit data of the gfx9 family.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kRsrcWord3 = 0x00020000;
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)n,
+                                           kRsrcWord3);
+}
+__device__ __forceinline__ void buffer_to_lds(Rsrc r, char* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, FLDCE_LPTR(lds), 16, voff, soff, 0, 0);
+}
+
+template <bool kTr, bool kGather = false>
 struct Tile;
 
+// K contiguous, rows read through a buffer whose range ends at the last
+// valid row: rows past it load as zeros.  Per lane the row offset r * ldx
+// (r < 256) is in the vector offset, K (k_begin + 64 t) in the scalar one.
+// Needs 256 * ldx * 2 < 2^32 (ldx < 2^23), which the entry points ensure.
 template <>
-struct Tile<false> {
+struct Tile<false, false> {
   static constexpr int kReads = 1;  // LDS reads per fragment
-  const bf16* p[4];
-  // rows = number of valid rows (M or N); r0 = first row of the tile.  With
-  // gidx, tile row q is source row gidx[goff + q] (a gather), else goff + q.
+  Rsrc rs;
+  uint32_t voff[4];
+  uint32_t kb;  // K offset in bytes
+  // rows = number of valid rows (M or N); r0 = first row of the tile.
   __device__ __forceinline__ void init(const bf16* X, int64_t ldx, int rows, int cols, int r0,
                                        int64_t k_begin, int lane, int wave,
-                                       const int* gidx = nullptr, int64_t goff = 0) {
+                                       const int* = nullptr, int64_t = 0) {
     (void)cols;
+    rs = make_rsrc(X + (int64_t)r0 * ldx, (int64_t)(rows - r0) * ldx * 2);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = i * kWaves * 8 + wave * 8 + (lane >> 3);
-      const int64_t q = min(r0 + r, rows - 1);
-      const int64_t src = gidx != nullptr ? (int64_t)gidx[goff + q] : goff + q;
-      p[i] = X + src * ldx + lds_chunk(lane & 7, r) * 8 + k_begin;
+      voff[i] = (uint32_t)((int64_t)r * ldx * 2 + lds_chunk(lane & 7, r) * 16);
     }
+    kb = (uint32_t)(k_begin * 2);
   }
   __device__ __forceinline__ void issue(char* tile, int t, int wave) const {
     char* s = tile + wave * 8 * 128;
-    const int64_t ko = (int64_t)t * kBK;
+    const uint32_t so = kb + (uint32_t)t * (kBK * 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(FLDCE_GPTR(p[i] + ko), FLDCE_LPTR(s + i * kWaves * 8 * 128), 16, 0, 0);
+    for (int i = 0; i < 4; ++i) buffer_to_lds(rs, s + i * kWaves * 8 * 128, voff[i], so);
   }
   // fragments for 16-row sub-tiles at rows off + 16 t
   template <int T>
@@ -155,37 +178,72 @@ struct Tile<false> {
   }
 };
 
+// K contiguous, rows gathered: tile row q is source row gidx[goff + q]
+// (clamped to the valid rows), read with per-lane global addresses.
 template <>
-struct Tile<true> {
+struct Tile<false, true> {
+  static constexpr int kReads = 1;
+  const bf16* p[4];
+  __device__ __forceinline__ void init(const bf16* X, int64_t ldx, int rows, int cols, int r0,
+                                       int64_t k_begin, int lane, int wave,
+                                       const int* gidx = nullptr, int64_t goff = 0) {
+    (void)cols;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = i * kWaves * 8 + wave * 8 + (lane >> 3);
+      const int64_t q = min(r0 + r, rows - 1);
+      p[i] = X + (int64_t)gidx[goff + q] * ldx + lds_chunk(lane & 7, r) * 8 + k_begin;
+    }
+  }
+  __device__ __forceinline__ void issue(char* tile, int t, int wave) const {
+    char* s = tile + wave * 8 * 128;
+    const int64_t ko = (int64_t)t * kBK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(FLDCE_GPTR(p[i] + ko), FLDCE_LPTR(s + i * kWaves * 8 * 128), 16, 0, 0);
+  }
+  template <int T>
+  __device__ __forceinline__ void frags(const char* tile, int ks, int off, int lane, bf16x8 (&f)[T]) const {
+    Tile<false, false>().frags<T>(tile, ks, off, lane, f);
+  }
+};
+
+// K as the row index: each K step reads 64 source rows through a buffer
+// based at its first row (and the tile's first column), whose range ends at
+// the last valid row, so rows past it load as zeros; per lane the offset of
+// its row (< 64) and column is fixed.  Only scalars change per step.
+template <>
+struct Tile<true, false> {
   static constexpr int kReads = 2;
-  const bf16* p[4];  // column pointers (row 0 of the source)
-  int64_t ldx;
-  int krows, k_begin;
+  const bf16* X;  // column c0 of row 0
+  int64_t ldx, kb, tail;  // tail: bytes from column c0 of a row to the end of that row
+  int krows;
+  uint32_t voff[4];
   // rows = number of valid K rows of the source; cols = valid columns;
-  // r0 = first column of the tile; k_begin = first K row
-  __device__ __forceinline__ void init(const bf16* X, int64_t ld, int rows, int cols, int c0,
-                                       int64_t kb, int lane, int wave, const int* = nullptr,
+  // c0 = first column of the tile; kb = first K row
+  __device__ __forceinline__ void init(const bf16* X_, int64_t ld, int rows, int cols, int c0,
+                                       int64_t kb_, int lane, int wave, const int* = nullptr,
                                        int64_t = 0) {
+    X = X_ + c0;
     ldx = ld;
     krows = rows;
-    k_begin = (int)kb;
+    kb = kb_;
+    tail = (ld - c0) * 2;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = i * 16 + wave * 2 + (lane >> 5);  // LDS row this lane fills
       const int pos = lane & 31;                       // 16-byte unit in the 512 B row
       const int u = (((pos >> 1) ^ tr_swz(r)) << 1) | (pos & 1);
-      p[i] = X + min(c0 + u * 8, cols - 8);
+      voff[i] = (uint32_t)((int64_t)r * ld * 2 + (int64_t)(min(c0 + u * 8, cols - 8) - c0) * 2);
     }
   }
   __device__ __forceinline__ void issue(char* tile, int t, int wave) const {
     char* s = tile + wave * 2 * 512;
-    const int lane = threadIdx.x & 63;
+    const int64_t row0 = kb + (int64_t)t * kBK;
+    // valid bytes from the base: the rest of row row0 and the rows after it
+    const Rsrc rs = make_rsrc(X + row0 * ldx, (krows - row0 - 1) * ldx * 2 + tail);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = min(k_begin + t * kBK + i * 16 + wave * 2 + (lane >> 5), krows - 1);
-      __builtin_amdgcn_global_load_lds(FLDCE_GPTR(p[i] + (int64_t)row * ldx), FLDCE_LPTR(s + i * 16 * 512), 16,
-                                       0, 0);
-    }
+    for (int i = 0; i < 4; ++i) buffer_to_lds(rs, s + i * 16 * 512, voff[i], 0);
   }
   template <int T>
   __device__ __forceinline__ void frags(const char* tile, int ks, int off, int lane, bf16x8 (&f)[T]) const {
@@ -208,7 +266,7 @@ struct Tile<true> {
 // [kt0, kt0 + nk), starting from zero (kZeroAcc) or from the values the
 // caller put in acc.  For a normal operand X_rows/X_cols are (valid rows,
 // unused); for a transposed one (valid K rows, valid columns).
-template <bool kATr, bool kBTr, bool kZeroAcc = true>
+template <bool kATr, bool kBTr, bool kZeroAcc = true, bool kBGather = false>
 __device__ __forceinline__ void gemm_mainloop(const bf16* __restrict__ A, int64_t lda, int a_rows,
                                               int a_cols, int m0, const bf16* __restrict__ B,
                                               int64_t ldb, int b_rows, int b_cols, int n0, int64_t kt0,
@@ -226,7 +284,7 @@ __device__ __forceinline__ void gemm_mainloop(const bf16* __restrict__ A, int64_
   if (nk <= 0) return;
 
   Tile<kATr> ta;
-  Tile<kBTr> tb;
+  Tile<kBTr, kBGather> tb;
   ta.init(A, lda, a_rows, a_cols, m0, kt0 * kBK, lane, wave);
   tb.init(B, ldb, b_rows, b_cols, n0, kt0 * kBK, lane, wave, b_gidx, b_goff);
   auto issue = [&](int stage, int t) {
@@ -246,7 +304,7 @@ __device__ __forceinline__ void gemm_mainloop(const bf16* __restrict__ A, int64_
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
   };
   constexpr int NM = kTM * kTN, NH = NM / 2;
-  constexpr int ND = kTM * Tile<kATr>::kReads + kTN * Tile<kBTr>::kReads;
+  constexpr int ND = kTM * Tile<kATr>::kReads + kTN * Tile<kBTr, kBGather>::kReads;
   constexpr int ND1 = ND < NM ? ND : NM, ND2 = ND < NM - NH ? ND : NM - NH;
   bf16x8 fa0[kTM], fb0[kTN], fa1[kTM], fb1[kTN];
   issue(0, 0);
@@ -497,8 +555,8 @@ __device__ __forceinline__ void logits_tile(const LogitsArgs& a, int C, int tm, 
                                             char* smem) {
   const int m0 = tm * kBM, n0 = tn * kBN;
   Acc acc;
-  gemm_mainloop<false, false>(a.W, a.H, a.V, 0, m0, a.h, a.H, C, 0, n0, 0, a.H / kBK, smem, acc,
-                              kIndirect ? a.gidx : nullptr, 0);
+  gemm_mainloop<false, false, true, kIndirect>(a.W, a.H, a.V, 0, m0, a.h, a.H, C, 0, n0, 0,
+                                               a.H / kBK, smem, acc, a.gidx, 0);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN;

@@ -192,6 +192,8 @@ def test_extended_argument_checks(L, f):
     assert f(L, eob=-1, eob_w=-1.0, wsb=8) == -5  # no EOB: the weight is not checked
     assert f(L, bias=BAD) == -6
     assert f(L, H=96) == -8
+    assert f(L, V=1 << 23) == -8                  # bf16 reads its operands through buffers
+    assert f(L, V=(1 << 23) - 1, wsb=8) == -5     # just below: fails on the workspace only
     assert f(L, wsb=8) == -5
     if f is _ex:
         assert f(L, db=BAD) == -6
