@@ -85,17 +85,19 @@ def _counter_per_kernel(path: str, counter: str) -> dict:
 
 # the kernel instance each stage launches: plain fwd+bwd, and for the vocab
 # shard workload the shard partials and the shard backward
-STAGE_KERNELS = {"logits_gemm": "k_logits_bf16<1, true, false>", "dH_gemm": "k_gemm_dh_bf16",
+STAGE_KERNELS = {"logits_gemm": "k_logits_bf16<1, 1, false>", "dH_gemm": "k_gemm_dh_bf16",
                  "dW_gemm": "k_gemm_dw_bf16<0>"}
-SHARD_STAGE_KERNELS = {"partials_logits": "k_logits_bf16<0, false, false>",
-                       "bwd_logits": "k_logits_bf16<2, true, false>", "dH_gemm": "k_gemm_dh_bf16",
+SHARD_STAGE_KERNELS = {"partials_logits": "k_logits_bf16<0, 0, false>",
+                       "bwd_logits": "k_logits_bf16<2, 1, false>", "dH_gemm": "k_gemm_dh_bf16",
                        "dW_gemm": "k_gemm_dw_bf16<0>"}
+XCDS = 8  # MI355X: GRBM_GUI_ACTIVE is reported summed over the 8 XCDs' instances
 
 
 WORKLOAD_NAMES = ("tiny", "4b", "headline", "block", "shard")
 
 
-def traffic_summary(fetch_csv: str, write_csv: str, workload: str, calib_mib: int) -> int:
+def traffic_summary(fetch_csv: str, write_csv: str, workload: str, calib_mib: int,
+                    cmd: str = "") -> int:
     """FETCH_SIZE / WRITE_SIZE per launch of each stage kernel, scaled by the
     ratio of the calibration copy's known bytes to what the same counter read
     for it; writes profiles/traffic.json and profiles/<workload>_traffic.md."""
@@ -118,9 +120,11 @@ def traffic_summary(fetch_csv: str, write_csv: str, workload: str, calib_mib: in
     out = {}
     lines = [f"# HBM traffic per launch, {workload} workload",
              "",
-             "FETCH_SIZE and WRITE_SIZE (KiB per dispatch) from two rocprofv3 --pmc runs of",
-             f"`bench.py --workload {workload} --steps 2 --warmup 1 --no-cpu-baseline --no-extras --calib-copy-mib {calib_mib}`",
-             "(`rocprofv3 --pmc FETCH_SIZE` and `--pmc WRITE_SIZE`, each `-- python3 bench.py ...`),",
+             "FETCH_SIZE and WRITE_SIZE (KiB per dispatch) from two rocprofv3 --pmc runs,",
+             "one with FETCH_SIZE and one with WRITE_SIZE (each beside one more TCC counter),",
+             "",
+             f"    {cmd or 'rocprofv3 --kernel-trace --pmc <counters> -- python3 bench.py --workload ' + workload + ' --steps 2 --warmup 1 --no-cpu-baseline --no-extras --sweep= --calib-copy-mib ' + str(calib_mib)}",
+             "",
              f"scaled by the calibration copy of {calib_mib} MiB (read scale {cf:.4f}, write scale {cw:.4f}).",
              "",
              "| stage | kernel | fetch GB/launch | write GB/launch | launches |",
@@ -166,8 +170,9 @@ def counter_summary(run_dirs, workload: str, cmd: str, calib_mib: int) -> int:
     busy (SQ_VALU_MFMA_BUSY_CYCLES over 4 SIMDs x 256 CUs x those cycles),
     VALU busy (SQ_ACTIVE_INST_VALU over 256 CUs x cycles, rocprofv3's VALUBusy),
     LDS active (SQ_LDS_IDX_ACTIVE over 256 CUs x cycles), the MFMA bf16 work,
-    and the requests the L2 sent to DRAM addresses against all its read
-    requests.  Writes profiles/<workload>_counters.md."""
+    the L2's fetch and write bytes, and the bytes of the requests it sent to
+    local HBM addresses, each scaled by what the same counter read for the
+    calibration copy.  Writes profiles/<workload>_counters.md."""
     import csv
     import glob
     vals: dict = {}     # (kernel, counter) -> [per-dispatch values]
@@ -197,7 +202,7 @@ def counter_summary(run_dirs, workload: str, cmd: str, calib_mib: int) -> int:
     # FETCH_SIZE / WRITE_SIZE scaled by what they read for the calibration copy
     # of calib_mib MiB (the run's first device copy)
     scale = {}
-    for cname in ("FETCH_SIZE", "WRITE_SIZE"):
+    for cname in ("FETCH_SIZE", "WRITE_SIZE", "TCC_EA0_RDREQ_DRAM_sum", "TCC_EA0_WRREQ_DRAM_sum"):
         cal = [v for (k, c), v in vals.items() if c == cname and
                ("copy" in k.lower() or "elementwise" in k.lower())]
         scale[cname] = calib_mib * 1024.0 / max(cal[0]) if cal and calib_mib else 1.0
@@ -205,26 +210,30 @@ def counter_summary(run_dirs, workload: str, cmd: str, calib_mib: int) -> int:
     lines = [f"# Counters per launch of the stage kernels, {workload} workload", "",
              "rocprofv3 --pmc runs with --kernel-trace (one counter group per run), each", "",
              f"    {cmd}", "",
-             "clock = GRBM_GUI_ACTIVE / launch duration; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / "
-             "(1024 SIMDs x GRBM_GUI_ACTIVE) (rocprofv3's MfmaUtil); VALU busy = "
+             "clock = GRBM_GUI_ACTIVE / (8 XCDs x launch duration) (the counter is summed over "
+             "the 8 XCDs' instances; a device copy reads 2.4 GHz this way); MFMA busy = "
+             "SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles) (rocprofv3's MfmaUtil); VALU busy = "
              "SQ_ACTIVE_INST_VALU / (256 CUs x GRBM_GUI_ACTIVE) (rocprofv3's VALUBusy); LDS "
              "active = SQ_LDS_IDX_ACTIVE / (256 CUs x GRBM_GUI_ACTIVE) (rocprofv3's LdsUtil); "
-             "MFMA TFLOP = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; DRAM share = TCC_EA0_RDREQ_DRAM / "
-             "TCC_EA0_RDREQ and TCC_EA0_WRREQ_DRAM / TCC_EA0_WRREQ (L2 requests to local HBM "
-             "addresses, which the memory-side MALL may serve; no counter here separates "
-             f"MALL hits); fetch / write = FETCH_SIZE / WRITE_SIZE scaled by what they read for "
+             "MFMA TFLOP = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; fetch / write = FETCH_SIZE / "
+             "WRITE_SIZE, each scaled by what it read for "
              f"a {calib_mib} MiB device copy (read x {scale['FETCH_SIZE']:.3f}, write x "
-             f"{scale['WRITE_SIZE']:.3f}).", "",
+             f"{scale['WRITE_SIZE']:.3f}); HBM read / write = TCC_EA0_RDREQ_DRAM / "
+             "TCC_EA0_WRREQ_DRAM (L2 requests to local HBM addresses) times the bytes per "
+             f"request of the same copy ({scale['TCC_EA0_RDREQ_DRAM_sum'] * 1024:.0f} B read, "
+             f"{scale['TCC_EA0_WRREQ_DRAM_sum'] * 1024:.0f} B write); the memory-side cache "
+             "(MALL) may serve some of those requests, and no counter here separates its hits.", "",
              "| stage | kernel | launches | ms | clock GHz | MFMA busy % | MFMA TFLOP/s | "
-             "VALU busy % | LDS active % | fetch GB | write GB | DRAM read / write share |",
-             "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+             "VALU busy % | LDS active % | fetch GB | write GB | HBM read GB | HBM write GB | "
+             "HBM GB/s |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for stage, kname in kernels.items():
         ks = [k for (k, _) in vals if kname in k]
         if not ks:
             continue
         k = ks[0]
         g = lambda c: avg(vals.get((k, c), []))  # noqa: E731
-        gui = g("GRBM_GUI_ACTIVE")
+        gui = g("GRBM_GUI_ACTIVE") / XCDS  # cycles of one XCD
         ms = avg(durs.get(k, [])) * 1e-6
         clock = gui / (ms * 1e6) if ms == ms and ms > 0 else float("nan")
         mfma = 100.0 * g("SQ_VALU_MFMA_BUSY_CYCLES") / (1024.0 * gui)
@@ -233,11 +242,11 @@ def counter_summary(run_dirs, workload: str, cmd: str, calib_mib: int) -> int:
         tf = g("SQ_INSTS_VALU_MFMA_MOPS_BF16") * 512.0 / (ms * 1e-3) / 1e12
         fetch = g("FETCH_SIZE") * 1024 * scale["FETCH_SIZE"] / 1e9
         write = g("WRITE_SIZE") * 1024 * scale["WRITE_SIZE"] / 1e9
-        rd = g("TCC_EA0_RDREQ_DRAM_sum") / g("TCC_EA0_RDREQ_sum")
-        wr = g("TCC_EA0_WRREQ_DRAM_sum") / g("TCC_EA0_WRREQ_sum")
+        hr = g("TCC_EA0_RDREQ_DRAM_sum") * 1024 * scale["TCC_EA0_RDREQ_DRAM_sum"] / 1e9
+        hw = g("TCC_EA0_WRREQ_DRAM_sum") * 1024 * scale["TCC_EA0_WRREQ_DRAM_sum"] / 1e9
         lines.append(f"| {stage} | {kname} | {len(durs.get(k, []))} | {ms:.3f} | {clock:.2f} | "
                      f"{mfma:.1f} | {tf:.0f} | {valu:.1f} | {lds:.1f} | {fetch:.2f} | {write:.2f} | "
-                     f"{rd:.3f} / {wr:.3f} |")
+                     f"{hr:.2f} | {hw:.2f} | {(hr + hw) / (ms * 1e-3):.0f} |")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     with open(os.path.join(ROOT, "profiles", f"{workload}_counters.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -491,7 +500,7 @@ def main() -> int:
                                args.calib_mib)
     if args.traffic_summary:
         return traffic_summary(args.traffic_summary[0], args.traffic_summary[1], args.workload,
-                               args.calib_mib)
+                               args.calib_mib, cmd=args.counter_cmd)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -207,7 +207,6 @@ void set_gemm_attributes() {
     allow_gemm_lds(k_gemm_dh_bf16);
     allow_gemm_lds(k_gemm_dw_bf16<0>);
     allow_gemm_lds(k_gemm_dw_bf16<1>);
-    allow_gemm_lds(k_gemm_dw_bf16<2>);
     allow_gemm_lds(k_gemm_dw_bf16<3>);
   });
 }
@@ -616,7 +615,10 @@ int run_core_bf16(const Core& c, const Plan& p, char* ws, hipStream_t st) {
       k_scale_transpose_bf16<<<g, 256, 0, st>>>(hc, c.count, c0, cmax, H, alpha, coef, hT, p.Cp,
                                                 need_u ? upart : nullptr, u_off);
       u_off += Cpc / 64;
-      if (need_u && last)  // u = sum_t coef_t h_t and sum_t coef_t over every row
+      // u = sum_t coef_t h_t and sum_t coef_t over the rows so far: after the
+      // chunk holding the last row it is final (later blocks add +0), as the
+      // dW GEMM of that chunk needs it
+      if (need_u && (last || c.count != nullptr))
         k_colsum_finish<float><<<grid1(H + 1, 256), 256, 0, st>>>(upart, u_off, H + 1, H + 1, u);
     }
     if (c.dH != nullptr) {  // 3. dH (split over the vocabulary, ordered reduction, scattered rows)
@@ -643,14 +645,13 @@ int run_core_bf16(const Core& c, const Plan& p, char* ws, hipStream_t st) {
     }
     if (c.dW != nullptr) {  // 4. dW += (alpha h)^T E, the smoothing term with the final value
       StageTimer tm(kDWGemm, st);
-      int mode = 0;
-      if (p.nchunks > 1) mode = ic == 0 ? 1 : (last ? 3 : 2);
+      // (several chunks: the first, or a later one; the final one, found on
+      // the device, writes the bf16 result)
       const int blocks = (int)(cdiv(V, kBM) * cdiv(H, kBN));
-      auto kern = mode == 0 ? k_gemm_dw_bf16<0>
-                            : (mode == 1 ? k_gemm_dw_bf16<1> : (mode == 2 ? k_gemm_dw_bf16<2> : k_gemm_dw_bf16<3>));
+      auto kern = p.nchunks == 1 ? k_gemm_dw_bf16<0> : (ic == 0 ? k_gemm_dw_bf16<1> : k_gemm_dw_bf16<3>);
       kern<<<blocks, kGemmThreads, kGemmLds, st>>>(E, Vp, (int)cmax, c.count, c0, (int)V, hT, p.Cp,
                                                    (int)H, (bf16*)c.dW, dW32, kGroupMBwd,
-                                                   fused_smooth ? u : nullptr, epsV);
+                                                   fused_smooth ? u : nullptr, epsV, last ? 1 : 0);
     }
     if (c.db != nullptr) {  // 5. db partials: sum_t alpha_t E[t, :] per 64 rows
       StageTimer tm(kDb, st);

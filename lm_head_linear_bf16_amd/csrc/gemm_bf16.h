@@ -729,16 +729,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dh_bf16(
 // and the epilogue transposes it back through LDS.  h^T columns C..Kp-1 are
 // zero (E rows there are finite).
 // kMode 0: out (bf16) = acc                      (single chunk)
-// kMode 1: acc32 = acc                           (first of several chunks)
-// kMode 2: acc32 += acc                          (middle chunk)
-// kMode 3: out (bf16) = acc32 + acc              (last chunk)
-// acc32 keeps each tile in the accumulators' own register layout (tile,
-// then sub-tile (i, j), then thread, 4 floats each), so a thread reads and
-// writes its 128 values as 32 coalesced 16-byte pieces.  Mode 2 loads them
-// into the accumulators before the main loop, which then adds this chunk's
-// products on top (the loads overlap the first operand loads), and ends with
-// plain stores, as mode 1 does; mode 3 adds them after its main loop (a
-// preload there leaves too few registers for its bf16 epilogue).
+// kMode 1: acc32 = acc, or out (bf16) = acc      (first of several chunks)
+// kMode 3: acc32 += acc, or out (bf16) = acc32 + acc   (a later chunk)
+// A chunk is the final one when no rows follow it: last_chunk, or, with
+// count != nullptr, *count - c0 <= cmax (chunks hold the compacted rows in
+// order, so the chunks after the one holding the last row are empty).  The
+// final chunk writes the bf16 result; an empty later chunk returns at once,
+// since an earlier one was final.  acc32 keeps each tile in the
+// accumulators' own register layout (tile, then sub-tile (i, j), then
+// thread, 4 floats each), so a thread reads and writes its 128 values as 32
+// coalesced 16-byte pieces.  Mode 3 adds them after its main loop, where the
+// operand registers are free (loaded into the accumulators before it, they
+// leave too few registers for the bf16 epilogue).
 // ---------------------------------------------------------------------------
 // The chunk's tokens: Kp = the padded count (multiple of 64), or, when
 // count != nullptr, min(*count - c0, cmax) rounded up to 64.
@@ -746,38 +748,34 @@ template <int kMode>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dw_bf16(
     const bf16* __restrict__ E, int64_t ldE, int cmax, const int* __restrict__ count, int64_t c0,
     int V, const bf16* __restrict__ hT, int64_t ldh, int H, bf16* __restrict__ out,
-    float* __restrict__ acc32, int group_m, const float* __restrict__ usum, float epsV) {
+    float* __restrict__ acc32, int group_m, const float* __restrict__ usum, float epsV,
+    int last_chunk) {
+  static_assert(kMode == 0 || kMode == 1 || kMode == 3, "dW modes: 0, 1, 3");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const TileCoord tc = tile_coord((int)cdiv(V, kBM), (int)cdiv(H, kBN), 1, group_m);
   if (!tc.active) return;
   const int v0 = tc.tm * kBM, h0 = tc.tn * kBN;  // vocabulary rows and H columns of dW
   int Ce = cmax;
+  bool final_chunk = kMode == 0 || last_chunk != 0;
   if (count != nullptr) {
     const int64_t n = (int64_t)*count - c0;
     Ce = n < 0 ? 0 : (n < cmax ? (int)n : cmax);
+    if (n <= cmax) final_chunk = true;
+    if (kMode == 3 && n <= 0) return;  // an earlier chunk held the last row and wrote dW
   }
   const int Kp = (int)round_up(Ce, kBK);
   Acc acc;  // acc[i][j][r] = dW[v0 + acc_col(wn, j)][h0 + acc_row(wm, i, r)]
   floatx4* t32 = reinterpret_cast<floatx4*>(acc32) +
                  ((int64_t)tc.tm * cdiv(H, kBN) + tc.tn) * (kTM * kTN * kGemmThreads) + threadIdx.x;
-  if constexpr (kMode == 2) {
-#pragma unroll
-    for (int i = 0; i < kTM; ++i)
-#pragma unroll
-      for (int j = 0; j < kTN; ++j) acc[i][j] = __builtin_nontemporal_load(t32 + (i * kTN + j) * kGemmThreads);
-    gemm_mainloop<false, true, false>(hT, ldh, H, 0, h0, E, ldE, max(Kp, 1), (int)ldE, v0, 0,
-                                      Kp / kBK, smem, acc);
-  } else {
-    gemm_mainloop<false, true>(hT, ldh, H, 0, h0, E, ldE, max(Kp, 1), (int)ldE, v0, 0, Kp / kBK,
-                               smem, acc);
-  }
+  gemm_mainloop<false, true>(hT, ldh, H, 0, h0, E, ldE, max(Kp, 1), (int)ldE, v0, 0, Kp / kBK,
+                             smem, acc);
   if constexpr (kMode == 3) {  // (after the main loop, where the operand registers are free)
 #pragma unroll
     for (int i = 0; i < kTM; ++i)
 #pragma unroll
       for (int j = 0; j < kTN; ++j) acc[i][j] += __builtin_nontemporal_load(t32 + (i * kTN + j) * kGemmThreads);
   }
-  if constexpr (kMode == 1 || kMode == 2) {  // carried to the next chunk in fp32
+  if (!final_chunk) {  // carried to the next chunk in fp32
 #pragma unroll
     for (int i = 0; i < kTM; ++i)
 #pragma unroll
