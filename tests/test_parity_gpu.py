@@ -75,8 +75,26 @@ def test_bf16_small(w):
 
 @pytest.mark.parametrize("chunk", [64, 256, 300])
 def test_bf16_chunked(chunk):
+    """316 of 700 rows have a target: a first chunk, later ones carried in
+    fp32, a final one that holds the last row and writes dW, and empty
+    chunks after it (chunks cover the compacted rows in order)."""
     w = synth.custom("chunked_bf16", 7, 100, 128, 1500, label_smoothing=0.1, logit_scale=0.5)
     r, o, t = _run(w, chunk_rows=chunk)
+    _compare(w, r, o, t)
+
+
+@pytest.mark.parametrize("n_valid", [64, 128, 129])
+def test_bf16_chunked_rows_fill_whole_chunks(n_valid):
+    """The valid rows end exactly at a chunk boundary (64, 128) or one row
+    past it (129): the chunk holding the last row is final although a full
+    chunk, and every chunk after it is empty."""
+    w = synth.custom("chunked_fill_bf16", 3, 100, 128, 1001, label_smoothing=0.2, logit_scale=0.7)
+    target, p_mask = synth.targets(w)
+    rng = np.random.default_rng(n_valid)
+    target = np.full(w.N, -100, dtype=np.int64)
+    keep = np.sort(rng.choice(w.N, n_valid, replace=False))
+    target[keep] = rng.integers(0, w.V, n_valid)
+    r, o, t = _run(w, chunk_rows=64, target=target, p_mask=p_mask)
     _compare(w, r, o, t)
 
 
