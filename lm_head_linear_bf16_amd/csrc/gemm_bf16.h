@@ -22,7 +22,9 @@
 //     its MFMAs, one LDS read between two MFMAs (explicit scheduling groups);
 //     the stage barrier sits in the middle of the last step's MFMAs and the
 //     loop body has no branch, so the next tile's first reads and the global
-//     loads of the tile after overlap MFMA work;
+//     loads of the tile after overlap MFMA work; the global loads are spread
+//     between MFMAs, one operand's after the barrier, the other's early in
+//     the next step;
 //   * blocks are renumbered so that consecutive logical tiles run on one XCD
 //     (the dispatcher deals block ids round-robin over the 8 XCDs) and tiles
 //     are walked in groups of `group_m` rows of tiles, so operand slabs are
@@ -86,16 +88,23 @@ __device__ __forceinline__ TileCoord tile_coord(int tiles_m, int tiles_n, int sp
 // 16-byte chunk position of logical chunk c (0..7) in LDS row r.
 __device__ __forceinline__ int lds_chunk(int c, int r) { return c ^ ((r >> 1) & 7); }
 
-// Scheduling groups: ND (MFMA, LDS read) pairs, then the remaining MFMAs.
-template <int I, int NM, int ND>
-__device__ __forceinline__ void interleave_groups() {
-  if constexpr (I < ND) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-    interleave_groups<I + 1, NM, ND>();
-  } else if constexpr (NM > ND) {
-    __builtin_amdgcn_sched_group_barrier(0x008, NM - ND, 0);
+// Scheduling groups with loads: NL times (one MFMA, one global->LDS load,
+// DR LDS reads), then ND (MFMA, LDS read) pairs, then the rest of NM MFMAs.
+template <int NL, int DR, int ND, int NM>
+__device__ __forceinline__ void spread_groups() {
+  static_assert(NL + ND <= NM, "more groups than MFMAs");
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one load
+    __builtin_amdgcn_sched_group_barrier(0x100, DR, 0);  // DR LDS reads
   }
+#pragma unroll
+  for (int i = 0; i < ND; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  if constexpr (NM > NL + ND) __builtin_amdgcn_sched_group_barrier(0x008, NM - NL - ND, 0);
 }
 
 typedef floatx4 Acc[kTM][kTN];
@@ -163,11 +172,10 @@ struct Tile<false, false> {
     }
     kb = (uint32_t)(k_begin * 2);
   }
-  __device__ __forceinline__ void issue(char* tile, int t, int wave) const {
-    char* s = tile + wave * 8 * 128;
-    const uint32_t so = kb + (uint32_t)t * (kBK * 2);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) buffer_to_lds(rs, s + i * kWaves * 8 * 128, voff[i], so);
+  // load i (of 4) of K tile t into the LDS tile
+  __device__ __forceinline__ void issue1(char* tile, int t, int wave, int i) const {
+    buffer_to_lds(rs, tile + wave * 8 * 128 + i * kWaves * 8 * 128, voff[i],
+                  kb + (uint32_t)t * (kBK * 2));
   }
   // fragments for 16-row sub-tiles at rows off + 16 t
   template <int T>
@@ -195,12 +203,9 @@ struct Tile<false, true> {
       p[i] = X + (int64_t)gidx[goff + q] * ldx + lds_chunk(lane & 7, r) * 8 + k_begin;
     }
   }
-  __device__ __forceinline__ void issue(char* tile, int t, int wave) const {
-    char* s = tile + wave * 8 * 128;
-    const int64_t ko = (int64_t)t * kBK;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(FLDCE_GPTR(p[i] + ko), FLDCE_LPTR(s + i * kWaves * 8 * 128), 16, 0, 0);
+  __device__ __forceinline__ void issue1(char* tile, int t, int wave, int i) const {
+    __builtin_amdgcn_global_load_lds(FLDCE_GPTR(p[i] + (int64_t)t * kBK),
+                                     FLDCE_LPTR(tile + wave * 8 * 128 + i * kWaves * 8 * 128), 16, 0, 0);
   }
   template <int T>
   __device__ __forceinline__ void frags(const char* tile, int ks, int off, int lane, bf16x8 (&f)[T]) const {
@@ -237,13 +242,11 @@ struct Tile<true, false> {
       voff[i] = (uint32_t)((int64_t)r * ld * 2 + (int64_t)(min(c0 + u * 8, cols - 8) - c0) * 2);
     }
   }
-  __device__ __forceinline__ void issue(char* tile, int t, int wave) const {
-    char* s = tile + wave * 2 * 512;
+  __device__ __forceinline__ void issue1(char* tile, int t, int wave, int i) const {
     const int64_t row0 = kb + (int64_t)t * kBK;
     // valid bytes from the base: the rest of row row0 and the rows after it
     const Rsrc rs = make_rsrc(X + row0 * ldx, (krows - row0 - 1) * ldx * 2 + tail);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) buffer_to_lds(rs, s + i * 16 * 512, voff[i], 0);
+    buffer_to_lds(rs, tile + wave * 2 * 512 + i * 16 * 512, voff[i], 0);
   }
   template <int T>
   __device__ __forceinline__ void frags(const char* tile, int ks, int off, int lane, bf16x8 (&f)[T]) const {
@@ -266,7 +269,19 @@ struct Tile<true, false> {
 // [kt0, kt0 + nk), starting from zero (kZeroAcc) or from the values the
 // caller put in acc.  For a normal operand X_rows/X_cols are (valid rows,
 // unused); for a transposed one (valid K rows, valid columns).
-template <bool kATr, bool kBTr, bool kZeroAcc = true, bool kBGather = false>
+// Load orders of the main loop: every load of a K step issued at once after
+// the stage barrier (kLoadBurst), or each operand's loads spread over the
+// window between two barriers: the first operand's after barrier t (K tile
+// t+2), one next to each of four MFMAs, and the other's at the start of step
+// t+1 (same tile), interleaved with that step's fragment reads, which leaves
+// them about a quarter step less to land.  Measured at the headline shapes
+// (one box, same inputs): the logits and dH GEMMs fastest with A first (W,
+// E), dW with B first (E, streamed from HBM; the small h^T mostly hits the
+// L2): 1.4-2.8% per GEMM over the burst.
+enum { kLoadBurst = 0, kLoadAFirst = 1, kLoadBFirst = 2 };
+
+template <bool kATr, bool kBTr, bool kZeroAcc = true, bool kBGather = false,
+          int kOrder = kLoadAFirst>
 __device__ __forceinline__ void gemm_mainloop(const bf16* __restrict__ A, int64_t lda, int a_rows,
                                               int a_cols, int m0, const bf16* __restrict__ B,
                                               int64_t ldb, int b_rows, int b_cols, int n0, int64_t kt0,
@@ -287,13 +302,15 @@ __device__ __forceinline__ void gemm_mainloop(const bf16* __restrict__ A, int64_
   Tile<kBTr, kBGather> tb;
   ta.init(A, lda, a_rows, a_cols, m0, kt0 * kBK, lane, wave);
   tb.init(B, ldb, b_rows, b_cols, n0, kt0 * kBK, lane, wave, b_gidx, b_goff);
-  auto issue = [&](int stage, int t) {
-    ta.issue(smem + stage * kStageBytes, t, wave);
-    tb.issue(smem + stage * kStageBytes + kABytes, t, wave);
+  auto stage_a = [&](int stage) { return smem + stage * kStageBytes; };
+  auto stage_b = [&](int stage) { return smem + stage * kStageBytes + kABytes; };
+  auto frag_a = [&](int stage, int ks, int i, bf16x8& f) {
+    bf16x8 x[1];
+    ta.template frags<1>(stage_a(stage), ks, wm * kTM * 16 + 16 * i, lane, x);
+    f = x[0];
   };
-  auto frags = [&](int stage, int ks, bf16x8(&a)[kTM], bf16x8(&b)[kTN]) {
-    ta.template frags<kTM>(smem + stage * kStageBytes, ks, wm * kTM * 16, lane, a);
-    tb.template frags<kTN>(smem + stage * kStageBytes + kABytes, ks, wn * kTN * 16, lane, b);
+  auto frags_b = [&](int stage, int ks, bf16x8(&b)[kTN]) {
+    tb.template frags<kTN>(stage_b(stage), ks, wn * kTN * 16, lane, b);
   };
   auto mma = [&](const bf16x8(&a)[kTM], const bf16x8(&b)[kTN], int i0, int i1) {
 #pragma unroll
@@ -304,31 +321,68 @@ __device__ __forceinline__ void gemm_mainloop(const bf16* __restrict__ A, int64_
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
   };
   constexpr int NM = kTM * kTN, NH = NM / 2;
-  constexpr int ND = kTM * Tile<kATr>::kReads + kTN * Tile<kBTr, kBGather>::kReads;
-  constexpr int ND1 = ND < NM ? ND : NM, ND2 = ND < NM - NH ? ND : NM - NH;
+  constexpr int RA = Tile<kATr>::kReads, RB = Tile<kBTr, kBGather>::kReads;
+  static_assert(kTM == 8 && kRoundsA == 4 && kRoundsB == 4, "4 loads per operand, 2 A fragments each");
   bf16x8 fa0[kTM], fb0[kTN], fa1[kTM], fb1[kTN];
-  issue(0, 0);
+  // loads q of the operand issued after the barrier (early) or at the start
+  // of the next step (late)
+  auto early1 = [&](int stage, int t, int q) {
+    if constexpr (kOrder == kLoadBFirst) tb.issue1(stage_b(stage), t, wave, q);
+    else ta.issue1(stage_a(stage), t, wave, q);
+  };
+  auto late1 = [&](int stage, int t, int q) {
+    if constexpr (kOrder == kLoadBFirst) ta.issue1(stage_a(stage), t, wave, q);
+    else tb.issue1(stage_b(stage), t, wave, q);
+  };
+  constexpr int NL = kOrder == kLoadBurst ? 0 : 4;  // loads placed in the scheduling groups
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    early1(0, 0, q);
+    late1(0, 0, q);
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();  // stage 0 landed in every wave
-  issue(1, min(1, nk - 1));
-  frags(0, 0, fa0, fb0);
+  __syncthreads();  // K tile 0 landed in every wave
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    early1(1, min(1, nk - 1), q);
+    if constexpr (kOrder == kLoadBurst) late1(1, min(1, nk - 1), q);
+  }
+#pragma unroll
+  for (int i = 0; i < kTM; ++i) frag_a(0, 0, i, fa0[i]);
+  frags_b(0, 0, fb0);
+  // The stage barrier of step t sits after 48 of its 64 MFMAs per wave; the
+  // next step's first fragments are read during the 16 after it.  The last
+  // steps re-load the last K tile (unused), so the body has no branch.
   for (int t = 0; t < nk; ++t) {
     const int st = t & 1;
-    frags(st, 1, fa1, fb1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if constexpr (kOrder != kLoadBurst) late1(st ^ 1, min(t + 1, nk - 1), q);
+      frag_a(st, 1, 2 * q, fa1[2 * q]);
+      frag_a(st, 1, 2 * q + 1, fa1[2 * q + 1]);
+    }
+    frags_b(st, 1, fb1);
     mma(fa0, fb0, 0, NM);
-    interleave_groups<0, NM, ND1>();
+    spread_groups<NL, NL ? 2 * RA : 0, (NL ? 0 : kTM * RA) + kTN * RB, NM>();
     __builtin_amdgcn_sched_barrier(0);
     mma(fa1, fb1, 0, NH);
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // tile t+1 landed in every wave; stage st fully read
+    __syncthreads();  // K tile t+1 landed in every wave; stage st fully read
     __builtin_amdgcn_sched_barrier(0);
-    // After the last tile these re-load the last tile into the idle stage and
-    // read a landed stage; both results go unused (keeps the body branch-free).
-    issue(st, min(t + 2, nk - 1));
-    frags(st ^ 1, 0, fa0, fb0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      early1(st, min(t + 2, nk - 1), q);
+      if constexpr (kOrder == kLoadBurst) late1(st, min(t + 2, nk - 1), q);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      frag_a(st ^ 1, 0, 2 * q, fa0[2 * q]);
+      frag_a(st ^ 1, 0, 2 * q + 1, fa0[2 * q + 1]);
+    }
+    frags_b(st ^ 1, 0, fb0);
     mma(fa1, fb1, NH, NM);
-    interleave_groups<0, NM - NH, ND2>();
+    spread_groups<NL, NL ? 2 * RA : 0, (NL ? 0 : kTM * RA) + kTN * RB, NM - NH>();
     __builtin_amdgcn_sched_barrier(0);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -555,8 +609,9 @@ __device__ __forceinline__ void logits_tile(const LogitsArgs& a, int C, int tm, 
                                             char* smem) {
   const int m0 = tm * kBM, n0 = tn * kBN;
   Acc acc;
-  gemm_mainloop<false, false, true, kIndirect>(a.W, a.H, a.V, 0, m0, a.h, a.H, C, 0, n0, 0,
-                                               a.H / kBK, smem, acc, a.gidx, 0);
+  // (the gathered-row variant keeps the burst: spread, it needs 16 bytes of spill)
+  gemm_mainloop<false, false, true, kIndirect, kIndirect ? kLoadBurst : kLoadAFirst>(
+      a.W, a.H, a.V, 0, m0, a.h, a.H, C, 0, n0, 0, a.H / kBK, smem, acc, a.gidx, 0);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN;
@@ -674,7 +729,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dh_bf16(
   const int kt0 = (int)((int64_t)k_tiles * tc.split / splits);
   const int kt1 = (int)((int64_t)k_tiles * (tc.split + 1) / splits);
   Acc acc;
-  gemm_mainloop<false, true>(E, ldE, Me, 0, m0, W, H, V, H, n0, kt0, kt1 - kt0, smem, acc);
+  gemm_mainloop<false, true, true, false, kLoadAFirst>(E, ldE, Me, 0, m0, W, H, V, H, n0, kt0, kt1 - kt0, smem, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN;
@@ -767,7 +822,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dw_bf16(
   Acc acc;  // acc[i][j][r] = dW[v0 + acc_col(wn, j)][h0 + acc_row(wm, i, r)]
   floatx4* t32 = reinterpret_cast<floatx4*>(acc32) +
                  ((int64_t)tc.tm * cdiv(H, kBN) + tc.tn) * (kTM * kTN * kGemmThreads) + threadIdx.x;
-  gemm_mainloop<false, true>(hT, ldh, H, 0, h0, E, ldE, max(Kp, 1), (int)ldE, v0, 0, Kp / kBK,
+  gemm_mainloop<false, true, true, false, kLoadBFirst>(hT, ldh, H, 0, h0, E, ldE, max(Kp, 1), (int)ldE, v0, 0, Kp / kBK,
                              smem, acc);
   if constexpr (kMode == 3) {  // (after the main loop, where the operand registers are free)
 #pragma unroll
