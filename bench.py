@@ -35,7 +35,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 vector, published
-STAGE_FLOP_KERNELS = ("logits_gemm", "dH_gemm", "dW_gemm")
+# GEMM stages and their flops per step in units of rows * H * V: dH and dW
+# are one launch ("bwd_gemms") when both are computed
+STAGE_FLOP_KERNELS = {"logits_gemm": 2, "dH_gemm": 2, "dW_gemm": 2, "bwd_gemms": 4}
 
 
 def log(msg: str) -> None:
@@ -427,11 +429,15 @@ def shard_bench(args, w) -> int:
     n_valid = int(np.count_nonzero(target != synth.IGNORE_INDEX))
     peak = PEAK_BF16_TFLOPS
     gemm = 2.0 * n_valid * H * Vl              # one GEMM over the shard, valid rows
-    # dominant kernel: the slowest GEMM stage of either call
-    cands = {"partials_logits": sp.get("logits_gemm", 0.0), "bwd_logits": sb.get("logits_gemm", 0.0),
-             "dH_gemm": sb.get("dH_gemm", 0.0), "dW_gemm": sb.get("dW_gemm", 0.0)}
-    dom = max(cands, key=cands.get)
-    achieved = gemm / (cands[dom] * 1e-3) / 1e12
+    # dominant kernel: the GEMM stage with the largest time in either call
+    # (ms per step, flops per launch)
+    cands = {"partials_logits": (sp.get("logits_gemm", 0.0), gemm),
+             "bwd_logits": (sb.get("logits_gemm", 0.0), gemm),
+             "bwd_gemms": (sb.get("bwd_gemms", 0.0), 2 * gemm),
+             "dH_gemm": (sb.get("dH_gemm", 0.0), gemm), "dW_gemm": (sb.get("dW_gemm", 0.0), gemm)}
+    dom = max(cands, key=lambda k: cands[k][0])
+    dom_ms, dom_flops = cands[dom]
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
     result = {
         "metric": "fused LM-head CE fwd+bwd tokens/s and TFLOP/s (% bf16 MFMA peak), 1 GPU",
         "value": round(N / (ms * 1e-3), 1),
@@ -455,8 +461,8 @@ def shard_bench(args, w) -> int:
                      "stage_ms": sb},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": traffic_entry(dom, "shard"), "avg_launch_ms": cands[dom],
-                     "flops_per_launch": gemm},
+                     "traffic": traffic_entry(dom, "shard"), "avg_launch_ms": dom_ms,
+                     "flops_per_launch": dom_flops},
         "env": env_info(torch),
     }
     print(json.dumps(result), flush=True)
@@ -601,10 +607,11 @@ def main() -> int:
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
     # dominant kernel: the GEMM stage with the largest time; per step it does
-    # 2 * rows * H * V flops over all its launches (one per chunk)
+    # 2 (one GEMM) or 4 (dH and dW) * rows * H * V flops over all its
+    # launches (one per chunk)
     dom = max((k for k in stages if k in STAGE_FLOP_KERNELS), key=lambda k: stages[k]["total_ms"])
     d = stages[dom]
-    per_launch_flops = 2.0 * rows_mult * H * V * args.steps / d["launches"]
+    per_launch_flops = STAGE_FLOP_KERNELS[dom] * rows_mult * H * V * args.steps / d["launches"]
     avg_ms = d["total_ms"] / d["launches"]
     achieved = per_launch_flops / (avg_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,

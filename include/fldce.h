@@ -329,7 +329,9 @@ int fldce_shard_bwd(const void* h, const void* W_local, const int64_t* target,
  *
  * Stages: 0 prep (divisor, W^T, column sums, target/row-sum dots),
  * 1 h^T, 2 logits GEMM (+ softmax partials), 3 row combine, 4 dlogits,
- * 5 dH GEMM, 6 dH split-K reduction, 7 dW GEMM, 8 loss reduction.
+ * 5 dH GEMM, 6 dH split-K reduction, 7 dW GEMM, 8 loss reduction,
+ * 9 flagged rows (redone relative to their lse), 10 db, 11 dH and dW GEMMs
+ * in one launch (bf16 with several row chunks).
  */
 int fldce_profile_num_stages(void);
 const char* fldce_profile_stage_name(int stage);

@@ -177,14 +177,15 @@ Plan make_plan(int mode, int64_t N, int64_t H, int64_t V, int dtype, int64_t chu
 }
 
 // A dispatch holds fewer than 2^32 work-items per grid dimension: the
-// largest 1-D GEMM grid (logits: vocabulary tiles x chunk-row tiles; dW:
-// vocabulary tiles x H tiles; dH: row tiles x H tiles x splits) must fit.
+// largest 1-D GEMM grid (logits: vocabulary tiles x chunk-row tiles; dH and
+// dW in one launch: row tiles x H tiles x splits, rounded up to 8, plus
+// vocabulary tiles x H tiles) must fit.
 bool grids_fit(const Plan& p, int dtype) {
   if (dtype != FLDCE_DTYPE_BF16) return true;
   const int64_t lim = (int64_t(1) << 32) / kGemmThreads;
   const int64_t tv = cdiv(p.V, kBM), tc = cdiv(std::max<int64_t>(p.C, 1), kBN), th = cdiv(p.H, kBN);
   const int64_t tdh = cdiv(p.C + 1, kBM);  // dH: the chunk's rows and the all-ones row
-  return tv * tc < lim && tv * th < lim && tdh * th * std::max(p.splits, 1) < lim;
+  return tv * tc < lim && round_up(tdh * th * std::max(p.splits, 1), 8) + tv * th < lim;
 }
 
 template <typename K>
@@ -208,6 +209,8 @@ void set_gemm_attributes() {
     allow_gemm_lds(k_gemm_dw_bf16<0>);
     allow_gemm_lds(k_gemm_dw_bf16<1>);
     allow_gemm_lds(k_gemm_dw_bf16<3>);
+    allow_gemm_lds(k_gemm_dhdw_bf16<1>);
+    allow_gemm_lds(k_gemm_dhdw_bf16<3>);
   });
 }
 
@@ -244,11 +247,11 @@ int scratch_of_current_device(char** out) {
 // ---------------------------------------------------------------------------
 enum Stage {
   kPrep = 0, kHT, kLogits, kCombine, kDlogits, kDHGemm, kDHReduce, kDWGemm, kLoss, kFlagged, kDb,
-  kNumStages
+  kBwdGemms, kNumStages
 };
 const char* const kStageNames[kNumStages] = {
-    "prep",    "h_transpose", "logits_gemm", "row_combine", "dlogits", "dH_gemm",
-    "dH_reduce", "dW_gemm",   "loss",        "flagged_rows", "db"};
+    "prep",      "h_transpose", "logits_gemm", "row_combine",  "dlogits", "dH_gemm",
+    "dH_reduce", "dW_gemm",     "loss",        "flagged_rows", "db",      "bwd_gemms"};
 
 struct Profiler {
   bool on = false;
@@ -621,37 +624,63 @@ int run_core_bf16(const Core& c, const Plan& p, char* ws, hipStream_t st) {
       if (need_u && (last || c.count != nullptr))
         k_colsum_finish<float><<<grid1(H + 1, 256), 256, 0, st>>>(upart, u_off, H + 1, H + 1, u);
     }
-    if (c.dH != nullptr) {  // 3. dH (split over the vocabulary, ordered reduction, scattered rows)
-      const int S = p.splits;
-      const int blocks = (int)(cdiv(cmax + extra, kBM) * cdiv(H, kBN) * S);
-      {
+    // 3. dH (split over the vocabulary, ordered reduction, scattered rows) and
+    // 4. dW += (alpha h)^T E (the smoothing term with the final value; with
+    // several chunks the final one, found on the device, writes the bf16
+    // result).  With several chunks both go in one launch when both are
+    // wanted: dW's accumulator traffic then runs beside dH's MFMA work
+    // (1024-row chunks at the headline: step 11.35 -> 11.04 ms).  In one
+    // chunk, where both are MFMA-bound, separate launches measured as fast
+    // or faster (the CUs a partly filled last wave leaves idle are partly
+    // paid back by a higher clock under the power limit).
+    const int S = p.splits;
+    DhArgs da{};
+    DwArgs wa{};
+    int dh_blocks = 0, dw_blocks = 0;
+    if (c.dH != nullptr) {
+      da.E = E; da.ldE = Vp; da.M = (int)cmax; da.extra = extra; da.count = c.count; da.c0 = c0;
+      da.W = W; da.V = (int)V; da.H = (int)H; da.k_tiles = (int)(Vp / kBK); da.max_splits = S;
+      da.out = dHpart; da.group_m = kGroupMBwd; da.dst = c.dH; da.dst_f32 = c.dH_f32 ? 1 : 0;
+      da.rows = c.rows; da.alpha = alpha; da.coef = coef; da.wsum = wsum; da.epsV = epsV;
+      dh_blocks = (int)(cdiv(cmax + extra, kBM) * cdiv(H, kBN) * S);
+    }
+    const int dw_mode = p.nchunks == 1 ? 0 : (ic == 0 ? 1 : 3);
+    if (c.dW != nullptr) {
+      wa.E = E; wa.ldE = Vp; wa.cmax = (int)cmax; wa.count = c.count; wa.c0 = c0; wa.V = (int)V;
+      wa.hT = hT; wa.ldh = p.Cp; wa.H = (int)H; wa.out = (bf16*)c.dW; wa.acc32 = dW32;
+      wa.group_m = kGroupMBwd; wa.usum = fused_smooth ? u : nullptr; wa.epsV = epsV;
+      wa.last_chunk = last ? 1 : 0;
+      dw_blocks = (int)(cdiv(V, kBM) * cdiv(H, kBN));
+    }
+    if (c.dH != nullptr && c.dW != nullptr && p.nchunks > 1) {
+      StageTimer tm(kBwdGemms, st);
+      const int dhb = (int)round_up(dh_blocks, 8);  // keeps every dW block on its XCD
+      auto kern = dw_mode == 1 ? k_gemm_dhdw_bf16<1> : k_gemm_dhdw_bf16<3>;
+      kern<<<dhb + dw_blocks, kGemmThreads, kGemmLds, st>>>(da, wa, dhb);
+    } else {
+      if (c.dH != nullptr) {
         StageTimer tm(kDHGemm, st);
-        k_gemm_dh_bf16<<<blocks, kGemmThreads, kGemmLds, st>>>(
-            E, Vp, (int)cmax, extra, c.count, c0, W, (int)V, (int)H, (int)(Vp / kBK), S, dHpart,
-            kGroupMBwd, c.dH, c.dH_f32 ? 1 : 0, c.rows, alpha, coef, wsum, epsV);
+        k_gemm_dh_bf16<<<dh_blocks, kGemmThreads, kGemmLds, st>>>(da);
       }
-      StageTimer tm(kDHReduce, st);
-      if (S > 1 || extra) {  // (the kernel returns at once when the GEMM wrote the rows)
-        const unsigned g = (unsigned)std::min<int64_t>(cmax, 2048);
-        if (c.dH_f32)
-          k_splitk_scatter<float><<<g, 256, 0, st>>>(dHpart, S, Vp / kBK, cmax, extra, H, c.rows,
-                                                     c.count, c0, alpha, coef, epsV, wsum,
-                                                     (float*)c.dH);
-        else
-          k_splitk_scatter<bf16><<<g, 256, 0, st>>>(dHpart, S, Vp / kBK, cmax, extra, H, c.rows,
-                                                    c.count, c0, alpha, coef, epsV, wsum,
-                                                    (bf16*)c.dH);
+      if (c.dW != nullptr) {
+        StageTimer tm(kDWGemm, st);
+        auto kern = dw_mode == 0 ? k_gemm_dw_bf16<0>
+                                 : (dw_mode == 1 ? k_gemm_dw_bf16<1> : k_gemm_dw_bf16<3>);
+        kern<<<dw_blocks, kGemmThreads, kGemmLds, st>>>(wa);
       }
     }
-    if (c.dW != nullptr) {  // 4. dW += (alpha h)^T E, the smoothing term with the final value
-      StageTimer tm(kDWGemm, st);
-      // (several chunks: the first, or a later one; the final one, found on
-      // the device, writes the bf16 result)
-      const int blocks = (int)(cdiv(V, kBM) * cdiv(H, kBN));
-      auto kern = p.nchunks == 1 ? k_gemm_dw_bf16<0> : (ic == 0 ? k_gemm_dw_bf16<1> : k_gemm_dw_bf16<3>);
-      kern<<<blocks, kGemmThreads, kGemmLds, st>>>(E, Vp, (int)cmax, c.count, c0, (int)V, hT, p.Cp,
-                                                   (int)H, (bf16*)c.dW, dW32, kGroupMBwd,
-                                                   fused_smooth ? u : nullptr, epsV, last ? 1 : 0);
+    if (c.dH != nullptr && (S > 1 || extra)) {
+      // (the scatter returns at once when the GEMM wrote the rows itself)
+      StageTimer tm(kDHReduce, st);
+      const unsigned g = (unsigned)std::min<int64_t>(cmax, 2048);
+      if (c.dH_f32)
+        k_splitk_scatter<float><<<g, 256, 0, st>>>(dHpart, S, Vp / kBK, cmax, extra, H, c.rows,
+                                                   c.count, c0, alpha, coef, epsV, wsum,
+                                                   (float*)c.dH);
+      else
+        k_splitk_scatter<bf16><<<g, 256, 0, st>>>(dHpart, S, Vp / kBK, cmax, extra, H, c.rows,
+                                                  c.count, c0, alpha, coef, epsV, wsum,
+                                                  (bf16*)c.dH);
     }
     if (c.db != nullptr) {  // 5. db partials: sum_t alpha_t E[t, :] per 64 rows
       StageTimer tm(kDb, st);

@@ -708,28 +708,52 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_logits_bf16(const LogitsArg
 // given, straight to row rows[c0 + m] of dst (fp32 when dst_f32, else bf16)
 // and the reduction kernel returns at once.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dh_bf16(
-    const bf16* __restrict__ E, int64_t ldE, int M, int extra, const int* __restrict__ count,
-    int64_t c0, const bf16* __restrict__ W, int V, int H, int k_tiles, int max_splits,
-    float* __restrict__ out, int group_m, void* __restrict__ dst, int dst_f32,
-    const int* __restrict__ rows, const float* __restrict__ alpha, const float* __restrict__ coef,
-    const float* __restrict__ wsum, float epsV) {
-  extern __shared__ __attribute__((aligned(1024))) char smem[];
+struct DhArgs {
+  const bf16* E;  // [>= rows, ldE]
+  int64_t ldE;
+  int M, extra;       // chunk rows (upper bound), extra all-ones row (0 or 1)
+  const int* count;   // compacted row count (nullptr: M rows)
+  int64_t c0;
+  const bf16* W;      // [V, H]
+  int V, H, k_tiles, max_splits;
+  float* out;         // split partials [split][rows + extra][H]
+  int group_m;
+  void* dst;          // dH [N, H], fp32 when dst_f32
+  int dst_f32;
+  const int* rows;    // chunk row -> batch row rows[c0 + row]
+  const float *alpha, *coef, *wsum;
+  float epsV;
+};
+
+// One dH work item: block bid of a grid of at least (row tiles x H tiles x
+// max_splits) blocks.
+__device__ __forceinline__ void dh_item(const DhArgs& a, int bid, char* smem) {
+  const bf16* __restrict__ E = a.E;
+  const int64_t ldE = a.ldE;
+  const int M = a.M, extra = a.extra, H = a.H, k_tiles = a.k_tiles;
+  const int64_t c0 = a.c0;
+  const int* __restrict__ rows = a.rows;
+  const float* __restrict__ alpha = a.alpha;
+  const float* __restrict__ coef = a.coef;
+  const float* __restrict__ wsum = a.wsum;
+  const float epsV = a.epsV;
   int Me = M;
+  const int* __restrict__ count = a.count;
   if (count != nullptr) {
     const int64_t n = (int64_t)*count - c0;
     Me = n < 0 ? 0 : (n < M ? (int)n : M);
   }
   const int Mr = Me;  // real rows
   Me += extra;
-  const int splits = choose_splits(cdiv(Me, kBM) * cdiv(H, kBN), k_tiles, max_splits);
-  const TileCoord tc = tile_coord((int)cdiv(Me, kBM), (int)cdiv(H, kBN), splits, group_m);
+  const int splits = choose_splits(cdiv(Me, kBM) * cdiv(H, kBN), k_tiles, a.max_splits);
+  const TileCoord tc = tile_coord_of(bid, (int)cdiv(Me, kBM), (int)cdiv(H, kBN), splits, a.group_m);
   if (!tc.active) return;
   const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
   const int kt0 = (int)((int64_t)k_tiles * tc.split / splits);
   const int kt1 = (int)((int64_t)k_tiles * (tc.split + 1) / splits);
   Acc acc;
-  gemm_mainloop<false, true, true, false, kLoadAFirst>(E, ldE, Me, 0, m0, W, H, V, H, n0, kt0, kt1 - kt0, smem, acc);
+  gemm_mainloop<false, true, true, false, kLoadAFirst>(E, ldE, Me, 0, m0, a.W, H, a.V, H, n0, kt0,
+                                                       kt1 - kt0, smem, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN;
@@ -747,13 +771,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dh_bf16(
           const int col = n0 + acc_col(wn, j, lane);
           if (col >= H) continue;
           const float v = al * acc[i][j][r] - (wsum != nullptr ? ce * wsum[col] : 0.f);
-          if (dst_f32) static_cast<float*>(dst)[drow + col] = v;
-          else static_cast<bf16*>(dst)[drow + col] = (bf16)v;
+          if (a.dst_f32) static_cast<float*>(a.dst)[drow + col] = v;
+          else static_cast<bf16*>(a.dst)[drow + col] = (bf16)v;
         }
       }
     return;
   }
-  float* o = out + (int64_t)tc.split * Me * H;  // partials [split][Me][H]
+  float* o = a.out + (int64_t)tc.split * Me * H;  // partials [split][Me][H]
 #pragma unroll
   for (int i = 0; i < kTM; ++i)
 #pragma unroll
@@ -765,6 +789,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dh_bf16(
         if (row < Me && col < H) o[(int64_t)row * H + col] = acc[i][j][r];  // re-read from the MALL
       }
     }
+}
+
+__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dh_bf16(const DhArgs a) {
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  dh_item(a, blockIdx.x, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -799,19 +828,41 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dh_bf16(
 // ---------------------------------------------------------------------------
 // The chunk's tokens: Kp = the padded count (multiple of 64), or, when
 // count != nullptr, min(*count - c0, cmax) rounded up to 64.
+struct DwArgs {
+  const bf16* E;      // [>= Kp rows, ldE]
+  int64_t ldE;
+  int cmax;           // chunk rows (upper bound)
+  const int* count;   // compacted row count (nullptr: cmax rows)
+  int64_t c0;
+  int V;
+  const bf16* hT;     // (alpha h)^T [H, ldh]
+  int64_t ldh;
+  int H;
+  bf16* out;          // dW [V, H]
+  float* acc32;       // fp32 accumulator across chunks (tile layout)
+  int group_m;
+  const float* usum;  // sum_t coef_t h_t, or nullptr
+  float epsV;
+  int last_chunk;
+};
+
+// One dW tile: block bid of a grid of (vocabulary tiles x H tiles) blocks.
 template <int kMode>
-__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dw_bf16(
-    const bf16* __restrict__ E, int64_t ldE, int cmax, const int* __restrict__ count, int64_t c0,
-    int V, const bf16* __restrict__ hT, int64_t ldh, int H, bf16* __restrict__ out,
-    float* __restrict__ acc32, int group_m, const float* __restrict__ usum, float epsV,
-    int last_chunk) {
+__device__ __forceinline__ void dw_tile(const DwArgs& a, int bid, char* smem) {
   static_assert(kMode == 0 || kMode == 1 || kMode == 3, "dW modes: 0, 1, 3");
-  extern __shared__ __attribute__((aligned(1024))) char smem[];
-  const TileCoord tc = tile_coord((int)cdiv(V, kBM), (int)cdiv(H, kBN), 1, group_m);
+  const bf16* __restrict__ E = a.E;
+  const int64_t ldE = a.ldE;
+  const int cmax = a.cmax, V = a.V, H = a.H;
+  const int* __restrict__ count = a.count;
+  const int64_t c0 = a.c0;
+  const float* __restrict__ usum = a.usum;
+  const float epsV = a.epsV;
+  bf16* __restrict__ out = a.out;
+  const TileCoord tc = tile_coord_of(bid, (int)cdiv(V, kBM), (int)cdiv(H, kBN), 1, a.group_m);
   if (!tc.active) return;
   const int v0 = tc.tm * kBM, h0 = tc.tn * kBN;  // vocabulary rows and H columns of dW
   int Ce = cmax;
-  bool final_chunk = kMode == 0 || last_chunk != 0;
+  bool final_chunk = kMode == 0 || a.last_chunk != 0;
   if (count != nullptr) {
     const int64_t n = (int64_t)*count - c0;
     Ce = n < 0 ? 0 : (n < cmax ? (int)n : cmax);
@@ -820,10 +871,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dw_bf16(
   }
   const int Kp = (int)round_up(Ce, kBK);
   Acc acc;  // acc[i][j][r] = dW[v0 + acc_col(wn, j)][h0 + acc_row(wm, i, r)]
-  floatx4* t32 = reinterpret_cast<floatx4*>(acc32) +
+  floatx4* t32 = reinterpret_cast<floatx4*>(a.acc32) +
                  ((int64_t)tc.tm * cdiv(H, kBN) + tc.tn) * (kTM * kTN * kGemmThreads) + threadIdx.x;
-  gemm_mainloop<false, true, true, false, kLoadBFirst>(hT, ldh, H, 0, h0, E, ldE, max(Kp, 1), (int)ldE, v0, 0, Kp / kBK,
-                             smem, acc);
+  gemm_mainloop<false, true, true, false, kLoadBFirst>(a.hT, a.ldh, H, 0, h0, E, ldE, max(Kp, 1),
+                                                       (int)ldE, v0, 0, Kp / kBK, smem, acc);
   if constexpr (kMode == 3) {  // (after the main loop, where the operand registers are free)
 #pragma unroll
     for (int i = 0; i < kTM; ++i)
@@ -873,6 +924,29 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dw_bf16(
     }
     return;
   }
+}
+
+template <int kMode>
+__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dw_bf16(const DwArgs a) {
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  dw_tile<kMode>(a, blockIdx.x, smem);
+}
+
+// ---------------------------------------------------------------------------
+// dH and dW in one launch (used with several chunks, kMode 1 or 3): blocks
+// [0, dh_blocks) are dH work items, the rest dW tiles.  Blocks are
+// dispatched in order, so the long dH items start first and the dW tiles,
+// whose fp32 accumulator read-modify-write is bound by HBM, run beside them
+// and fill the CUs that dH's partly filled last wave leaves idle.
+// dh_blocks is a multiple of 8, so a dW tile's block id keeps its XCD
+// (block b runs on XCD b mod 8) and the dW tile order is unchanged.
+// ---------------------------------------------------------------------------
+template <int kMode>
+__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dhdw_bf16(const DhArgs d, const DwArgs w,
+                                                                    int dh_blocks) {
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  if ((int)blockIdx.x < dh_blocks) dh_item(d, blockIdx.x, smem);
+  else dw_tile<kMode>(w, blockIdx.x - dh_blocks, smem);
 }
 
 }  // namespace fldce
