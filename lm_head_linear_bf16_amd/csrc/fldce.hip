@@ -364,6 +364,15 @@ struct Core {
 };
 
 // Row-combine arguments of a chunk common to every mode (mode 0, no chunk outputs).
+// The row combine over up to `rows` rows (the block shape by that bound;
+// the rows that exist are counted on the device).
+void launch_combine(int64_t rows, hipStream_t st, const CombineArgs& a) {
+  if (rows >= 4096)
+    k_combine_rows<32><<<grid1(rows, 32), 256, 0, st>>>(a);
+  else
+    k_combine_rows<8><<<grid1(rows, 8), 256, 0, st>>>(a);
+}
+
 CombineArgs combine_args(const Core& c, const Plan& p, const floatx2* part, int64_t c0,
                          int64_t cmax) {
   CombineArgs a{};
@@ -442,7 +451,7 @@ void run_flagged_rows(const Core& c, const Plan& p, const LogitsArgs& la, const 
   cb.E = nullptr;
   cb.flag_count = nullptr;
   cb.flag_list = nullptr;
-  k_combine_rows<<<grid1(cmax, 32), 256, 0, st>>>(cb);
+  launch_combine(cmax, st, cb);
   if (E == nullptr) return;
   LogitsArgs e = f;
   e.part = nullptr;
@@ -462,7 +471,7 @@ const float* run_rows_f32(const Core& c, const Plan& p, const floatx2* part, flo
   if (c.lse_in == nullptr) {
     CombineArgs a = combine_args(c, p, part, c0, cmax);
     a.coef_out = coef;
-    k_combine_rows<<<grid1(cmax, 32), 256, 0, st>>>(a);
+    launch_combine(cmax, st, a);
     return c.lse_out + c0;
   }
   k_coef_rows<<<grid1(cmax, 256), 256, 0, st>>>(c.target, c.p_mask, c.ignore, cmax, nullptr,
@@ -600,7 +609,7 @@ int run_core_bf16(const Core& c, const Plan& p, char* ws, hipStream_t st) {
       ca.flag_list = flist;
       {
         StageTimer tm(kCombine, st);
-        k_combine_rows<<<grid1(cmax, 32), 256, 0, st>>>(ca);
+        launch_combine(cmax, st, ca);
       }
       run_flagged_rows(c, p, la, ca, flist, nflag + ic, exact ? nullptr : la.E, tcol, cmax, st);
     }
@@ -903,7 +912,7 @@ int run_fwd(const Plan& p, const void* h, const void* W, const void* bias, const
     ca.flag_list = flist;
     {
       StageTimer tm(kCombine, st);
-      k_combine_rows<<<grid1(N, 32), 256, 0, st>>>(ca);
+      launch_combine(N, st, ca);
     }
     run_flagged_rows(c, p, la, ca, flist, nflag, nullptr, nullptr, N, st);
   } else {  // fp32: z per chunk, row partials, combine
@@ -922,7 +931,7 @@ int run_fwd(const Plan& p, const void* h, const void* W, const void* bias, const
         k_row_partials_f32<<<g2, 64, 0, st>>>(zb, p.Vp, Cc, V, part, p.C);
       }
       StageTimer tm(kCombine, st);
-      k_combine_rows<<<grid1(Cc, 32), 256, 0, st>>>(combine_args(c, p, part, c0, Cc));
+      launch_combine(Cc, st, combine_args(c, p, part, c0, Cc));
     }
   }
   {
@@ -1182,9 +1191,9 @@ int fldce_shard_partials(const void* h, const void* W_local, const int64_t* targ
     }
     {
       StageTimer tm(kCombine, st);
-      k_combine_rows<<<grid1(N, 32), 256, 0, st>>>(
-          shard_combine_args(part, row_sumlogit ? rpart : nullptr, p, N, rows, count, 0, row_max,
-                             row_sumexp, row_sumlogit));
+      launch_combine(N, st,
+                     shard_combine_args(part, row_sumlogit ? rpart : nullptr, p, N, rows, count, 0,
+                                        row_max, row_sumexp, row_sumlogit));
     }
     StageTimer tm(kPrep, st);
     k_rowdot<bf16><<<grid_strided(N, 4), 256, 0, st>>>((const bf16*)h, (const bf16*)W_local, nullptr, H,
@@ -1199,7 +1208,7 @@ int fldce_shard_partials(const void* h, const void* W_local, const int64_t* targ
                                        V, H, logit_scale, zb, p.Vp, 0);
       dim3 g2((unsigned)cdiv(Cc, 64), (unsigned)p.nT);
       k_row_partials_f32<<<g2, 64, 0, st>>>(zb, p.Vp, Cc, V, part, p.C);
-      k_combine_rows<<<grid1(Cc, 32), 256, 0, st>>>(shard_combine_args(
+      launch_combine(Cc, st, shard_combine_args(
           part, nullptr, p, Cc, nullptr, nullptr, c0, row_max, row_sumexp, nullptr));
     }
     if (row_sumlogit) launch_colsum((const float*)W_local, V, H, colpart, wsum, st);

@@ -728,20 +728,13 @@ struct DhArgs {
 // One dH work item: block bid of a grid of at least (row tiles x H tiles x
 // max_splits) blocks.
 __device__ __forceinline__ void dh_item(const DhArgs& a, int bid, char* smem) {
-  const bf16* __restrict__ E = a.E;
-  const int64_t ldE = a.ldE;
-  const int M = a.M, extra = a.extra, H = a.H, k_tiles = a.k_tiles;
+  const int H = a.H, k_tiles = a.k_tiles, extra = a.extra;
   const int64_t c0 = a.c0;
-  const int* __restrict__ rows = a.rows;
-  const float* __restrict__ alpha = a.alpha;
-  const float* __restrict__ coef = a.coef;
   const float* __restrict__ wsum = a.wsum;
-  const float epsV = a.epsV;
-  int Me = M;
-  const int* __restrict__ count = a.count;
-  if (count != nullptr) {
-    const int64_t n = (int64_t)*count - c0;
-    Me = n < 0 ? 0 : (n < M ? (int)n : M);
+  int Me = a.M;
+  if (a.count != nullptr) {
+    const int64_t n = (int64_t)*a.count - c0;
+    Me = n < 0 ? 0 : (n < a.M ? (int)n : a.M);
   }
   const int Mr = Me;  // real rows
   Me += extra;
@@ -752,8 +745,8 @@ __device__ __forceinline__ void dh_item(const DhArgs& a, int bid, char* smem) {
   const int kt0 = (int)((int64_t)k_tiles * tc.split / splits);
   const int kt1 = (int)((int64_t)k_tiles * (tc.split + 1) / splits);
   Acc acc;
-  gemm_mainloop<false, true, true, false, kLoadAFirst>(E, ldE, Me, 0, m0, a.W, H, a.V, H, n0, kt0,
-                                                       kt1 - kt0, smem, acc);
+  gemm_mainloop<false, true, true, false, kLoadAFirst>(a.E, a.ldE, Me, 0, m0, a.W, H, a.V, H, n0,
+                                                       kt0, kt1 - kt0, smem, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN;
@@ -764,8 +757,8 @@ __device__ __forceinline__ void dh_item(const DhArgs& a, int bid, char* smem) {
       for (int r = 0; r < 4; ++r) {
         const int row = m0 + acc_row(wm, i, lane, r);
         if (row >= Mr) continue;
-        const int64_t drow = (int64_t)rows[c0 + row] * H;
-        const float al = alpha[row], ce = wsum != nullptr ? coef[row] * epsV : 0.f;
+        const int64_t drow = (int64_t)a.rows[c0 + row] * H;
+        const float al = a.alpha[row], ce = wsum != nullptr ? a.coef[row] * a.epsV : 0.f;
 #pragma unroll
         for (int j = 0; j < kTN; ++j) {
           const int col = n0 + acc_col(wn, j, lane);
@@ -850,21 +843,16 @@ struct DwArgs {
 template <int kMode>
 __device__ __forceinline__ void dw_tile(const DwArgs& a, int bid, char* smem) {
   static_assert(kMode == 0 || kMode == 1 || kMode == 3, "dW modes: 0, 1, 3");
-  const bf16* __restrict__ E = a.E;
-  const int64_t ldE = a.ldE;
   const int cmax = a.cmax, V = a.V, H = a.H;
-  const int* __restrict__ count = a.count;
-  const int64_t c0 = a.c0;
   const float* __restrict__ usum = a.usum;
   const float epsV = a.epsV;
-  bf16* __restrict__ out = a.out;
   const TileCoord tc = tile_coord_of(bid, (int)cdiv(V, kBM), (int)cdiv(H, kBN), 1, a.group_m);
   if (!tc.active) return;
   const int v0 = tc.tm * kBM, h0 = tc.tn * kBN;  // vocabulary rows and H columns of dW
   int Ce = cmax;
   bool final_chunk = kMode == 0 || a.last_chunk != 0;
-  if (count != nullptr) {
-    const int64_t n = (int64_t)*count - c0;
+  if (a.count != nullptr) {
+    const int64_t n = (int64_t)*a.count - a.c0;
     Ce = n < 0 ? 0 : (n < cmax ? (int)n : cmax);
     if (n <= cmax) final_chunk = true;
     if (kMode == 3 && n <= 0) return;  // an earlier chunk held the last row and wrote dW
@@ -873,8 +861,8 @@ __device__ __forceinline__ void dw_tile(const DwArgs& a, int bid, char* smem) {
   Acc acc;  // acc[i][j][r] = dW[v0 + acc_col(wn, j)][h0 + acc_row(wm, i, r)]
   floatx4* t32 = reinterpret_cast<floatx4*>(a.acc32) +
                  ((int64_t)tc.tm * cdiv(H, kBN) + tc.tn) * (kTM * kTN * kGemmThreads) + threadIdx.x;
-  gemm_mainloop<false, true, true, false, kLoadBFirst>(a.hT, a.ldh, H, 0, h0, E, ldE, max(Kp, 1),
-                                                       (int)ldE, v0, 0, Kp / kBK, smem, acc);
+  gemm_mainloop<false, true, true, false, kLoadBFirst>(a.hT, a.ldh, H, 0, h0, a.E, a.ldE, max(Kp, 1),
+                                                       (int)a.ldE, v0, 0, Kp / kBK, smem, acc);
   if constexpr (kMode == 3) {  // (after the main loop, where the operand registers are free)
 #pragma unroll
     for (int i = 0; i < kTM; ++i)
@@ -920,7 +908,7 @@ __device__ __forceinline__ void dw_tile(const DwArgs& a, int bid, char* smem) {
       const int row = v0 + rl, col = h0 + ch * 8;
       if (row < V && col < H)  // H % 64 == 0: a chunk is wholly in or out
         __builtin_nontemporal_store(*(const bf16x8*)&stg[rl * kBN + ((ch ^ (rl & 15)) << 3)],
-                                    (bf16x8*)(out + (int64_t)row * H + col));
+                                    (bf16x8*)(a.out + (int64_t)row * H + col));
     }
     return;
   }
