@@ -328,6 +328,46 @@ def _timed(fn, steps: int, warmup: int):
     return (t1 - t0) * 1e3 / steps, stages
 
 
+def vendor_leg(w, rows: int, peak: float, reps: int = 10) -> dict:
+    """For scale, not part of the path: torch.matmul (hipBLASLt) as plain bf16
+    GEMMs at the three contractions' shapes of this workload, with the
+    operands in the layouts the fused kernels read (rows = the rows with a
+    target): logits W [V, H] x h [rows, H]^T, dH E [rows, V] x W [V, H], dW
+    as its transpose h^T [H, rows] x E [rows, V].  Random operands; the
+    median of `reps` timed calls per shape."""
+    import numpy as np
+    import torch
+    dev = torch.device("cuda:0")
+    H, V = w.H, w.V
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    bf = torch.bfloat16
+    Wm = torch.randn(V, H, device=dev, dtype=bf, generator=g)
+    hm = torch.randn(rows, H, device=dev, dtype=bf, generator=g)
+    Em = torch.randn(rows, V, device=dev, dtype=bf, generator=g)
+    hT = hm.t().contiguous()
+    shapes = {"logits": (lambda: torch.matmul(Wm, hm.t()), 2.0 * V * rows * H),
+              "dH": (lambda: torch.matmul(Em, Wm), 2.0 * rows * V * H),
+              "dW": (lambda: torch.matmul(hT, Em), 2.0 * H * rows * V)}
+    out = {}
+    for name, (fn, flops) in shapes.items():
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record()
+        for i in range(reps):
+            fn()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        ms = float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
+        tf = flops / (ms * 1e-3) / 1e12
+        out[name] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac": round(tf / peak, 4)}
+        log(f"vendor GEMM {name}: {ms:.3f} ms, {tf:.0f} TFLOP/s")
+    del Wm, hm, Em, hT
+    return out
+
+
 def extra_legs(args, w, h, W, tgt, pm, dt, rows_mult: int, ms_plain: float, peak: float) -> dict:
     """The rest of page 1's interface on the same inputs: forward only
     (fldce_fwd: 2 * rows * H * V flops), with --frozen-leg fwd+bwd without
@@ -472,8 +512,8 @@ def shard_bench(args, w) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="headline")
     ap.add_argument("--chunk-rows", type=int, default=0)
     ap.add_argument("--cpu-rows", type=int, default=0,
@@ -497,6 +537,8 @@ def main() -> int:
                     help="skip the forward-only leg (and the bias + db leg)")
     ap.add_argument("--frozen-leg", action="store_true",
                     help="also time fwd+bwd without dW (a frozen weight: fldce_fwd_bwd_ex)")
+    ap.add_argument("--vendor-leg", action="store_true",
+                    help="also time torch.matmul (hipBLASLt) at the three GEMM shapes, for scale")
     ap.add_argument("--bias-leg", action="store_true",
                     help="also time fwd+bwd with the seeded bias and db (fldce_fwd_bwd_ex); off by "
                          "default so that the plain step is the only user of its logits kernel")
@@ -650,6 +692,8 @@ def main() -> int:
     }
     if not args.no_extras:
         result.update(extra_legs(args, w, h, W, tgt, pm, dt, rows_mult, ms, peak))
+    if args.vendor_leg and w.dtype == "bf16":
+        result["vendor_gemm"] = vendor_leg(w, rows_mult, peak)
     if args.sweep and w.name == "headline":
         # rows per chunk, taken over the compacted rows (page 1 chunks the rows
         # to bound the [C, V] buffer); C >= the rows with a target is one chunk
