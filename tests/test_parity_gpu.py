@@ -98,6 +98,42 @@ def test_bf16_chunked_rows_fill_whole_chunks(n_valid):
     _compare(w, r, o, t)
 
 
+def test_bf16_largest_vocabulary():
+    """The largest bf16 vocabulary, V = 2^23 - 64 (the last multiple of 64
+    below the 2^23 limit): a lane's byte offset into the stored exponentials
+    (row < 256 of a 256-row tile, times 2 Vp) reaches just under 2^32, and
+    targets sit in the last vocabulary columns.  Every row's lse, the loss,
+    the whole dH, and dW on the first and last 256 vocabulary rows and the
+    targets' rows, against the oracle."""
+    torch = torch_cuda()
+    from lm_head_linear_bf16_amd import fldce
+    dev = torch.device("cuda:0")
+    V = (1 << 23) - 64
+    w = synth.custom("largest_vocab_bf16", 1, 16, 64, V, label_smoothing=0.1, logit_scale=0.5,
+                     reduction="sum", index=420)
+    _, p = synth.targets(w)
+    rng = np.random.default_rng(420)
+    t = rng.integers(0, V, w.N)
+    t[:4] = [V - 1, V - 64, V - 65, 0]
+    h, W = synth.hidden(w), synth.weight(w)
+    say(f"case largest vocabulary: N={w.N} H={w.H} V={V}")
+    r = fldce.fldce_fwd_bwd(to_dev(h, dev), to_dev(W, dev), torch.from_numpy(t).to(dev),
+                            torch.from_numpy(p).to(dev), label_smoothing=0.1, logit_scale=0.5,
+                            reduction="sum", row_stats=True)
+    torch.cuda.synchronize()
+    rows = np.arange(w.N)
+    lse, zt, zs = O.row_stats(h.values, W.values, t, rows, 0.5)
+    np.testing.assert_allclose(host(r["row_lse"]), lse, rtol=0, atol=2e-3)
+    valid = np.ones(w.N, dtype=bool)
+    loss = O.loss_from_row_losses(O.row_losses(lse, zt, zs, V, p, valid, 0.1), 1.0)
+    assert abs(float(r["loss"].item()) - loss) <= LOSS_RTOL["bf16"] * abs(loss)
+    dH = O.dH_rows(h.values, W.values, t, p, lse, rows, 1.0, 0.1, 0.5)
+    assert grad_err(host(r["dH"]), dH) <= GRAD_RTOL["bf16"]
+    vr = np.unique(np.concatenate([np.arange(256), np.arange(V - 256, V), t]))
+    dW = O.dW_rows(h.values, W.values, t, p, lse, vr, 1.0, 0.1, 0.5)
+    assert grad_err(host(r["dW"][torch.from_numpy(vr).to(dev)]), dW) <= GRAD_RTOL["bf16"]
+
+
 def test_fp32_tiny_workload():
     w = synth.WORKLOADS["tiny"]
     r, o, t = _run(w)
