@@ -4,20 +4,24 @@
 // caller's stream.  No allocation, no host synchronisation.
 //
 // One chunk of C token rows (page 1, fused_linear_cross_entropy_forward: the
-// rows are processed in chunks to bound the [C, V] logits buffer):
-//   1. logits GEMM + softmax partials (+ z stored)
-//   2. per-row combine -> lse, per-row loss, coefficient s / (p_i D)
-//   3. dlogits pass: z -> g
-//   4. dH = g W     (split-K GEMM over the vocabulary + ordered reduction)
-//   5. dW += g^T h  (fp32 across chunks, rounded once at the end)
-// Before the loop: divisor D and, on the bf16 path, the compacted list of
-// rows whose target is not ignore_index (only they are multiplied; chunks
-// are taken over that list); target logits by per-row dot products (and,
-// for fp32, the row sums of z from the column sums of W).  After it: the
-// loss.  bf16 GEMMs read W and g in their own layouts (one via the LDS
-// transpose read); the chunk's rows of h are gathered once, row-major and
-// transposed.  The fp32 path (float32 inputs) uses plain fp32 GEMMs over
-// transposed copies.
+// rows are processed in chunks to bound the [C, V] logits buffer), bf16:
+//   1. logits GEMM; its epilogue forms the softmax partials relative to each
+//      row's target logit and stores E = exp(z - target logit) (bf16)
+//   2. per-row combine -> lse, per-row loss, coefficient s / (p_i D), the row
+//      factor alpha = coef / sum E, and the target term put into E
+//   3. dH = alpha (E W) - the smoothing term (split-K GEMM over the
+//      vocabulary + ordered reduction)
+//   4. dW += (alpha h)^T E - the smoothing term (fp32 across chunks, rounded
+//      once by the chunk holding the last row)
+// so g = alpha E - coef eps / V is never written (for label smoothing above
+// 1/2 the logits are stored and one row pass forms g instead).  Before the
+// loop: divisor D and the compacted list of rows whose target is not
+// ignore_index (only they are multiplied; chunks are taken over that list);
+// target logits by per-row dot products.  After it: the loss.  bf16 GEMMs
+// read W and E in their own layouts (one via the LDS transpose read); the
+// chunk's rows of h are gathered once, row-major and (times alpha)
+// transposed.  The fp32 path (float32 inputs) stores z, forms g in place and
+// uses plain fp32 GEMMs over transposed copies.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>

@@ -12,8 +12,9 @@
 //     (N) grid, each wave owning a 128 x 64 accumulator (8 x 4 MFMA tiles of
 //     16 x 16, 128 fp32 per lane), two waves per SIMD so one wave's waits are
 //     covered by the other's MFMAs;
-//   * two LDS stages of (256 + 256) x 64 bf16 = 64 KB each, filled with
-//     direct global->LDS 16-byte loads (no VGPR staging).  The 16-byte chunk
+//   * two LDS stages of (256 + 256) x 64 bf16 = 64 KB each, filled by
+//     buffer loads straight into LDS, 16 bytes per lane (no VGPR staging).
+//     The 16-byte chunk
 //     c of row r sits at chunk position c ^ ((r >> 1) & 7): the LDS serves a
 //     16-byte read to 16 lanes per cycle, and the 16 rows those lanes read
 //     then fall on 16 distinct bank groups (measured: no bank-conflict
@@ -696,8 +697,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_logits_bf16(const LogitsArg
 // rows, ldE] (K contiguous): the stored exp(z - r) with the target entry
 // patched, so that alpha_m E[m, :] is the row's gradient g without its
 // smoothing term; B = W read as K rows (vocabulary rows of W [V, H],
-// transposed in LDS).  Rows of W past V are clamped: E is zero in those
-// columns.
+// transposed in LDS).  Rows of W past V read as zeros (the buffer range
+// ends at row V - 1), and E is zero in those columns.
 //
 // M = chunk rows: the grid covers M + extra (upper bound) x max_splits; the
 // rows that exist are min(*count - c0, M) (+ extra: the all-ones row after
@@ -797,7 +798,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dh_bf16(const DhArgs a
 // columns, transposed in LDS): alpha_t E[t, v] is g[t, v] without its
 // smoothing term, which is the same for every vocabulary row,
 // -(eps / V) sum_t c_t h_t = -epsV * usum, and is subtracted from the
-// final value (modes 0 and 3) when usum != nullptr.  In this order the
+// final value (written by the final chunk) when usum != nullptr.  In this order the
 // transposed operand is the one with 4 fragments per wave rather than 8 (16
 // LDS reads per 32-wide K step instead of 20: main loop 2.62 against
 // 2.72 ms at the 4B-scale shape).  Tiles are still numbered over (vocabulary
