@@ -350,7 +350,7 @@ __global__ __launch_bounds__(64) void k_row_partials_f32(const float* __restrict
 // ---------------------------------------------------------------------------
 // Combine the per-slab partials of each row in a fixed order (page 1: the
 // host-side logsumexp over the per-block results of logsumexp_fwd_kernel).
-// 256 threads = 32 rows x 8 slab groups.
+// 256 threads = kRows rows x (256 / kRows) slab groups (below).
 //
 // R_i (the row sum of the logits) is R[i] when R != nullptr, else the sum of
 // rpart over the slabs when rpart != nullptr (fixed order), else 0.
