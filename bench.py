@@ -301,9 +301,18 @@ def cpu_baseline(w, rows: int) -> dict:
 def env_info(torch) -> dict:
     """Device, HIP runtime and PyTorch versions of the run."""
     p = torch.cuda.get_device_properties(0)
-    return {"device": p.name, "arch": getattr(p, "gcnArchName", ""),
-            "compute_units": p.multi_processor_count, "hip": torch.version.hip,
-            "torch": torch.__version__}
+    env = {"device": p.name, "arch": getattr(p, "gcnArchName", ""),
+           "compute_units": p.multi_processor_count, "hip": torch.version.hip,
+           "torch": torch.__version__}
+    # the rated shader clock and L2 size, where this PyTorch build exposes them
+    # (the clock a kernel actually runs at is in the counter summaries)
+    clock_khz = getattr(p, "clock_rate", None)
+    if clock_khz:
+        env["max_clock_mhz"] = round(clock_khz / 1000.0)
+    l2 = getattr(p, "L2_cache_size", None)
+    if l2:
+        env["l2_cache_mb"] = round(l2 / 2**20, 1)
+    return env
 
 
 def _timed(fn, steps: int, warmup: int):
