@@ -36,6 +36,35 @@ def test_every_declared_symbol_is_exported_and_bound(L):
         assert hasattr(fldce, n) or n in ("fldce_status_string",), f"python name {n}"
 
 
+def test_header_is_a_c_abi(L, tmp_path):
+    """The header compiles as strict C99, and a C program that takes the
+    address of every declared entry point links against libfldce.so and
+    calls the two host-only ones (no GPU needed)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    names = _declared()
+    src = tmp_path / "abi.c"
+    src.write_text(
+        '#include "fldce.h"\n#include <stdio.h>\n'
+        "typedef void (*fn_t)(void);\n"
+        "int main(void) {\n"
+        "  static const fn_t all[] = {" + ", ".join(f"(fn_t){n}" for n in names) + "};\n"
+        '  printf("%d %s %d\\n", fldce_version(), fldce_status_string(0),\n'
+        "         (int)(sizeof(all) / sizeof(all[0])));\n"
+        "  return 0;\n}\n")
+    exe = tmp_path / "abi"
+    libdir = os.path.dirname(fldce.LIB_PATH)
+    subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                    "-Wno-cast-function-type", "-I", os.path.join(ROOT, "include"), str(src),
+                    "-o", str(exe), "-L", libdir, "-l:" + os.path.basename(fldce.LIB_PATH),
+                    "-Wl,-rpath," + libdir], check=True, capture_output=True, text=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()
+    assert out[0] == str(fldce.fldce_version()) and out[1] == "ok" and int(out[2]) == len(names)
+
+
 def test_status_strings(L):
     assert fldce.status_string(0) == "ok"
     for s in range(-9, 0):
